@@ -1,0 +1,225 @@
+"""CPU oracle: NF4 codebook, blockwise absmax quantizer, double quantization
+of the scales, and dequantization -- written step by step from the pages.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The GPU library
+never calls it and shares no code, table or constant generator with it.
+
+Sources (cited by page title and section):
+  [U] Ultralytics glossary "QLoRA", section "Come funziona QLoRA": the NF4
+      bullet (16 levels at normal quantiles, one absmax scale per block of 64),
+      the double-quantization bullet (scales to 8 bit in blocks of 256,
+      0.5 -> ~0.127 bit/param), the forward/backward paragraph (dequantize to
+      bfloat16 just before the matmul) and the printed NF4-vs-INT4 example
+      (level construction, absmax per block, nearest-level encode, restore).
+  [M] "Modulo 4: QLoRA" (courses.eduardonacimiento.com), section 4.3 b)
+      "Cuantizacion Doble": weights are quantized to 4 bit first, then the
+      scale constants to 8 bit.
+
+Precision: every quantizer step is carried out in IEEE float32 exactly as
+stated (numpy float32 ops are correctly rounded, keep denormals and never
+contract), except the codebook itself, which is computed in float64 and
+rounded once to float32.
+
+Readings where the pages are silent (each also listed in the design doc):
+  * the quantile offset is the printed literal 0.9677083, levels built in
+    float64 and rounded once to float32;
+  * nearest level = argmin of the float32 distance |x - L_k|, ties to the
+    lowest index (what numpy/torch ``argmin`` return);
+  * x = w / absmax is a correctly rounded float32 division;
+  * an all-zero block encodes to the exact-zero level (code 7) with scale 0;
+  * blocks are runs of 64 consecutive elements of the row-major flattening,
+    the last run may be partial; double-quant groups are runs of 256 blocks;
+  * two codes per byte, element 2i in the low nibble, 2i+1 in the high nibble
+    (parity unpinned: a storage convention no page fixes); an odd element
+    count leaves the final high nibble 0;
+  * the 8-bit scale code is the unsigned linear codebook U_k = k/255 on
+    [0, 1] times the group absmax M_g, encoded by the same nearest-level rule
+    (parity unpinned: the pages say only "8 bit in blocks of 256");
+  * the weights are encoded with their exact block absmax; the decoded scale
+    s_b = fl32(U[c2_b] * M_g) is what dequantization uses;
+  * dequantized value = fl32(L[code] * s_b), then round-to-nearest-even bf16.
+"""
+from __future__ import annotations
+
+import math
+import statistics
+
+import numpy as np
+
+NF4_QUANTILE_OFFSET = 0.9677083  # the literal printed in [U]'s example
+BLOCK = 64                       # weights per absmax block [U]
+DQ_GROUP = 256                   # blocks per second-level group [U]
+ZERO_CODE = 7                    # index of the exact-zero level
+
+
+# ---------------------------------------------------------------------------
+# Codebooks
+# ---------------------------------------------------------------------------
+def nf4_levels(inv_cdf=None) -> np.ndarray:
+    """16 NF4 levels, ascending, float32 [U].
+
+    Positive side: the standard-normal quantiles at 8 probabilities evenly
+    spaced from the offset down to 0.5 (0.5 itself excluded). Negative side:
+    minus the quantiles at 7 such probabilities. Add an exact 0, sort, divide
+    by the largest level so the table spans [-1, 1].
+    ``inv_cdf`` is the float64 standard-normal quantile function; by default
+    Python's ``statistics.NormalDist().inv_cdf``.
+    """
+    if inv_cdf is None:
+        inv_cdf = statistics.NormalDist(0.0, 1.0).inv_cdf
+    o = NF4_QUANTILE_OFFSET
+    pos_p = np.linspace(o, 0.5, 9)[:-1]   # 9 points from o down to 0.5, 0.5 dropped
+    neg_p = np.linspace(o, 0.5, 8)[:-1]   # 8 points from o down to 0.5, 0.5 dropped
+    values = [float(inv_cdf(p)) for p in pos_p] + [0.0] + [-float(inv_cdf(p)) for p in neg_p]
+    values.sort()
+    top = values[-1]
+    return np.array([v / top for v in values], dtype=np.float64).astype(np.float32)
+
+
+def int4_levels() -> np.ndarray:
+    """16 evenly spaced levels on [-1, 1] -- [U]'s comparison baseline."""
+    return np.linspace(-1.0, 1.0, 16, dtype=np.float32)
+
+
+def u8_scale_levels() -> np.ndarray:
+    """U_k = fl32(k / 255), k = 0..255: the 8-bit code for a scale relative to
+    its group absmax (the plain reading of "8 bit" in [U] and [M])."""
+    return np.arange(256, dtype=np.float32) / np.float32(255.0)
+
+
+# ---------------------------------------------------------------------------
+# Nearest-level encoder shared by both quantization levels (same rule twice)
+# ---------------------------------------------------------------------------
+def encode_nearest(x: np.ndarray, levels: np.ndarray, chunk: int = 1 << 20) -> np.ndarray:
+    """code_i = argmin_k fl32(|x_i - L_k|), first index on ties. uint8."""
+    x = np.asarray(x, dtype=np.float32).reshape(-1)
+    levels = np.asarray(levels, dtype=np.float32)
+    out = np.empty(x.size, dtype=np.uint8)
+    for s in range(0, x.size, chunk):
+        d = np.abs(x[s:s + chunk, None] - levels[None, :])   # float32
+        out[s:s + chunk] = np.argmin(d, axis=1)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Blockwise absmax quantization [U]
+# ---------------------------------------------------------------------------
+def num_blocks(numel: int) -> int:
+    return -(-numel // BLOCK)
+
+
+def num_groups(numel: int) -> int:
+    return -(-num_blocks(numel) // DQ_GROUP)
+
+
+def block_absmax(w: np.ndarray) -> np.ndarray:
+    """a_b = max |w| over each run of 64 consecutive elements (fp32, exact)."""
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    nb = num_blocks(w.size)
+    padded = np.zeros(nb * BLOCK, dtype=np.float32)   # |0| never raises a max
+    padded[: w.size] = np.abs(w)
+    return padded.reshape(nb, BLOCK).max(axis=1)
+
+
+def normalize(w: np.ndarray, absmax: np.ndarray) -> np.ndarray:
+    """x = fl32(w / a_b); an all-zero block gives x = 0."""
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    a = np.repeat(np.asarray(absmax, dtype=np.float32), BLOCK)[: w.size]
+    x = np.zeros_like(w)
+    nz = a > 0
+    x[nz] = w[nz] / a[nz]
+    return x
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """Byte i = code[2i] | code[2i+1] << 4; a missing last code counts as 0."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(-1)
+    if codes.size % 2:
+        codes = np.concatenate([codes, np.zeros(1, dtype=np.uint8)])
+    return (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray, numel: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8).reshape(-1)
+    out = np.empty(packed.size * 2, dtype=np.uint8)
+    out[0::2] = packed & 0x0F
+    out[1::2] = packed >> 4
+    return out[:numel]
+
+
+def double_quantize(absmax: np.ndarray):
+    """Second level [U], [M]: per group of 256 blocks, M_g = max a_b; each
+    a_b / M_g is encoded to the nearest U_k. Returns (c2 uint8, M_g float32)."""
+    absmax = np.asarray(absmax, dtype=np.float32)
+    nb = absmax.size
+    ng = -(-nb // DQ_GROUP)
+    padded = np.zeros(ng * DQ_GROUP, dtype=np.float32)
+    padded[:nb] = absmax
+    group_max = padded.reshape(ng, DQ_GROUP).max(axis=1)
+    mg = np.repeat(group_max, DQ_GROUP)[:nb]
+    x2 = np.zeros(nb, dtype=np.float32)
+    nz = mg > 0
+    x2[nz] = absmax[nz] / mg[nz]
+    c2 = encode_nearest(x2, u8_scale_levels())
+    return c2, group_max
+
+
+def decode_scales(c2: np.ndarray, group_max: np.ndarray) -> np.ndarray:
+    """s_b = fl32(U[c2_b] * M_g)."""
+    c2 = np.asarray(c2, dtype=np.uint8)
+    mg = np.repeat(np.asarray(group_max, dtype=np.float32), DQ_GROUP)[: c2.size]
+    return u8_scale_levels()[c2] * mg
+
+
+def quantize(w: np.ndarray, double_quant: bool = True, levels: np.ndarray | None = None) -> dict:
+    """Full quantizer. Weights first (with exact a_b), then the scales [M]."""
+    if levels is None:
+        levels = nf4_levels()
+    w = np.asarray(w, dtype=np.float32).reshape(-1)
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    absmax = block_absmax(w)
+    codes = encode_nearest(normalize(w, absmax), levels)
+    out = {"numel": w.size, "codes": pack_nibbles(codes), "absmax": absmax, "double_quant": bool(double_quant)}
+    if double_quant:
+        c2, mg = double_quantize(absmax)
+        out["scale_codes"] = c2
+        out["group_scale"] = mg
+        out["scales"] = decode_scales(c2, mg)
+    else:
+        out["scales"] = absmax
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Dequantization [U]
+# ---------------------------------------------------------------------------
+def bf16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bfloat16, nearest-even, returned as uint16 bit patterns
+    (finite inputs only)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + keep_lsb) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def dequantize(q: dict, levels: np.ndarray | None = None):
+    """w32 = fl32(L[code] * s_b) and its bf16 rounding (as uint16 bits)."""
+    if levels is None:
+        levels = nf4_levels()
+    numel = q["numel"]
+    codes = unpack_nibbles(q["codes"], numel)
+    s = np.repeat(np.asarray(q["scales"], dtype=np.float32), BLOCK)[:numel]
+    w32 = levels[codes] * s
+    return w32, bf16_rne_bits(w32)
+
+
+def bits_per_param(numel: int, double_quant: bool) -> float:
+    """Scale storage per weight: 32-bit absmax per block, or an 8-bit code per
+    block plus one 32-bit M_g per 256 blocks [U]."""
+    nb, ng = num_blocks(numel), num_groups(numel)
+    return (8.0 * nb + 32.0 * ng) / numel if double_quant else 32.0 * nb / numel
