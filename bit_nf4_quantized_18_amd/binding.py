@@ -1,0 +1,203 @@
+"""Thin ctypes binding over libqlora_nf4.so (the C ABI in include/qlora_nf4.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels.
+Tensors are torch tensors on the current HIP device; work is enqueued on
+torch's current stream. There is no fallback: if the library is missing the
+functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libqlora_nf4.so")
+
+QLORA_BF16, QLORA_F32 = 0, 1
+MAX_RANK = 128
+BLOCK, DQ_GROUP = 64, 256
+
+STATUS = {0: "QLORA_OK", -1: "QLORA_ERR_NULL", -2: "QLORA_ERR_SHAPE", -3: "QLORA_ERR_ALIGN",
+          -4: "QLORA_ERR_UNSUPPORTED", -5: "QLORA_ERR_WORKSPACE", -6: "QLORA_ERR_HIP"}
+
+# Every symbol include/qlora_nf4.h declares.
+EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
+           "qlora_linear_workspace_bytes", "qlora_status_string", "qlora_nf4_levels")
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class NF4WeightC(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scale_codes", ctypes.c_void_p), ("group_scale", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                ("double_quant", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def load():
+    """Load the library (once). Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_nf4_quantized_18_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    wp = ctypes.POINTER(NF4WeightC)
+    lib.qlora_nf4_quantize.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp]
+    lib.qlora_nf4_quantize.restype = i32
+    lib.qlora_nf4_dequantize.argtypes = [wp, i32, vp, vp]
+    lib.qlora_nf4_dequantize.restype = i32
+    lib.qlora_linear_fwd.argtypes = [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    lib.qlora_linear_fwd.restype = i32
+    lib.qlora_linear_bwd.argtypes = [wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.qlora_linear_bwd.restype = i32
+    lib.qlora_linear_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    lib.qlora_linear_workspace_bytes.restype = sz
+    lib.qlora_status_string.argtypes = [i32]
+    lib.qlora_status_string.restype = ctypes.c_char_p
+    lib.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    lib.qlora_nf4_levels.restype = i32
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().qlora_status_string(status).decode()
+
+
+def levels():
+    """The 16 float32 levels the kernels use (host call)."""
+    buf = (ctypes.c_float * 16)()
+    n = load().qlora_nf4_levels(buf)
+    if n != 16:
+        raise QloraError(n, "qlora_nf4_levels")
+    return list(buf)
+
+
+def workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    return int(load().qlora_linear_workspace_bytes(m, n, k, r))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QloraError(status, where)
+
+
+@dataclasses.dataclass
+class PackedNF4:
+    """A packed NF4 weight on the device (n x k row-major)."""
+    n: int
+    k: int
+    codes: "object"                 # uint8 [ceil(n*k/2)]
+    double_quant: bool
+    scale_codes: "object" = None    # uint8 [nblocks]        (double quant)
+    group_scale: "object" = None    # float32 [ngroups]      (double quant)
+    absmax: "object" = None         # float32 [nblocks]      (exact a_b; required without double quant)
+
+    def c_struct(self) -> NF4WeightC:
+        return NF4WeightC(self.n, self.k, self.codes.data_ptr(),
+                          None if self.scale_codes is None else self.scale_codes.data_ptr(),
+                          None if self.group_scale is None else self.group_scale.data_ptr(),
+                          None if self.absmax is None else self.absmax.data_ptr(), int(self.double_quant))
+
+
+def _empty(n, dtype, device):
+    import torch
+
+    # 16 extra bytes so even empty-ish buffers get a real, aligned allocation
+    return torch.empty(max(n, 1), dtype=dtype, device=device)
+
+
+def quantize(w, double_quant: bool = True, keep_absmax: bool = False) -> PackedNF4:
+    """Quantize a float32 CUDA tensor (any shape; flattened row-major).
+    A 2-D tensor gives n, k = its shape; other shapes give n = 1."""
+    import torch
+
+    if w.dtype != torch.float32 or not w.is_cuda:
+        raise TypeError("quantize expects a float32 tensor on the GPU")
+    w = w.contiguous()
+    numel = w.numel()
+    n, k = (w.shape[0], w.shape[1]) if w.dim() == 2 else (1, numel)
+    nb = -(-numel // BLOCK)
+    ng = -(-nb // DQ_GROUP)
+    dev = w.device
+    codes = _empty((numel + 1) // 2, torch.uint8, dev)
+    sc = _empty(nb, torch.uint8, dev) if double_quant else None
+    gs = _empty(ng, torch.float32, dev) if double_quant else None
+    am = _empty(nb, torch.float32, dev) if (keep_absmax or not double_quant) else None
+    st = load().qlora_nf4_quantize(_ptr(w), numel, int(double_quant), _ptr(codes), _ptr(sc), _ptr(gs), _ptr(am),
+                                   _stream())
+    _check(st, "qlora_nf4_quantize")
+    return PackedNF4(n, k, codes[: (numel + 1) // 2], double_quant, None if sc is None else sc[:nb],
+                     None if gs is None else gs[:ng], None if am is None else am[:nb])
+
+
+def dequantize(q: PackedNF4, dtype=None):
+    import torch
+
+    dtype = torch.bfloat16 if dtype is None else dtype
+    code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32}[dtype]
+    out = torch.empty((q.n, q.k), dtype=dtype, device=q.codes.device)
+    ws = q.c_struct()
+    _check(load().qlora_nf4_dequantize(ctypes.byref(ws), code, _ptr(out), _stream()), "qlora_nf4_dequantize")
+    return out
+
+
+def _workspace(m, n, k, r, device):
+    import torch
+
+    nbytes = workspace_bytes(m, n, k, r)
+    return (torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None), nbytes
+
+
+def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool = True, out=None):
+    """Y = X W16^T + (alpha/r) (X A^T) B^T. x: bf16 (m, k). Returns (y, h)."""
+    import torch
+
+    m = x.shape[0]
+    r = 0 if a is None else a.shape[0]
+    dev = x.device
+    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=dev)
+    h = torch.empty((m, r), dtype=torch.float32, device=dev) if (want_h and r > 0) else None
+    ws, nbytes = _workspace(m, q.n, q.k, r, dev)
+    wc = q.c_struct()
+    st = load().qlora_linear_fwd(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(y), _ptr(h),
+                                 _ptr(ws), nbytes, _stream())
+    _check(st, "qlora_linear_fwd")
+    return y, h
+
+
+def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, need_dx: bool = True):
+    """Returns (dx bf16 (m,k) or None, dA float32 (r,k), dB float32 (n,r))."""
+    import torch
+
+    m = dy.shape[0]
+    r = 0 if a is None else a.shape[0]
+    dev = dy.device
+    dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev) if need_dx else None
+    da = torch.empty((r, q.k), dtype=torch.float32, device=dev) if r else None
+    db = torch.empty((q.n, r), dtype=torch.float32, device=dev) if r else None
+    ws, nbytes = _workspace(m, q.n, q.k, r, dev)
+    wc = q.c_struct()
+    st = load().qlora_linear_bwd(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(h),
+                                 _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes, _stream())
+    _check(st, "qlora_linear_bwd")
+    return dx, da, db

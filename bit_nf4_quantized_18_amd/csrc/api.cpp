@@ -1,0 +1,256 @@
+// C ABI: argument validation, workspace layout and kernel dispatch.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace {
+
+using qlora::PackedW;
+
+constexpr int64_t kAlign = 256;  // workspace sub-buffer alignment (bytes)
+constexpr int64_t kGemvMaxM = 16;
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+int rank_pad(int r) { return r == 0 ? 0 : static_cast<int>(round_up(r, 32)); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workspace layout: consecutive 256-byte aligned sub-buffers.
+struct Carve {
+  int64_t off = 0;
+  int64_t take(int64_t bytes) {
+    const int64_t at = off;
+    off += round_up(bytes, kAlign);
+    return at;
+  }
+};
+
+struct FwdLayout {
+  int64_t h32, hs, xp, total;
+};
+FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r) {
+  (void)n;
+  Carve c;
+  FwdLayout L{};
+  L.h32 = c.take((m <= kGemvMaxM ? qlora::skinny_splits(m, k) : 1) * m * r * 4);
+  L.hs = c.take(m <= kGemvMaxM ? 0 : m * rank_pad(r) * 2);
+  L.xp = c.take(m <= kGemvMaxM ? m * k * 2 : 0);
+  L.total = c.off;
+  return L;
+}
+
+struct BwdLayout {
+  int64_t h32, dh32, dhs, at, bt, part, total;
+};
+BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r) {
+  Carve c;
+  BwdLayout L{};
+  const int rp = rank_pad(r);
+  const int splits = qlora::rank_reduce_splits(m);
+  L.h32 = c.take(m * r * 4);
+  L.dh32 = c.take(m * r * 4);
+  L.dhs = c.take(m * rp * 2);
+  L.at = c.take(k * rp * 2);
+  L.bt = c.take(n * rp * 2);
+  L.part = c.take(r == 0 ? 0 : static_cast<int64_t>(splits) * r * (k > n ? k : n) * 4);
+  L.total = c.off;
+  return L;
+}
+
+qlora_status check_weight(const qlora_nf4_weight* w, bool linear) {
+  if (w == nullptr || w->codes == nullptr) return QLORA_ERR_NULL;
+  if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (w->double_quant) {
+    if (w->scale_codes == nullptr || w->group_scale == nullptr) return QLORA_ERR_NULL;
+    if (!aligned16(w->scale_codes) || !aligned16(w->group_scale)) return QLORA_ERR_ALIGN;
+  } else {
+    if (w->absmax == nullptr) return QLORA_ERR_NULL;
+    if (!aligned16(w->absmax)) return QLORA_ERR_ALIGN;
+  }
+  if (!aligned16(w->codes)) return QLORA_ERR_ALIGN;
+  if (w->n < 1 || w->k < 1) return QLORA_ERR_SHAPE;
+  if (w->n > (INT64_C(1) << 40) / w->k) return QLORA_ERR_SHAPE;
+  if (linear && ((w->k % QLORA_BLOCK) != 0 || (w->n % 16) != 0)) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+PackedW view(const qlora_nf4_weight* w) {
+  PackedW p;
+  p.codes = w->codes;
+  p.scale_codes = w->scale_codes;
+  p.group_scale = w->group_scale;
+  p.absmax = w->absmax;
+  p.n = w->n;
+  p.k = w->k;
+  p.dq = w->double_quant;
+  return p;
+}
+
+qlora_status hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+#define QLORA_TRY(expr)                       \
+  do {                                        \
+    const hipError_t e_ = (expr);             \
+    if (e_ != hipSuccess) return QLORA_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_string(qlora_status status) {
+  switch (status) {
+    case QLORA_OK:
+      return "ok";
+    case QLORA_ERR_NULL:
+      return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE:
+      return "invalid size (negative, zero, too large, k not a multiple of 64 or n not a multiple of 16)";
+    case QLORA_ERR_ALIGN:
+      return "a pointer is not 16-byte aligned";
+    case QLORA_ERR_UNSUPPORTED:
+      return "unsupported argument (rank above QLORA_MAX_RANK, dtype or flag)";
+    case QLORA_ERR_WORKSPACE:
+      return "workspace missing or too small";
+    case QLORA_ERR_HIP:
+      return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
+  if (m <= 0 || n <= 0 || k <= 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  const int64_t f = fwd_layout(m, n, k, r).total;
+  const int64_t b = bwd_layout(m, n, k, r).total;
+  return static_cast<size_t>(f > b ? f : b);
+}
+
+qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant, uint8_t* codes,
+                                uint8_t* scale_codes, float* group_scale, float* absmax, hipStream_t stream) {
+  if (double_quant != 0 && double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (w == nullptr || codes == nullptr) return QLORA_ERR_NULL;
+  if (double_quant && (scale_codes == nullptr || group_scale == nullptr)) return QLORA_ERR_NULL;
+  if (!double_quant && absmax == nullptr) return QLORA_ERR_NULL;
+  if (numel < 1 || numel > (INT64_C(1) << 40)) return QLORA_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(codes)) return QLORA_ERR_ALIGN;
+  if (double_quant && (!aligned16(scale_codes) || !aligned16(group_scale))) return QLORA_ERR_ALIGN;
+  if (absmax != nullptr && !aligned16(absmax)) return QLORA_ERR_ALIGN;
+  return hip_status(qlora::launch_quantize(w, numel, double_quant, codes, double_quant ? scale_codes : nullptr,
+                                           double_quant ? group_scale : nullptr, absmax, stream));
+}
+
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dtype, void* out,
+                                  hipStream_t stream) {
+  const qlora_status st = check_weight(w, false);
+  if (st != QLORA_OK) return st;
+  if (out_dtype != QLORA_BF16 && out_dtype != QLORA_F32) return QLORA_ERR_UNSUPPORTED;
+  if (out == nullptr) return QLORA_ERR_NULL;
+  if (!aligned16(out)) return QLORA_ERR_ALIGN;
+  return hip_status(qlora::launch_dequantize(view(w), out_dtype == QLORA_F32, out, stream));
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                              const uint16_t* b, int r, float alpha, uint16_t* y, float* h_out, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  qlora_status st = check_weight(w, true);
+  if (st != QLORA_OK) return st;
+  if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
+  if (r < 0) return QLORA_ERR_SHAPE;
+  if (r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
+  if (m == 0) return QLORA_OK;
+  if (x == nullptr || y == nullptr) return QLORA_ERR_NULL;
+  if (r > 0 && (a == nullptr || b == nullptr)) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(y)) return QLORA_ERR_ALIGN;
+  if (r > 0 && (!aligned16(a) || !aligned16(b))) return QLORA_ERR_ALIGN;
+  if (h_out != nullptr && !aligned16(h_out)) return QLORA_ERR_ALIGN;
+  const int64_t n = w->n, k = w->k;
+  const size_t need = qlora_linear_workspace_bytes(m, n, k, r);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
+
+  const FwdLayout L = fwd_layout(m, n, k, r);
+  char* base = static_cast<char*>(ws);
+  const float s = (r == 0) ? 0.0f : alpha / static_cast<float>(r);
+  const int rp = rank_pad(r);
+  const PackedW pw = view(w);
+
+  if (m <= kGemvMaxM) {
+    // H as per-split partial sums in the workspace; the GEMV sums them.
+    uint16_t* xp = reinterpret_cast<uint16_t*>(base + L.xp);
+    float* hpart = (r == 0) ? nullptr : reinterpret_cast<float*>(base + L.h32);
+    QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, hpart, nullptr, xp,
+                                   qlora::skinny_splits(m, k), stream));
+    QLORA_TRY(qlora::launch_gemv(pw, xp, m, hpart, qlora::skinny_splits(m, k), b, r, s, y, h_out, stream));
+  } else {
+    float* h32 = (r == 0) ? nullptr : (h_out != nullptr ? h_out : reinterpret_cast<float*>(base + L.h32));
+    uint16_t* hs = (r == 0) ? nullptr : reinterpret_cast<uint16_t*>(base + L.hs);
+    if (r > 0) QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, s, h32, hs, nullptr, 1, stream));
+    QLORA_TRY(qlora::launch_gemm_fwd(pw, x, m, hs, b, r, rp, y, stream));
+  }
+  return QLORA_OK;
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t m,
+                              const uint16_t* a, const uint16_t* b, int r, float alpha, const float* h_saved,
+                              uint16_t* dx, float* da, float* db, void* ws, size_t ws_bytes, hipStream_t stream) {
+  qlora_status st = check_weight(w, true);
+  if (st != QLORA_OK) return st;
+  if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
+  if (r < 0) return QLORA_ERR_SHAPE;
+  if (r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
+  const int64_t n = w->n, k = w->k;
+  if (r > 0) {
+    if (a == nullptr || b == nullptr || da == nullptr || db == nullptr) return QLORA_ERR_NULL;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(da) || !aligned16(db)) return QLORA_ERR_ALIGN;
+  }
+  if (m == 0) {
+    if (r > 0) {
+      QLORA_TRY(qlora::launch_fill_zero(da, static_cast<int64_t>(r) * k, stream));
+      QLORA_TRY(qlora::launch_fill_zero(db, n * r, stream));
+    }
+    return QLORA_OK;
+  }
+  if (dy == nullptr) return QLORA_ERR_NULL;
+  if (r > 0 && x == nullptr) return QLORA_ERR_NULL;
+  if (dx == nullptr && r == 0) return QLORA_OK;  // nothing requested
+  if (!aligned16(dy) || (x != nullptr && !aligned16(x)) || (dx != nullptr && !aligned16(dx))) return QLORA_ERR_ALIGN;
+  if (h_saved != nullptr && !aligned16(h_saved)) return QLORA_ERR_ALIGN;
+  const size_t need = qlora_linear_workspace_bytes(m, n, k, r);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
+  if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
+
+  const BwdLayout L = bwd_layout(m, n, k, r);
+  char* base = static_cast<char*>(ws);
+  const float s = (r == 0) ? 0.0f : alpha / static_cast<float>(r);
+  const int rp = rank_pad(r);
+  const PackedW pw = view(w);
+  uint16_t* dhs = nullptr;
+  uint16_t* at = nullptr;
+
+  if (r > 0) {
+    uint16_t* bt = reinterpret_cast<uint16_t*>(base + L.bt);
+    at = reinterpret_cast<uint16_t*>(base + L.at);
+    float* dh32 = reinterpret_cast<float*>(base + L.dh32);
+    dhs = reinterpret_cast<uint16_t*>(base + L.dhs);
+    float* part = reinterpret_cast<float*>(base + L.part);
+    const float* h = h_saved;
+    if (h == nullptr) {
+      float* h32 = reinterpret_cast<float*>(base + L.h32);
+      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, h32, nullptr, nullptr, 1, stream));
+      h = h32;
+    }
+    QLORA_TRY(qlora::launch_lora_transpose(a, b, n, k, r, rp, at, bt, stream));
+    // dH = s dY B  (contraction over n, with B^T as the r x n operand)
+    QLORA_TRY(qlora::launch_skinny(dy, bt, m, n, r, rp, s, 1.0f, dh32, dhs, nullptr, 1, stream));
+    const int splits = qlora::rank_reduce_splits(m);
+    // dA = dH^T X  (r x k)
+    QLORA_TRY(qlora::launch_rank_reduce(dh32, x, m, k, r, 1.0f, splits, part, da, 0, stream));
+    // dB = s dY^T H  (n x r)
+    QLORA_TRY(qlora::launch_rank_reduce(h, dy, m, n, r, s, splits, part, db, 1, stream));
+  }
+  if (dx != nullptr) QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream));
+  return QLORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// NF4 level table, built once on the host.
+//
+// Ultralytics glossary "QLoRA", section "Come funziona QLoRA": 16 levels at
+// quantiles of the standard normal with an exact zero, normalised to [-1, 1];
+// the printed example takes 8 probabilities evenly spaced from 0.9677083 down
+// to 0.5 (0.5 excluded) for the positive side, 7 for the negative side.
+//
+// The quantile is found by bisection on the normal CDF written with erfc in
+// long double, independently of any published inverse-CDF approximation. The
+// bracket is halved 200 times, far below the float64 resolution of the result;
+// each level is divided by the largest in double and rounded once to float.
+#include <cmath>
+#include <mutex>
+
+#include "internal.h"
+
+namespace qlora {
+namespace {
+
+long double normal_cdf(long double x) { return 0.5L * std::erfc(-x / std::sqrt(2.0L)); }
+
+double normal_quantile_upper(double p) {  // p in [0.5, 1)
+  long double lo = 0.0L, hi = 40.0L;
+  for (int i = 0; i < 200; ++i) {
+    const long double mid = 0.5L * (lo + hi);
+    if (normal_cdf(mid) < static_cast<long double>(p)) {
+      lo = mid;
+    } else {
+      hi = mid;
+    }
+  }
+  return static_cast<double>(0.5L * (lo + hi));
+}
+
+Levels build_levels() {
+  const double offset = 0.9677083;
+  double v[16];
+  int n = 0;
+  // Evenly spaced probabilities from the offset to 0.5, endpoint dropped:
+  // start + i * ((0.5 - start) / (count - 1)), as a float64 linspace does.
+  const double step_pos = (0.5 - offset) / 8.0;
+  const double step_neg = (0.5 - offset) / 7.0;
+  for (int j = 0; j < 7; ++j) v[n++] = -normal_quantile_upper(static_cast<double>(j) * step_neg + offset);
+  v[n++] = 0.0;
+  for (int i = 0; i < 8; ++i) v[n++] = normal_quantile_upper(static_cast<double>(i) * step_pos + offset);
+  // ascending: negatives were produced from most negative (j = 0) upward,
+  // positives from largest (i = 0) downward; reverse the positive run.
+  for (int a = 8, b = 15; a < b; ++a, --b) {
+    const double t = v[a];
+    v[a] = v[b];
+    v[b] = t;
+  }
+  const double top = v[15];
+  Levels L;
+  for (int c = 0; c < 16; ++c) L.v[c] = static_cast<float>(v[c] / top);
+  return L;
+}
+
+}  // namespace
+
+const Levels& nf4_table() {
+  static std::once_flag once;
+  static Levels table;
+  std::call_once(once, [] { table = build_levels(); });
+  return table;
+}
+
+}  // namespace qlora
+
+extern "C" int qlora_nf4_levels(float out16[16]) {
+  if (out16 == nullptr) return QLORA_ERR_NULL;
+  const qlora::Levels& L = qlora::nf4_table();
+  for (int c = 0; c < 16; ++c) out16[c] = L.v[c];
+  return 16;
+}

@@ -1,0 +1,110 @@
+// Decode path (m <= 16 tokens): Y = X W16^T + s H B^T with W read straight
+// from its packed NF4 form.
+//
+// Ultralytics glossary "QLoRA", section "Come funziona QLoRA": each frozen
+// layer dequantizes its NF4 weights to bfloat16 right before the matmul and
+// adds the LoRA path output. At a handful of tokens the layer is bound by the
+// HBM stream of the packed weight (0.5 B of codes + 1/64 B of scale codes per
+// weight), so the kernel is built around that stream:
+//   * a workgroup owns 16 weight rows; its WAVES x 4 lane groups split the
+//     row's 64-blocks round-robin, so every lane loads whole blocks (32 B of
+//     codes, two 16-byte loads) and all loads of a lane are independent;
+//   * per block a lane decodes the scale, builds a 16-entry bf16 table in
+//     registers (nf4_lut.h) and looks up 8 weights per table access;
+//   * the dot products run on the matrix cores (16x16x32 bf16 MFMA with the
+//     tokens padded to 16 rows), so the vector ALU only unpacks;
+//   * X is pre-arranged by the LoRA-down kernel in the lookup's output order,
+//     and partial sums of the waves are reduced in a fixed order in LDS.
+#include "internal.h"
+#include "mfma.h"
+#include "nf4_lut.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kGroup = 256;
+
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ xp, int M,
+                                                          const float* __restrict__ hpart, int hsplits,
+                                                          const uint16_t* __restrict__ b, int r, float s,
+                                                          uint16_t* __restrict__ y, float* __restrict__ h_out,
+                                                          Levels L) {
+  constexpr int kLaneGroups = WAVES * 4;
+  __shared__ f32x4 red[WAVES][64];
+  __shared__ float h_lds[16 * QLORA_MAX_RANK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int G = wave * 4 + g;
+  const int64_t K = w.k, N = w.n;
+  const int64_t nbk = K / 64;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int64_t n = n0 + i;
+  const bool nvalid = n < N;
+  const bool mvalid = i < M;
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Wave-uniform trip count: block kb = G + kLaneGroups * t.
+  for (int64_t kb0 = wave * 4; kb0 < nbk; kb0 += kLaneGroups) {
+    const int64_t kb = kb0 + g;
+    const bool valid = nvalid && kb < nbk;
+    u32x4 c0 = u32x4{0, 0, 0, 0}, c1 = u32x4{0, 0, 0, 0};
+    float sc = 0.0f;
+    if (valid) {
+      const uint8_t* cp = w.codes + (n * K + kb * 64) / 2;
+      c0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp));
+      c1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp) + 1);
+      const int64_t bi = n * nbk + kb;
+      sc = w.dq ? (static_cast<float>(w.scale_codes[bi]) / 255.0f) * w.group_scale[bi / kGroup] : w.absmax[bi];
+    }
+    const BlockLut lut = make_block_lut(L.v, sc);
+    const uint16_t* xrow = xp + static_cast<int64_t>(i) * K + kb * 64;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
+      uint32_t wv[4];
+      lut8_decode_order(lut, cw, wv);
+      u32x4 a = u32x4{0, 0, 0, 0};
+      if (valid && mvalid) a = ld16(xrow + 8 * j);
+      acc = mfma_16x16x32(a, u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
+    }
+  }
+
+  red[wave][lane] = acc;
+  // H = sum of the LoRA-down partials (fixed order).
+  for (int idx = tid; idx < M * r; idx += WAVES * 64) {
+    float hv = 0.0f;
+    for (int sp = 0; sp < hsplits; ++sp) hv += hpart[static_cast<int64_t>(sp) * M * r + idx];
+    h_lds[idx] = hv;
+    if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
+  }
+  __syncthreads();
+  if (tid >= 256) return;
+  const int l2 = tid & 63, v = tid >> 6;
+  const int mo = 4 * (l2 >> 4) + v;
+  const int64_t no = n0 + (l2 & 15);
+  if (mo >= M || no >= N) return;
+  float sum = 0.0f;
+#pragma unroll
+  for (int wv = 0; wv < WAVES; ++wv) sum += red[wv][l2][v];
+  if (r > 0) {
+    float lo = 0.0f;
+    const uint16_t* brow = b + no * r;
+    for (int j = 0; j < r; ++j) lo = fmaf(h_lds[mo * r + j], __uint_as_float(static_cast<uint32_t>(brow[j]) << 16), lo);
+    sum = fmaf(s, lo, sum);
+  }
+  y[static_cast<int64_t>(mo) * N + no] = f32_to_bf16_rne(sum);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const PackedW& w, const uint16_t* xp, int64_t m, const float* hpart, int hsplits,
+                       const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
+  constexpr int kWaves = 8;
+  const unsigned grid = static_cast<unsigned>((w.n + 15) / 16);
+  hipLaunchKernelGGL(gemv_kernel<kWaves>, dim3(grid), dim3(kWaves * 64), 0, st, w, xp, static_cast<int>(m), hpart,
+                     hsplits, b, r, s, y, h_out, nf4_table());
+  return hipGetLastError();
+}
+
+}  // namespace qlora

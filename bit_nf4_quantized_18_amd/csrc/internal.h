@@ -1,0 +1,86 @@
+// Internal declarations shared by the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlora_nf4.h"
+
+namespace qlora {
+
+// Native vector types (for 16-byte loads/stores and MFMA operands).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The 16 NF4 levels as float32, passed to kernels by value (kernarg -> SGPRs).
+struct Levels {
+  float v[16];
+};
+
+// Host-side level table, built once (thread-safe) from the standard-normal
+// quantile function.
+const Levels& nf4_table();
+
+// ---------------------------------------------------------------------------
+// Launchers (each enqueues on `s` and returns hipGetLastError()).
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize(const float* w, int64_t numel, int dq, uint8_t* codes, uint8_t* scale_codes,
+                           float* group_scale, float* absmax, hipStream_t s);
+
+// Packed weight view used by all kernels that read NF4 weights.
+struct PackedW {
+  const uint8_t* codes;
+  const uint8_t* scale_codes;  // dq
+  const float* group_scale;    // dq
+  const float* absmax;         // !dq
+  int64_t n, k;
+  int dq;
+};
+
+hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream_t s);
+
+// H-like skinny projection: out[m][j] = scale * sum_q P[m][q] * Q[j][q] for j < r,
+// P bf16 m x qn (row stride qn, qn % 8 == 0), Q bf16 r x qn. With one
+// contraction split (m > 16) it writes out_f32 (m x r, may be null) and
+// out_bf16 (m x rpad, zero-padded for j >= r, may be null) holding
+// bf16(scale2 * scale * sum). With several splits (m <= 16, see
+// skinny_splits, decode path only) it writes raw partial sums to out_f32 as splits x m x r.
+// If p_perm is non-null it receives P with every group of 8 consecutive
+// elements reordered as (0,2,4,6,1,3,5,7) (the decode kernel's operand order).
+hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
+                         float scale, float scale2, float* out_f32, uint16_t* out_bf16, uint16_t* p_perm,
+                         int splits, hipStream_t s);
+int skinny_splits(int64_t m, int64_t qn);
+
+// Decode GEMV, m <= 16: y = x W16^T + s * h B^T. xp is x in decode operand
+// order, hpart holds hsplits partial sums of H (hsplits x m x r float32,
+// ignored when r = 0); h_out (m x r, may be null) receives H.
+hipError_t launch_gemv(const PackedW& w, const uint16_t* xp, int64_t m, const float* hpart, int hsplits,
+                       const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st);
+
+// Fused dequant-GEMM, forward: y = x W16^T + hs B^T where hs is bf16 m x rpad
+// (already scaled by s), b is n x r bf16.
+hipError_t launch_gemm_fwd(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* hs,
+                           const uint16_t* b, int r, int rpad, uint16_t* y, hipStream_t st);
+
+// Fused dequant-GEMM, backward data: dx = dy W16 + dhs At where dhs is bf16
+// m x rpad and at is bf16 k x rpad (A transposed, zero padded).
+hipError_t launch_gemm_dx(const PackedW& w, const uint16_t* dy, int64_t m, const uint16_t* dhs,
+                          const uint16_t* at, int rpad, uint16_t* dx, hipStream_t st);
+
+// Transposes with zero padding: bt (rpad x n) from b (n x r); at (k x rpad) from a (r x k).
+hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n, int64_t k, int r, int rpad,
+                                 uint16_t* at, uint16_t* bt, hipStream_t st);
+
+// out(j, c) = scale * sum_m U[m][j] * V[m][c], U float32 m x r, V bf16 m x cn.
+// Deterministic: `splits` partial sums over m-ranges into part (splits x r x cn),
+// then a fixed-order reduce. c_major=0 writes out[j*cn + c], 1 writes out[c*r + j].
+hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int64_t cn, int r, float scale,
+                              int splits, float* part, float* out, int c_major, hipStream_t st);
+
+hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
+
+int rank_reduce_splits(int64_t m);
+
+}  // namespace qlora

@@ -1,0 +1,215 @@
+// Rank-r side kernels of the LoRA path.
+//
+// "LoRA y QLoRA en Profundidad", section "La Idea Central": the adapter adds
+// (alpha / r) * B @ A with A r x d_in and B d_out x r. With H = X A^T the
+// forward adds s H B^T; the backward (Ultralytics glossary "QLoRA", "Come
+// funziona QLoRA": gradients only for the two LoRA matrices) needs
+// dH = s dY B, dA = dH^T X and dB = s dY^T H.
+//
+// These are thin (r <= 128 columns) and are bounded by one pass over X or dY.
+#include "internal.h"
+#include "mfma.h"
+#include "nf4_lut.h"
+
+namespace qlora {
+namespace {
+
+// out[m][j] = scale * sum_q P[m][q] Q[j][q]. One workgroup (4 waves) per 16
+// rows of P and one contraction split; waves take interleaved 32-wide chunks
+// of q and are summed in a fixed order through LDS. RT = rpad / 16 output
+// column tiles (0: only the reordered copy of P is produced).
+template <int RT>
+__global__ __launch_bounds__(256) void skinny_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
+                                                     int64_t M, int64_t qn, int r, int rpad, float scale,
+                                                     float scale2, float* __restrict__ out_f32,
+                                                     uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ p_perm,
+                                                     int splits) {
+  constexpr int kRT = RT > 0 ? RT : 1;
+  __shared__ f32x4 red[4][kRT][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, g = lane >> 4;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int split = blockIdx.y;
+  const int64_t m = m0 + i;
+  const bool mvalid = m < M;
+  const int64_t nchunks = (qn + 31) / 32;
+  const int64_t per = (nchunks + splits - 1) / splits;
+  const int64_t c_begin = split * per;
+  const int64_t c_end = (c_begin + per < nchunks) ? c_begin + per : nchunks;
+
+  f32x4 acc[kRT];
+#pragma unroll
+  for (int t = 0; t < kRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t c = c_begin + wave; c < c_end; c += 4) {
+    const int64_t q = c * 32 + 8 * g;
+    const bool qvalid = q < qn;  // qn % 8 == 0, so a valid run is whole
+    u32x4 a = u32x4{0, 0, 0, 0};
+    if (mvalid && qvalid) a = ld16(P + m * qn + q);
+    if (p_perm != nullptr && mvalid && qvalid) {
+      uint32_t in[4] = {a[0], a[1], a[2], a[3]}, o[4];
+      to_decode_order(in, o);
+      st16(p_perm + m * qn + q, u32x4{o[0], o[1], o[2], o[3]});
+    }
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int j = 16 * t + i;
+      u32x4 b = u32x4{0, 0, 0, 0};
+      if (j < r && qvalid) b = ld16(Q + static_cast<int64_t>(j) * qn + q);
+      acc[t] = mfma_16x16x32(a, b, acc[t]);
+    }
+  }
+  if (RT == 0) return;
+
+#pragma unroll
+  for (int t = 0; t < RT; ++t) red[wave][t][lane] = acc[t];
+  __syncthreads();
+  const int l2 = tid & 63, v = tid >> 6;
+  const int64_t mo = m0 + 4 * (l2 >> 4) + v;
+  if (mo >= M) return;
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int j = 16 * t + (l2 & 15);
+    const float sum = ((red[0][t][l2][v] + red[1][t][l2][v]) + red[2][t][l2][v]) + red[3][t][l2][v];
+    if (splits > 1) {
+      if (j < r) out_f32[(split * M + mo) * r + j] = sum;
+    } else {
+      const float val = scale * sum;
+      if (out_f32 != nullptr && j < r) out_f32[mo * r + j] = val;
+      if (out_bf16 != nullptr && j < rpad) out_bf16[mo * rpad + j] = f32_to_bf16_rne(scale2 * val);
+    }
+  }
+}
+
+// at (k x rpad) = A^T zero-padded; bt (rpad x n) = B^T zero-padded.
+__global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int64_t n,
+                                      int64_t k, int r, int rpad, uint16_t* __restrict__ at,
+                                      uint16_t* __restrict__ bt) {
+  int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t na = k * rpad;
+  if (idx < na) {
+    const int64_t kk = idx / rpad;
+    const int j = static_cast<int>(idx % rpad);
+    at[idx] = (j < r) ? a[static_cast<int64_t>(j) * k + kk] : uint16_t(0);
+    return;
+  }
+  idx -= na;
+  if (idx < static_cast<int64_t>(rpad) * n) {
+    const int j = static_cast<int>(idx / n);
+    const int64_t nn = idx % n;
+    bt[idx] = (j < r) ? b[nn * r + j] : uint16_t(0);
+  }
+}
+
+// part[s][j][c] = sum over rows m of split s of U[m][j] * V[m][c] (float32
+// U, bf16 V). Each thread owns two adjacent columns c and 16 ranks j; the
+// U row slice is uniform across the workgroup.
+__global__ __launch_bounds__(256) void rank_partial_kernel(const float* __restrict__ U, const uint16_t* __restrict__ V,
+                                                           int64_t M, int64_t cn, int r, int splits,
+                                                           float* __restrict__ part) {
+  const int64_t c = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
+  const int j0 = blockIdx.y * 16;
+  const int s = blockIdx.z;
+  const int64_t per = (M + splits - 1) / splits;
+  const int64_t mb = s * per;
+  const int64_t me = (mb + per < M) ? mb + per : M;
+  float acc[16][2];
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) acc[jj][0] = acc[jj][1] = 0.0f;
+  if (c < cn) {
+    for (int64_t m = mb; m < me; ++m) {
+      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(V + m * cn + c);
+      const float v0 = __uint_as_float(v2 << 16), v1 = __uint_as_float(v2 & 0xFFFF0000u);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const float u = (j0 + jj < r) ? U[m * r + j0 + jj] : 0.0f;
+        acc[jj][0] = fmaf(u, v0, acc[jj][0]);
+        acc[jj][1] = fmaf(u, v1, acc[jj][1]);
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+      if (j0 + jj < r) {
+        float* dst = part + (static_cast<int64_t>(s) * r + j0 + jj) * cn + c;
+        dst[0] = acc[jj][0];
+        dst[1] = acc[jj][1];
+      }
+    }
+  }
+}
+
+// out = scale * sum_s part[s], summed in split order.
+__global__ void rank_final_kernel(const float* __restrict__ part, int64_t cn, int r, int splits, float scale,
+                                  float* __restrict__ out, int c_major) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(r) * cn) return;
+  int64_t j, c;
+  if (c_major) {
+    c = idx / r;
+    j = idx % r;
+  } else {
+    j = idx / cn;
+    c = idx % cn;
+  }
+  float sum = 0.0f;
+  for (int s = 0; s < splits; ++s) sum += part[(static_cast<int64_t>(s) * r + j) * cn + c];
+  out[idx] = scale * sum;
+}
+
+template <int RT>
+void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r,
+                      int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, uint16_t* p_perm,
+                      int splits) {
+  hipLaunchKernelGGL(skinny_kernel<RT>, grid, dim3(256), 0, st, P, Q, m, qn, r, rpad, scale, scale2, out_f32,
+                     out_bf16, p_perm, splits);
+}
+
+}  // namespace
+
+int rank_reduce_splits(int64_t m) {
+  int64_t s = m / 128;
+  if (s < 1) s = 1;
+  if (s > 16) s = 16;
+  return static_cast<int>(s);
+}
+
+int skinny_splits(int64_t m, int64_t qn) {
+  if (m > 16) return 1;
+  const int64_t s = (qn + 511) / 512;  // ~512 contraction elements per workgroup
+  return static_cast<int>(s < 1 ? 1 : (s > 64 ? 64 : s));
+}
+
+hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad, float scale,
+                         float scale2, float* out_f32, uint16_t* out_bf16, uint16_t* p_perm, int splits,
+                         hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((m + 15) / 16), static_cast<unsigned>(splits));
+  switch (rpad / 16) {
+    case 0: launch_skinny_rt<0>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
+    case 2: launch_skinny_rt<2>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
+    case 4: launch_skinny_rt<4>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
+    case 6: launch_skinny_rt<6>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
+    case 8: launch_skinny_rt<8>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n, int64_t k, int r, int rpad,
+                                 uint16_t* at, uint16_t* bt, hipStream_t st) {
+  const int64_t total = (k + n) * rpad;
+  hipLaunchKernelGGL(lora_transpose_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, a, b,
+                     n, k, r, rpad, at, bt);
+  return hipGetLastError();
+}
+
+hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int64_t cn, int r, float scale,
+                              int splits, float* part, float* out, int c_major, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((cn / 2 + 255) / 256), static_cast<unsigned>((r + 15) / 16),
+                  static_cast<unsigned>(splits));
+  hipLaunchKernelGGL(rank_partial_kernel, grid, dim3(256), 0, st, U, V, m, cn, r, splits, part);
+  const int64_t total = static_cast<int64_t>(r) * cn;
+  hipLaunchKernelGGL(rank_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, part, cn,
+                     r, splits, scale, out, c_major);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -1,0 +1,43 @@
+// Matrix-core helpers for gfx950 (CDNA4).
+//
+// v_mfma_f32_16x16x32_bf16: D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).
+// Operand layout used throughout (per 64-lane wave, lane = 16 * g + i):
+//   A: lane holds 8 bf16 of row i, contraction slots 8g .. 8g+7;
+//   B: lane holds 8 bf16 of column i, the same contraction slots 8g .. 8g+7;
+//   D: lane holds D[4g + v][i], v = 0..3.
+// Which physical contraction index a slot carries is up to the caller, as
+// long as A and B agree, so the kernels may feed the 8 values of a lane in
+// any fixed order.
+#pragma once
+
+#include "internal.h"
+
+namespace qlora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// 8 bf16 from row_ptr[j0 .. j0+8) with zeros at and beyond `limit`; a 16-byte
+// load when the run is whole and aligned.
+__device__ __forceinline__ u32x4 ld8_bf16_guarded(const uint16_t* row_ptr, int j0, int limit, bool vec_ok) {
+  if (j0 + 8 <= limit && vec_ok) return ld16(row_ptr + j0);
+  uint32_t w[4] = {0, 0, 0, 0};
+  for (int e = 0; e < 8; ++e) {
+    if (j0 + e < limit) w[e >> 1] |= static_cast<uint32_t>(row_ptr[j0 + e]) << (16 * (e & 1));
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+}  // namespace qlora

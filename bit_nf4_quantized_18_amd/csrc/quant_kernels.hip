@@ -1,0 +1,247 @@
+// NF4 quantize (with double quantization of the scales) and dequantize.
+//
+// Ultralytics glossary "QLoRA", section "Come funziona QLoRA": every weight is
+// a 4-bit code into 16 normal-quantile levels with one absmax scale per block
+// of 64; the per-block scales are in turn quantized to 8 bit in blocks of 256.
+// "Modulo 4: QLoRA", 4.3 b): weights first, then the scale constants.
+//
+// Both kernels stream HBM once and are bandwidth bound. This translation unit
+// is built with -ffp-contract=off and IEEE float32 division and denormals,
+// because codes, scale codes and dequantized values are bit-exact outputs.
+#include "internal.h"
+#include "nf4_lut.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kBlock = 64;
+constexpr int kGroup = 256;
+
+// Nearest level of x in [-1, 1]: bracket L[k] <= x < L[k+1] by a 4-step
+// binary search over the ascending table (held in LDS, with lv[16] = +inf),
+// then the closer of the two fp32 distances; an exact tie keeps k (the lower
+// index). Levels further away cannot tie: the gaps exceed 0.079.
+__device__ __forceinline__ uint32_t nearest_nf4(float x, const float* lv) {
+  uint32_t k = 0;
+#pragma unroll
+  for (uint32_t half = 8; half >= 1; half >>= 1) {
+    if (x >= lv[k + half]) k += half;
+  }
+  const float d_lo = x - lv[k];      // >= 0, = fl32(|x - L_k|)
+  const float d_hi = lv[k + 1] - x;  // > 0,  = fl32(|x - L_k+1|); +inf for k = 15
+  return (d_hi < d_lo) ? k + 1 : k;
+}
+
+// U_k = fl32(k / 255): correctly rounded float32 division.
+__device__ __forceinline__ float u8_level(uint32_t k) { return static_cast<float>(k) / 255.0f; }
+
+// Nearest U_k to x2 in [0, 1], lowest k on ties. The fp32 argmin lies within
+// one step of rint(255 x2), so three candidates suffice.
+__device__ __forceinline__ uint32_t nearest_u8(float x2) {
+  int k0 = static_cast<int>(rintf(x2 * 255.0f));
+  k0 = min(max(k0, 0), 255);
+  const int lo = max(k0 - 1, 0), hi = min(k0 + 1, 255);
+  uint32_t best = lo;
+  float bd = fabsf(x2 - u8_level(lo));
+  for (int k = lo + 1; k <= hi; ++k) {
+    const float d = fabsf(x2 - u8_level(k));
+    if (d < bd) {
+      bd = d;
+      best = k;
+    }
+  }
+  return best;
+}
+
+// One workgroup (256 threads) per double-quantization group of 256 blocks.
+// Wave w owns blocks [64w, 64w + 64) of the group, 8 at a time: 8 lanes per
+// block, 8 consecutive elements per lane (two 16-byte loads), so a wave reads
+// 2 KB contiguous per step. The block absmax is an 8-lane max-reduction; the
+// codes of a lane's 8 elements form one 32-bit store. Block maxima go to LDS
+// and the group maximum M_g is a workgroup reduction.
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restrict__ w, int64_t numel, int dq,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scale_codes,
+                                                           float* __restrict__ group_scale,
+                                                           float* __restrict__ absmax_out, Levels L) {
+  __shared__ float lv[17];
+  __shared__ float blk_max[kGroup];
+  __shared__ float wave_max[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid < 16) lv[tid] = L.v[tid];
+  if (tid == 16) lv[16] = __builtin_inff();
+  __syncthreads();
+
+  const int64_t nblocks = (numel + kBlock - 1) / kBlock;
+  const int64_t g = blockIdx.x;
+  const int sub = lane >> 3, part = lane & 7;
+
+  float v[8][8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int64_t b = g * kGroup + wave * 64 + it * 8 + sub;
+    const int64_t e0 = b * kBlock + part * 8;
+    if (e0 + 8 <= numel) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(w + e0);
+      const f32x4 a = __builtin_nontemporal_load(p);
+      const f32x4 c = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[it][j] = a[j];
+        v[it][4 + j] = c[j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[it][j] = (e0 + j < numel) ? w[e0 + j] : 0.0f;
+    }
+  }
+
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int bl = wave * 64 + it * 8 + sub;
+    const int64_t b = g * kGroup + bl;
+    const int64_t e0 = b * kBlock + part * 8;
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[it][j]));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    m = fmaxf(m, __shfl_xor(m, 4));
+    uint32_t packed = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = (m > 0.0f) ? v[it][j] / m : 0.0f;
+      packed |= nearest_nf4(x, lv) << (4 * j);
+    }
+    if (e0 + 8 <= numel) {
+      *reinterpret_cast<uint32_t*>(codes + e0 / 2) = packed;
+    } else if (e0 < numel) {
+      const int64_t nvalid = numel - e0;  // 1..7 elements
+      const int nbytes = static_cast<int>((nvalid + 1) / 2);
+      const uint32_t keep = (nvalid >= 8) ? 0xFFFFFFFFu : ((1u << (4 * nvalid)) - 1u);
+      packed &= keep;  // an odd count leaves the last high nibble 0
+      for (int i = 0; i < nbytes; ++i) codes[e0 / 2 + i] = static_cast<uint8_t>(packed >> (8 * i));
+    }
+    if (part == 0) blk_max[bl] = (b < nblocks) ? m : 0.0f;
+  }
+  __syncthreads();
+
+  const int64_t b = g * kGroup + tid;
+  const float a = blk_max[tid];
+  float mg = a;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mg = fmaxf(mg, __shfl_xor(mg, off));
+  if (lane == 0) wave_max[wave] = mg;
+  __syncthreads();
+  mg = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+
+  if (b < nblocks) {
+    if (absmax_out != nullptr) absmax_out[b] = a;
+    if (dq) {
+      const float x2 = (mg > 0.0f) ? a / mg : 0.0f;
+      scale_codes[b] = static_cast<uint8_t>(nearest_u8(x2));
+    }
+  }
+  if (dq && tid == 0) group_scale[g] = mg;
+}
+
+__device__ __forceinline__ float block_scale(const PackedW& w, int64_t b) {
+  if (w.dq) return u8_level(w.scale_codes[b]) * w.group_scale[b / kGroup];
+  return w.absmax[b];
+}
+
+// Dequantize: each lane turns one 32-bit word of codes (8 weights) into 8
+// outputs per step; a wave covers 256 contiguous code bytes -> 1 KB of bf16
+// (or 2 KB of fp32) contiguous. Four steps per lane, all loads first.
+template <bool kF32>
+__global__ __launch_bounds__(256) void nf4_dequantize_kernel(PackedW w, void* __restrict__ out, Levels L) {
+  __shared__ float lv[16];
+  if (threadIdx.x < 16) lv[threadIdx.x] = L.v[threadIdx.x];
+  __syncthreads();
+  const int64_t numel = w.n * w.k;
+  const int64_t nwords = (numel + 7) / 8;  // 8 codes per 32-bit word
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
+  uint32_t cw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t q = base + j * 256;
+    cw[j] = 0;
+    if (q < nwords) {
+      const int64_t byte0 = q * 4;
+      const int64_t nbytes_total = (numel + 1) / 2;
+      if (byte0 + 4 <= nbytes_total) {
+        cw[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(w.codes) + q);
+      } else {
+        for (int i = 0; i < 4; ++i)
+          if (byte0 + i < nbytes_total) cw[j] |= static_cast<uint32_t>(w.codes[byte0 + i]) << (8 * i);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t q = base + j * 256;
+    if (q >= nwords) continue;
+    const int64_t e0 = q * 8;
+    const float s = block_scale(w, e0 / kBlock);
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = lv[(cw[j] >> (4 * i)) & 0xF] * s;
+    if (e0 + 8 <= numel) {
+      if (kF32) {
+        f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + e0);
+        __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, o);
+        __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]}, o + 1);
+      } else {
+        const u32x4 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                         pack_bf16x2(f[6], f[7])};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0));
+      }
+    } else {
+      for (int i = 0; i < 8; ++i) {
+        if (e0 + i >= numel) break;
+        if (kF32) {
+          static_cast<float*>(out)[e0 + i] = f[i];
+        } else {
+          static_cast<uint16_t*>(out)[e0 + i] = static_cast<uint16_t>(bf16_rne_hi(f[i]) >> 16);
+        }
+      }
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t count) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0.0f;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const float* w, int64_t numel, int dq, uint8_t* codes, uint8_t* scale_codes,
+                           float* group_scale, float* absmax, hipStream_t s) {
+  const int64_t nblocks = (numel + kBlock - 1) / kBlock;
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  hipLaunchKernelGGL(nf4_quantize_kernel, dim3(static_cast<unsigned>(ngroups)), dim3(256), 0, s, w, numel, dq,
+                     codes, scale_codes, group_scale, absmax, nf4_table());
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream_t s) {
+  const int64_t numel = w.n * w.k;
+  const int64_t nwords = (numel + 7) / 8;
+  const unsigned grid = static_cast<unsigned>((nwords + 1023) / 1024);
+  if (out_f32) {
+    hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3(grid), dim3(256), 0, s, w, out, nf4_table());
+  } else {
+    hipLaunchKernelGGL(nf4_dequantize_kernel<false>, dim3(grid), dim3(256), 0, s, w, out, nf4_table());
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>((count + 255) / 256)), dim3(256), 0, st, p,
+                     count);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

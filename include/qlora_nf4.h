@@ -1,0 +1,176 @@
+/*
+ * qlora_nf4.h -- C ABI of the MI355X (gfx950) QLoRA NF4 linear layer.
+ *
+ * What the library computes (pages cited by title and section):
+ *   - Ultralytics glossary "QLoRA", section "Come funziona QLoRA":
+ *       NF4 bullet: each weight is a 4-bit code pointing at one of 16 levels
+ *       placed at normal quantiles; every block of 64 weights has one absmax
+ *       scale. Double-quantization bullet: the per-block scales are themselves
+ *       quantized to 8 bit in blocks of 256 (0.5 -> ~0.127 bit/param).
+ *       Forward/backward paragraph: every frozen layer dequantizes its NF4
+ *       weights to bfloat16 right before the matmul and adds the LoRA path;
+ *       the backward goes through the dequantized weights but only the two
+ *       LoRA matrices receive gradients.
+ *   - "LoRA y QLoRA en Profundidad", sections "La Idea Central" and "Alpha":
+ *       W is d_out x d_in, A is r x d_in, B is d_out x r, and the adapter
+ *       contributes (alpha / r) * B @ A.
+ *   - "Modulo 4: QLoRA", section 4.3 b): the weights are quantized to 4 bit,
+ *       then the scale constants to 8 bit.
+ *
+ * Numeric conventions (the readings taken where the pages are silent):
+ *   - levels: 16 float32 values, ascending, level 7 is +0.0, levels 0 and 15
+ *     are -1 and +1 (see qlora_nf4_levels);
+ *   - block b covers elements [64 b, 64 b + 64) of the row-major flattening
+ *     (the last block may be partial); group g covers blocks [256 g, 256 g + 256);
+ *   - a_b = max |w| over block b; x = w / a_b (correctly rounded float32);
+ *     code = argmin_k fl32(|x - L_k|), lowest k on ties; an all-zero block
+ *     has code 7 everywhere;
+ *   - packing: byte i holds element 2i in bits 0..3 and element 2i+1 in bits
+ *     4..7; an odd element count leaves the last high nibble 0;
+ *   - double quantization: M_g = max a_b over group g; c2_b = argmin_k
+ *     fl32(|a_b / M_g - U_k|) with U_k = fl32(k / 255), lowest k on ties
+ *     (c2_b = 0 when M_g = 0); decoded scale s_b = fl32(U[c2_b] * M_g);
+ *     without double quantization s_b = a_b stored as float32;
+ *   - dequantized weight: w32 = fl32(L[code] * s_b); w16 = bf16 round-to-
+ *     nearest-even of w32. Codes, c2, M_g, w32 and w16 are bit-exact with the
+ *     CPU oracle;
+ *   - linear: s = fl32(alpha / r); Y = X W16^T + s (X A^T) B^T; bf16 inputs,
+ *     float32 accumulation, bf16 Y and dX, float32 H, dA and dB.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, 16-byte aligned, row-major,
+ *     owned by the caller. The library never allocates or frees caller memory
+ *     and keeps no state besides a constant level table built once on the host.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream). No
+ *     host synchronisation happens inside a call. Results are valid once the
+ *     stream reaches that point.
+ *   - Argument errors are detected on the host, before anything is enqueued,
+ *     and returned as a negative status; QLORA_ERR_HIP reports a failed
+ *     launch (hipGetLastError). Nothing is thrown across the ABI. Calls are
+ *     thread-safe; calls that write the same buffers must be ordered by the
+ *     caller.
+ *   - Weights must be finite; non-finite weights give undefined codes.
+ */
+#ifndef QLORA_NF4_H_
+#define QLORA_NF4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  QLORA_ERR_SHAPE = -2,       /* a size is negative / zero where not allowed,   */
+                              /* or, for the linear entry points, k % 64 != 0   */
+                              /* or n % 16 != 0                                 */
+  QLORA_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned               */
+  QLORA_ERR_UNSUPPORTED = -4, /* r > QLORA_MAX_RANK, unknown dtype or flag      */
+  QLORA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required        */
+  QLORA_ERR_HIP = -6          /* a kernel launch failed                         */
+} qlora_status;
+
+typedef enum { QLORA_BF16 = 0, QLORA_F32 = 1 } qlora_dtype;
+
+#define QLORA_BLOCK 64     /* weights per absmax block              */
+#define QLORA_DQ_GROUP 256 /* blocks per double-quantization group  */
+#define QLORA_MAX_RANK 128 /* largest LoRA rank r the kernels take  */
+
+/* A packed NF4 weight W (n x k, row-major, numel = n * k). Device pointers.
+ *   codes        : ceil(numel / 2) bytes, packing as above.
+ *   scale_codes  : double_quant = 1: ceil(numel / 64) uint8 codes c2_b.
+ *   group_scale  : double_quant = 1: ceil(ceil(numel / 64) / 256) float M_g.
+ *   absmax       : double_quant = 0: ceil(numel / 64) float a_b.
+ * Pointers not used by the selected mode may be NULL. */
+typedef struct {
+  int64_t n, k;
+  const uint8_t* codes;
+  const uint8_t* scale_codes;
+  const float* group_scale;
+  const float* absmax;
+  int32_t double_quant;
+} qlora_nf4_weight;
+
+/* Quantize `numel` float32 weights `w` (any numel >= 1; partial last block and
+ * group allowed). Ultralytics glossary "QLoRA", "Come funziona QLoRA" (NF4 and
+ * double-quantization bullets); "Modulo 4: QLoRA" 4.3 b) for the order
+ * (weights with their exact absmax first, then the scales).
+ * Outputs (caller-allocated device buffers):
+ *   codes       : ceil(numel/2) bytes.
+ *   double_quant = 1: scale_codes (ceil(numel/64) bytes) and group_scale
+ *     (ceil(ceil(numel/64)/256) floats) are required; absmax may be NULL, and
+ *     if given receives the exact float a_b.
+ *   double_quant = 0: absmax (ceil(numel/64) floats) is required;
+ *     scale_codes and group_scale are ignored.
+ * Errors: NULL / ALIGN / SHAPE (numel < 1) / UNSUPPORTED (flag not 0 or 1) / HIP. */
+qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant, uint8_t* codes,
+                                uint8_t* scale_codes, float* group_scale, float* absmax,
+                                hipStream_t stream);
+
+/* Dequantize a packed weight to bf16 (w16) or float32 (w32), n*k elements,
+ * row-major, into `out`. Ultralytics glossary "QLoRA", "Come funziona QLoRA"
+ * (restore = level[code] * scale; dequantize to bfloat16 before the matmul).
+ * Any n, k >= 1 (k need not be a multiple of 64 here).
+ * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED (dtype) / HIP. */
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dtype, void* out,
+                                  hipStream_t stream);
+
+/* Forward: Y = X W16^T + s (X A^T) B^T with s = fl32(alpha / r).
+ * Ultralytics glossary "QLoRA", "Come funziona QLoRA" (forward paragraph);
+ * "LoRA y QLoRA en Profundidad", "La Idea Central" / "Alpha".
+ *   w     : packed NF4 weight, n x k, k % 64 == 0 and n % 16 == 0.
+ *   x     : bf16 (uint16 bit patterns) m x k.
+ *   a     : bf16 r x k; b : bf16 n x r. r = 0 (a, b NULL) means base only.
+ *   y     : bf16 m x n output.
+ *   h_out : optional float32 m x r output of H = X A^T (pass it to the
+ *           backward to skip recomputing H); may be NULL.
+ *   ws    : device workspace of at least qlora_linear_workspace_bytes(m,n,k,r)
+ *           bytes (may be NULL when that is 0). Contents are scratch.
+ * m = 0 is a no-op. m <= 16 takes the decode (GEMV) kernels, larger m the
+ * fused dequant-GEMM. Y does not depend on which path runs beyond float32
+ * accumulation order.
+ * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED (r > QLORA_MAX_RANK) / WORKSPACE / HIP. */
+qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t m,
+                              const uint16_t* a, const uint16_t* b, int r, float alpha,
+                              uint16_t* y, float* h_out, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* Backward of the forward above for L with dL/dY = dy (bf16 m x n).
+ * Ultralytics glossary "QLoRA", "Come funziona QLoRA": gradients flow through
+ * the dequantized frozen weight; only A and B get gradients (no dW).
+ *   dX = dY W16 + dH A   (bf16 m x k; dx may be NULL to skip it)
+ *   dA = dH^T X          (float32 r x k, overwritten)
+ *   dB = s dY^T H        (float32 n x r, overwritten)
+ * with H = X A^T and dH = s dY B. h_saved (float32 m x r, from the forward's
+ * h_out) may be NULL, in which case H is recomputed. With r = 0, only dX is
+ * produced (a, b, da, db ignored). m = 0 writes zeros to dA and dB.
+ * dA and dB are computed in a fixed order: results are run-to-run identical.
+ * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED / WORKSPACE / HIP. */
+qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                              int64_t m, const uint16_t* a, const uint16_t* b, int r, float alpha,
+                              const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* Bytes of device workspace that qlora_linear_fwd and qlora_linear_bwd need
+ * for these sizes (the larger of the two); 0 if none. Host only, no GPU use. */
+size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+
+/* Static, NUL-terminated description of a status. Host only. */
+const char* qlora_status_string(qlora_status status);
+
+/* Copy the 16 float32 NF4 levels the kernels use into out16 (host memory).
+ * The table is built on the host from the standard-normal quantile at the
+ * offset 0.9677083 (Ultralytics glossary "QLoRA", the NF4-vs-INT4 example).
+ * Returns 16, or QLORA_ERR_NULL. Host only, no GPU use. */
+int qlora_nf4_levels(float out16[16]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H_ */

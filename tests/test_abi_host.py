@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every declared symbol, builds the same level table as the oracle, and rejects
+bad arguments before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from bit_nf4_quantized_18_amd import binding
+from oracle import nf4 as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qlora_nf4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load()
+    names = declared_functions()
+    assert set(names) == set(binding.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_levels_bit_equal_to_oracle():
+    got = np.array(binding.levels(), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), O.nf4_levels().view(np.uint32))
+
+
+def test_levels_null_pointer():
+    lib = binding.load()
+    assert lib.qlora_nf4_levels(None) == -1
+
+
+def test_status_strings():
+    for st in binding.STATUS:
+        assert binding.status_string(st)
+    assert "workspace" in binding.status_string(-5)
+
+
+def test_workspace_sizes():
+    assert binding.workspace_bytes(0, 4096, 4096, 16) == 0
+    assert binding.workspace_bytes(16, 4096, 4096, 200) == 0  # rank beyond the maximum
+    a = binding.workspace_bytes(2048, 4096, 4096, 16)
+    b = binding.workspace_bytes(4096, 4096, 4096, 16)
+    assert 0 < a < b
+    assert binding.workspace_bytes(1, 4096, 4096, 0) > 0  # decode path reorders X
+
+
+# Fake but aligned "device" addresses: every call below must fail validation
+# on the host, before any launch.
+P = 1 << 20
+
+
+def wstruct(n=64, k=64, dq=1, codes=P, sc=P, gs=P, am=None):
+    return binding.NF4WeightC(n, k, codes, sc, gs, am, dq)
+
+
+def test_quantize_argument_errors():
+    lib = binding.load()
+    q = lib.qlora_nf4_quantize
+    assert q(P, 100, 2, P, P, P, None, None) == -4
+    assert q(None, 100, 1, P, P, P, None, None) == -1
+    assert q(P, 100, 1, P, None, P, None, None) == -1
+    assert q(P, 100, 0, P, None, None, None, None) == -1
+    assert q(P, 0, 1, P, P, P, None, None) == -2
+    assert q(P, -5, 1, P, P, P, None, None) == -2
+    assert q(P + 4, 100, 1, P, P, P, None, None) == -3
+    assert q(P, 100, 1, P + 8, P, P, None, None) == -3
+
+
+def test_dequantize_argument_errors():
+    lib = binding.load()
+    d = lib.qlora_nf4_dequantize
+    w = wstruct()
+    assert d(ctypes.byref(w), 7, P, None) == -4
+    assert d(ctypes.byref(w), 0, None, None) == -1
+    assert d(ctypes.byref(w), 0, P + 2, None) == -3
+    assert d(None, 0, P, None) == -1
+    w = wstruct(dq=0, am=None)
+    assert d(ctypes.byref(w), 0, P, None) == -1
+    w = wstruct(n=0)
+    assert d(ctypes.byref(w), 0, P, None) == -2
+    w = wstruct(dq=3)
+    assert d(ctypes.byref(w), 0, P, None) == -4
+
+
+def test_linear_argument_errors():
+    lib = binding.load()
+    f, b = lib.qlora_linear_fwd, lib.qlora_linear_bwd
+    ok = wstruct(n=64, k=128)
+    ws_need = binding.workspace_bytes(32, 64, 128, 8)
+    assert f(ctypes.byref(wstruct(n=64, k=100)), P, 4, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
+    assert f(ctypes.byref(wstruct(n=60, k=128)), P, 4, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
+    assert f(ctypes.byref(ok), P, 32, P, P, 200, 16.0, P, None, P, ws_need, None) == -4
+    assert f(ctypes.byref(ok), P, 32, P, P, -1, 16.0, P, None, P, ws_need, None) == -2
+    assert f(ctypes.byref(ok), P, -3, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
+    assert f(ctypes.byref(ok), None, 32, P, P, 8, 16.0, P, None, P, ws_need, None) == -1
+    assert f(ctypes.byref(ok), P, 32, None, P, 8, 16.0, P, None, P, ws_need, None) == -1
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P + 2, None, P, ws_need, None) == -3
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, None, P, ws_need - 1, None) == -5
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, None, None, 0, None) == -5
+    assert f(ctypes.byref(ok), P, 0, None, None, 8, 16.0, None, None, None, 0, None) == 0  # m = 0: no-op
+    # backward
+    assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, None, P, None, P, P, ws_need, None) == -1
+    assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, None, P, P, P, P, 16, None) == -5
+    assert b(ctypes.byref(ok), P, None, 32, P, P, 8, 16.0, None, P, P, P, P, ws_need, None) == -1
+    assert b(ctypes.byref(ok), P, P, 32, P, P, 300, 16.0, None, P, P, P, P, ws_need, None) == -4

@@ -1,0 +1,196 @@
+"""GPU parity of qlora_linear_fwd / qlora_linear_bwd against the float64
+oracle (tolerance: max|gpu - ref| / max|ref| <= 1e-2 per tensor), plus the
+invariants that hold exactly on the GPU (B = 0 equals the base-only call,
+run-to-run determinism, saved vs recomputed H)."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_cases import TOL, f64, layer_inputs, oracle_weight, rel, say
+from oracle import linear as OL
+
+pytestmark = pytest.mark.gpu
+
+# (name, m, n, k, r, alpha, dq)
+FWD_BWD_CASES = [
+    ("single_256_m16_r8", 16, 256, 256, 8, 16.0, True),         # decode path (m <= 16)
+    ("single_256_m17_r8", 17, 256, 256, 8, 16.0, True),         # smallest prefill-path m
+    ("m1_r8", 1, 256, 256, 8, 16.0, True),
+    ("m4_r16", 4, 512, 320, 16, 32.0, True),
+    ("ragged_m300_n272_k320_r8", 300, 272, 320, 8, 16.0, True),  # ragged m, n tail, odd number of k-steps
+    ("base_only_m33", 33, 256, 192, 0, 0.0, True),
+    ("rank24", 40, 128, 256, 24, 48.0, True),                   # r not a multiple of 32
+    ("rank5_unaligned", 40, 128, 256, 5, 10.0, True),           # r % 8 != 0: guarded loads
+    ("rank64_alpha16", 64, 256, 512, 64, 16.0, True),            # s = 0.25
+    ("rank128", 48, 256, 256, 128, 64.0, True),
+    ("no_dq", 96, 384, 448, 16, 32.0, False),
+    ("decode_no_dq_m3", 3, 384, 448, 16, 32.0, False),
+    ("decode_m16_r0", 16, 256, 256, 0, 0.0, True),
+]
+
+
+def _run_case(gpu_lib, name, m, n, k, r, alpha, dq, check_bwd=True):
+    import torch
+
+    w, x, a, b, dy = layer_inputs(n, k, m, r, name)
+    q_ref, w16 = oracle_weight(w, dq)
+    say(f"[linear] case={name} m={m} n={n} k={k} r={r} dq={dq}")
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda(), double_quant=dq)
+    xc, dyc = x.cuda(), dy.cuda()
+    ac = a.cuda() if r else None
+    bc = b.cuda() if r else None
+    y, h = gpu_lib.linear_fwd(q, xc, ac, bc, alpha)
+    torch.cuda.synchronize()
+    y_ref, h_ref = OL.linear_fwd(f64(x), w16, f64(a) if r else None, f64(b) if r else None, alpha, r)
+    ey = rel(f64(y), y_ref)
+    say(f"   fwd rel err y={ey:.2e}")
+    assert ey <= TOL
+    if r:
+        eh = rel(f64(h), h_ref)
+        assert eh <= TOL, eh
+    if not check_bwd:
+        return
+    dx, da, db = gpu_lib.linear_bwd(q, xc, dyc, ac, bc, alpha, h=h)
+    torch.cuda.synchronize()
+    dx_ref, da_ref, db_ref = OL.linear_bwd(f64(x), w16, f64(a) if r else None, f64(b) if r else None, f64(dy),
+                                           alpha, r)
+    edx = rel(f64(dx), dx_ref)
+    msg = f"   bwd rel err dx={edx:.2e}"
+    assert edx <= TOL, msg
+    if r:
+        eda, edb = rel(f64(da), da_ref), rel(f64(db), db_ref)
+        msg += f" da={eda:.2e} db={edb:.2e}"
+        assert eda <= TOL and edb <= TOL, msg
+        # H recomputed inside the backward gives the same gradients bit for bit
+        dx2, da2, db2 = gpu_lib.linear_bwd(q, xc, dyc, ac, bc, alpha, h=None)
+        torch.cuda.synchronize()
+        assert rel(f64(da2), da_ref) <= TOL and rel(f64(db2), db_ref) <= TOL
+        assert torch.equal(dx2, dx)
+    say(msg)
+
+
+@pytest.mark.parametrize("case", FWD_BWD_CASES, ids=[c[0] for c in FWD_BWD_CASES])
+def test_linear_parity(gpu_lib, case):
+    _run_case(gpu_lib, *case)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+@pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096)])
+def test_decode_7b_shapes(gpu_lib, m, n, k):
+    """The decode (GEMV) path at the 7B layer shapes, forward only."""
+    _run_case(gpu_lib, f"decode_{n}x{k}_m{m}", m, n, k, 16, 32.0, True, check_bwd=False)
+
+
+@pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
+def test_7b_layer_full(gpu_lib, n, k):
+    """A full 2048-token 7B-shaped layer, forward and backward, checked on
+    every output element."""
+    _run_case(gpu_lib, f"layer7b_{n}x{k}", 2048, n, k, 16, 32.0, True)
+
+
+def test_65b_layer_sampled(gpu_lib):
+    """65B-shaped gate/up projection (22016 x 8192, r = 64, alpha = 16,
+    Student-t weights, 4096 tokens): dA and dB checked in full, Y and dX on
+    64 sampled token rows."""
+    import torch
+
+    m, n, k, r, alpha = 4096, 22016, 8192, 64, 16.0
+    tag = "layer65b_gate"
+    w = synth.student_t((n, k), 4, 0.02, tag, "W")
+    from gpu_cases import to_bf16
+    x = to_bf16(synth.normal((m, k), 1.0, tag, "X"))
+    a = to_bf16(synth.normal((r, k), 1.0 / r, tag, "A"))
+    b = to_bf16(synth.normal((n, r), 0.01, tag, "B"))
+    dy = to_bf16(synth.normal((m, n), 1.0, tag, "dY"))
+    say(f"[linear] case={tag} quantize")
+    _, w16 = oracle_weight(w, True)
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+    del w
+    xc, ac, bc, dyc = x.cuda(), a.cuda(), b.cuda(), dy.cuda()
+    say(f"[linear] case={tag} fwd")
+    y, h = gpu_lib.linear_fwd(q, xc, ac, bc, alpha)
+    say(f"[linear] case={tag} bwd")
+    dx, da, db = gpu_lib.linear_bwd(q, xc, dyc, ac, bc, alpha, h=h)
+    torch.cuda.synchronize()
+    rows = np.random.Generator(np.random.PCG64(5)).choice(m, 64, replace=False)
+    xs, dys = f64(x)[rows], f64(dy)[rows]
+    a64, b64 = f64(a), f64(b)
+    y_ref, _ = OL.linear_fwd(xs, w16, a64, b64, alpha, r)
+    dx_ref, _, _ = OL.linear_bwd(xs, w16, a64, b64, dys, alpha, r)
+    ey, edx = rel(f64(y)[rows], y_ref), rel(f64(dx)[rows], dx_ref)
+    s = OL.lora_scale(alpha, r)
+    x64 = f64(x)
+    h_ref = x64 @ a64.T
+    dh_ref = s * (f64(dy) @ b64)
+    da_ref = dh_ref.T @ x64
+    db_ref = s * (f64(dy).T @ h_ref)
+    eda, edb = rel(f64(da), da_ref), rel(f64(db), db_ref)
+    say(f"   rel err y={ey:.2e} dx={edx:.2e} da={eda:.2e} db={edb:.2e}")
+    assert max(ey, edx, eda, edb) <= TOL
+
+
+def test_b_zero_equals_base_only(gpu_lib):
+    """B = 0 (the LoRA init) gives exactly the base-only output, on both paths."""
+    import torch
+
+    for m in (8, 200):
+        w, x, a, b, dy = layer_inputs(256, 320, m, 16, f"bzero{m}")
+        say(f"[linear] B=0 m={m}")
+        q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+        xc = x.cuda()
+        y0, _ = gpu_lib.linear_fwd(q, xc)
+        y1, _ = gpu_lib.linear_fwd(q, xc, a.cuda(), torch.zeros_like(b).cuda(), 32.0)
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)
+        _, da, db = gpu_lib.linear_bwd(q, xc, dy.cuda(), a.cuda(), torch.zeros_like(b).cuda(), 32.0)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(da).item() == 0 and torch.count_nonzero(db).item() > 0
+
+
+def test_run_twice_bit_equal(gpu_lib):
+    import torch
+
+    w, x, a, b, dy = layer_inputs(512, 512, 600, 16, "det")
+    say("[linear] determinism")
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+    args = (x.cuda(), a.cuda(), b.cuda())
+    y1, h1 = gpu_lib.linear_fwd(q, *args, 32.0)
+    y2, h2 = gpu_lib.linear_fwd(q, *args, 32.0)
+    g1 = gpu_lib.linear_bwd(q, args[0], dy.cuda(), args[1], args[2], 32.0, h=h1)
+    g2 = gpu_lib.linear_bwd(q, args[0], dy.cuda(), args[1], args[2], 32.0, h=h1)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(h1, h2)
+    for u, v in zip(g1, g2):
+        assert torch.equal(u, v)
+
+
+def test_empty_batch(gpu_lib):
+    """m = 0: the forward is a no-op; the backward writes zero dA and dB."""
+    import torch
+
+    w, x, a, b, dy = layer_inputs(128, 128, 4, 8, "empty")
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+    say("[linear] m=0")
+    x0 = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    dy0 = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    y, h = gpu_lib.linear_fwd(q, x0, a.cuda(), b.cuda(), 16.0)
+    assert y.shape == (0, 128)
+    dx, da, db = gpu_lib.linear_bwd(q, x0, dy0, a.cuda(), b.cuda(), 16.0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(da).item() == 0 and torch.count_nonzero(db).item() == 0
+
+
+def test_fused_gemm_matches_dequantize_then_matmul(gpu_lib):
+    """The fused kernel's base product equals an fp32 matmul of the separately
+    dequantized bf16 weight (a check of the in-loop dequantization)."""
+    import torch
+
+    w, x, _, _, _ = layer_inputs(1024, 1024, 512, 0, "fusedvsdeq")
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+    xc = x.cuda()
+    say("[linear] fused vs dequantize+matmul")
+    y, _ = gpu_lib.linear_fwd(q, xc)
+    w16 = gpu_lib.dequantize(q, torch.bfloat16)
+    ref = xc.float() @ w16.float().t()
+    torch.cuda.synchronize()
+    assert rel(f64(y), f64(ref)) <= 4e-3

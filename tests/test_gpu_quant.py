@@ -1,0 +1,125 @@
+"""GPU parity of qlora_nf4_quantize / qlora_nf4_dequantize: codes, scale codes,
+group maxima, exact absmax and dequantized bf16/fp32 values must be bit-equal
+to the oracle's."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import nf4 as O
+from gpu_cases import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _ties_case():
+    """Blocks whose normalised values sit within a few ulp of every decision
+    midpoint (exact fp32 distance ties included)."""
+    L = O.nf4_levels()
+    a = np.float32(0.0371)
+    xs = []
+    for k in range(15):
+        v = np.float32((np.float64(L[k]) + np.float64(L[k + 1])) / 2)
+        for _ in range(4):
+            v = np.nextafter(v, np.float32(-2))
+        for _ in range(9):
+            xs.append(v)
+            v = np.nextafter(v, np.float32(2))
+    w = (np.array(xs, np.float64) * np.float64(a)).astype(np.float32)
+    w = np.clip(w, -a, a)
+    w = np.concatenate([w, np.zeros((-w.size) % 63, np.float32)]).reshape(-1, 63)
+    w = np.concatenate([np.full((w.shape[0], 1), a, np.float32), w], axis=1)  # absmax a in every block
+    return w.reshape(-1)
+
+
+def _denormal_case():
+    rng = np.random.Generator(np.random.PCG64(31))
+    w = (rng.standard_normal(64 * 512) * 1e-39).astype(np.float32)  # subnormal weights and scales
+    w[64 * 100: 64 * 101] = 0.0
+    w[64 * 200: 64 * 300] *= np.float32(1e30)
+    return w
+
+
+def _zeros_case():
+    w = synth.normal(64 * 256 * 3 + 64 * 5, 0.02, "zeros")
+    w[: 64 * 256] = 0.0           # a whole zero group
+    w[64 * 600: 64 * 601] = 0.0   # a zero block
+    w[-10:] = -0.0
+    return w
+
+
+CASES = {
+    "single_256x256": lambda: synth.normal((256, 256), 0.02, "q", "single"),
+    "attn_4096x4096_outliers": lambda: synth.with_outliers(synth.normal((4096, 4096), 0.02, "q", "attn"),
+                                                            0.001, 10.0, "q", "attn"),
+    "mlp_11008x4096_outliers": lambda: synth.with_outliers(synth.normal((11008, 4096), 0.02, "q", "mlp"),
+                                                            0.001, 10.0, "q", "mlp"),
+    "student_t_2048x8192": lambda: synth.student_t((2048, 8192), 4, 0.02, "q", "t"),
+    "ragged_1d": lambda: synth.normal(64 * 257 + 37, 0.02, "q", "ragged"),
+    "numel_1": lambda: np.array([0.3], np.float32),
+    "numel_3": lambda: np.array([0.3, -1.0, 2e-3], np.float32),
+    "numel_63": lambda: synth.normal(63, 1.0, "q", "63"),
+    "numel_65": lambda: synth.normal(65, 1.0, "q", "65"),
+    "ties": _ties_case,
+    "denormals": _denormal_case,
+    "zeros": _zeros_case,
+}
+
+
+def _u8(t):
+    return t.cpu().numpy().view(np.uint8)
+
+
+def _f32bits(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+@pytest.mark.parametrize("dq", [True, False])
+@pytest.mark.parametrize("name", list(CASES))
+def test_quantize_dequantize_bit_exact(gpu_lib, name, dq):
+    import torch
+
+    w = CASES[name]()
+    say(f"[quantize] case={name} dq={dq} numel={w.size}")
+    ref = O.quantize(w.reshape(-1), dq)
+    wt = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    q = gpu_lib.quantize(wt, double_quant=dq, keep_absmax=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u8(q.codes), ref["codes"])
+    assert np.array_equal(_f32bits(q.absmax), ref["absmax"].view(np.uint32))
+    if dq:
+        assert np.array_equal(_u8(q.scale_codes), ref["scale_codes"])
+        assert np.array_equal(_f32bits(q.group_scale), ref["group_scale"].view(np.uint32))
+    # dequantize (without the exact absmax in DQ mode: the kernel must use c2 and M_g)
+    if dq:
+        q.absmax = None
+    w32_ref, bits_ref = O.dequantize(ref)
+    say(f"[dequantize] case={name} dq={dq}")
+    d16 = gpu_lib.dequantize(q, torch.bfloat16)
+    d32 = gpu_lib.dequantize(q, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(d16.reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16), bits_ref)
+    assert np.array_equal(d32.reshape(-1).cpu().numpy().view(np.uint32), w32_ref.view(np.uint32))
+
+
+def test_dequantize_2d_non_multiple_of_64(gpu_lib):
+    """Dequantize takes any n x k; blocks still follow the flattened order."""
+    import torch
+
+    w = synth.normal((37, 50), 0.02, "q", "37x50")
+    say("[dequantize] 37x50")
+    ref = O.quantize(w.reshape(-1), True)
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+    w32_ref, bits_ref = O.dequantize(ref)
+    d16 = gpu_lib.dequantize(q, torch.bfloat16)
+    assert d16.shape == (37, 50)
+    assert np.array_equal(d16.reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16), bits_ref)
+
+
+def test_quantize_deterministic(gpu_lib):
+    import torch
+
+    w = torch.from_numpy(synth.normal((1024, 1024), 0.02, "q", "det")).cuda()
+    say("[quantize] determinism")
+    a = gpu_lib.quantize(w)
+    b = gpu_lib.quantize(w)
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scale_codes, b.scale_codes)
