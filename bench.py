@@ -1,0 +1,354 @@
+"""Benchmark of the QLoRA NF4 linear layer on one MI355X.
+
+Step = one training step of the 7B-shaped layer set (q/k/v/o 4096x4096,
+gate/up 11008x4096, down 4096x11008; 2048 tokens; LoRA r=16, alpha=32 on all
+seven): forward (H saved) + backward (dX, dA, dB) of every linear, captured in
+one HIP graph and replayed. ``value`` is its algorithmic TFLOP/s.
+
+In the same run (reported under "parts"):
+  * decode GEMV GB/s at 1/4/16 tokens on 4096x4096 and 11008x4096 (LoRA r=16),
+    rotating over > 2 GB of distinct packed copies so the 256 MB
+    Infinity Cache cannot serve the weights;
+  * dequantize (bf16) and quantize (double quant) GB/s on the same shapes;
+  * the fused dequant-GEMM kernels timed per launch with HIP events (base-only
+    calls, which launch exactly that kernel) against the bf16 MFMA peak;
+  * the CPU oracle on a bounded sample (the "cpu_baseline").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NF4 linear fwd+bwd TFLOP/s and GEMV GB/s (7B-shaped), % of roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+ROT_BYTES = 2.2e9  # > 8x the 256 MB Infinity Cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemv_bytes(m, n, k, r):
+    nk = n * k
+    return nk * (0.5 + 1 / 64 + 1 / 4096) + 2 * m * k + 2 * m * n + 2 * r * (k + n)
+
+
+def fwd_flops(m, n, k, r):
+    return 2 * m * n * k + 2 * m * r * (k + n)
+
+
+def bwd_flops(m, n, k, r):
+    # dX = dY W (2mnk) + dH A (2mrk); dH = s dY B (2mnr); dA = dH^T X (2mrk); dB = s dY^T H (2mnr)
+    return 2 * m * n * k + 4 * m * r * k + 4 * m * n * r
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", default="", help="comma list of parts to run (train,gemm,decode,dequant,quant,cpu)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    only = set(filter(None, args.only.split(",")))
+    want = (lambda p: not only or p in only)
+
+    import numpy as np
+    import torch
+
+    import bit_nf4_quantized_18_amd as qn
+    import synth
+
+    qn.load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    wl = synth.LAYERS_7B
+    M, R, ALPHA = wl.m, wl.r, wl.alpha
+    parts = {}
+
+    # ---------------------------------------------------------------- setup
+    log("[bench] quantizing the 7B layer set")
+    layers = []
+    for lay in wl.layers:
+        w = torch.from_numpy(synth.weight(wl, lay)).to(dev)
+        q = qn.quantize(w)
+        del w
+        x = torch.from_numpy(synth.activations(wl, lay)).to(torch.bfloat16).to(dev)
+        a = torch.from_numpy(synth.lora_a(wl, lay)).to(torch.bfloat16).to(dev)
+        b = torch.from_numpy(synth.lora_b(wl, lay)).to(torch.bfloat16).to(dev)
+        dy = torch.from_numpy(synth.grad_output(wl, lay)).to(torch.bfloat16).to(dev)
+        nbytes = qn.workspace_bytes(M, lay.n, lay.k, R)
+        layers.append(dict(
+            lay=lay, q=q, x=x, a=a, b=b, dy=dy,
+            y=torch.empty((M, lay.n), dtype=torch.bfloat16, device=dev),
+            h=torch.empty((M, R), dtype=torch.float32, device=dev),
+            dx=torch.empty((M, lay.k), dtype=torch.bfloat16, device=dev),
+            da=torch.empty((R, lay.k), dtype=torch.float32, device=dev),
+            db=torch.empty((lay.n, R), dtype=torch.float32, device=dev),
+            ws=torch.empty(nbytes, dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+
+    def train_step():
+        for L in layers:
+            qn.linear_fwd(L["q"], L["x"], L["a"], L["b"], ALPHA, out=L["y"], h_out=L["h"], ws=L["ws"])
+            qn.linear_bwd(L["q"], L["x"], L["dy"], L["a"], L["b"], ALPHA, h=L["h"], dx=L["dx"], da=L["da"],
+                          db=L["db"], ws=L["ws"])
+
+    step_fwd = sum(fwd_flops(M, L["lay"].n, L["lay"].k, R) for L in layers)
+    step_bwd = sum(bwd_flops(M, L["lay"].n, L["lay"].k, R) for L in layers)
+    step_flops = step_fwd + step_bwd
+
+    # ------------------------------------------------------- training step
+    value = ms_step = None
+    if want("train"):
+        log("[bench] training step: capture")
+        train_step()  # eager warm-up (also loads every kernel)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            train_step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] training step: timing {args.steps} steps")
+        t0 = time.perf_counter()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(args.steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_step = e0.elapsed_time(e1) / args.steps
+        value = step_flops / (ms_step * 1e-3) / 1e12
+        parts["train_step"] = {"ms_per_step": ms_step, "tflops": value, "gflop_per_step": step_flops / 1e9,
+                               "frac_bf16_peak": value / BF16_PEAK_TFLOPS, "wall_s": wall}
+        log(f"[bench] training step {ms_step:.3f} ms  {value:.1f} TFLOP/s")
+        del g
+
+    # ------------------------------------------- fused dequant-GEMM kernels
+    roofline = None
+    if want("gemm"):
+        log("[bench] fused dequant-GEMM kernels, per launch")
+        res = {}
+        for kind in ("fwd", "dx"):
+            tot_flops, tot_ms, per = 0.0, 0.0, []
+            for L in layers:
+                lay = L["lay"]
+                reps = 10
+                call = (lambda: qn.linear_fwd(L["q"], L["x"], out=L["y"], ws=L["ws"])) if kind == "fwd" else \
+                    (lambda: qn.linear_bwd(L["q"], L["x"], L["dy"], dx=L["dx"], ws=L["ws"]))
+                call()
+                torch.cuda.synchronize()
+                pairs = []
+                for _ in range(reps):
+                    s0, s1 = ev(), ev()
+                    s0.record()
+                    call()
+                    s1.record()
+                    pairs.append((s0, s1))
+                torch.cuda.synchronize()
+                ms = sum(a.elapsed_time(b) for a, b in pairs) / reps
+                fl = 2.0 * M * lay.n * lay.k
+                tot_flops += fl
+                tot_ms += ms
+                per.append({"layer": lay.name, "n": lay.n, "k": lay.k, "ms": ms, "tflops": fl / ms / 1e9})
+            ach = tot_flops / tot_ms / 1e9
+            res[kind] = {"kernel": f"nf4_gemm_kernel<{'true' if kind == 'dx' else 'false'}>", "achieved_tflops": ach,
+                         "frac": ach / BF16_PEAK_TFLOPS, "avg_launch_ms": tot_ms / len(layers), "per_layer": per}
+            log(f"[bench] gemm {kind}: {ach:.1f} TFLOP/s ({100 * ach / BF16_PEAK_TFLOPS:.1f}% of bf16 peak)")
+        parts["fused_gemm"] = res
+        roofline = {"bound": "mfma", "achieved": res["fwd"]["achieved_tflops"], "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": res["fwd"]["frac"], "traffic": None,
+                    "kernel": res["fwd"]["kernel"],
+                    "per_launch_gflop": step_fwd_base(layers, M) / len(layers) / 1e9,
+                    "avg_launch_ms": res["fwd"]["avg_launch_ms"]}
+
+    # ---------------------------------------------------------- decode GEMV
+    shapes = [(4096, 4096), (11008, 4096)]
+    if want("decode"):
+        dec = []
+        for (n, k) in shapes:
+            lay = synth.Linear(f"{n}x{k}", n, k)
+            w = torch.from_numpy(synth.weight(synth.DECODE_7B, synth.DECODE_7B.layers[0 if n == 4096 else 1]))
+            q0 = qn.quantize(w.to(dev))
+            del w
+            per_copy = q0.codes.numel() + q0.scale_codes.numel() + 4 * q0.group_scale.numel()
+            copies = int(ROT_BYTES // per_copy) + 1
+            log(f"[bench] decode {n}x{k}: {copies} packed copies ({copies * per_copy / 1e9:.2f} GB)")
+            pool = [qn.PackedNF4(n, k, q0.codes.clone(), True, q0.scale_codes.clone(), q0.group_scale.clone())
+                    for _ in range(copies)]
+            a = torch.from_numpy(synth.lora_a(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
+            b = torch.from_numpy(synth.lora_b(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
+            for m in (1, 4, 16):
+                x = torch.from_numpy(synth.activations(synth.DECODE_7B, lay, m)).to(torch.bfloat16).to(dev)
+                y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+                ws = torch.empty(qn.workspace_bytes(m, n, k, 16), dtype=torch.uint8, device=dev)
+                for q in pool[:2]:
+                    qn.linear_fwd(q, x, a, b, 32.0, want_h=False, out=y, ws=ws)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for q in pool:
+                        qn.linear_fwd(q, x, a, b, 32.0, want_h=False, out=y, ws=ws)
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = ev(), ev()
+                reps = 3
+                e0.record()
+                for _ in range(reps):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (reps * len(pool))
+                byt = gemv_bytes(m, n, k, 16)
+                gbs = byt / (us * 1e-6) / 1e9
+                dec.append({"n": n, "k": k, "m": m, "us_per_call": us, "bytes": byt, "GBps": gbs,
+                            "frac_hbm_peak": gbs / HBM_PEAK_GBS})
+                log(f"[bench] decode {n}x{k} m={m}: {us:.2f} us/call  {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+                del g
+            # dequantize on the same pool
+            if want("dequant"):
+                out = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+                nsub = min(len(pool), 64)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for q in pool[:nsub]:
+                        qn.binding._check(qn.load().qlora_nf4_dequantize(
+                            qn.binding.ctypes.byref(q.c_struct()), 0, qn.binding._ptr(out), qn.binding._stream()),
+                            "dequantize")
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = ev(), ev()
+                e0.record()
+                for _ in range(3):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (3 * nsub)
+                byt = n * k * (2.5 + 1 / 64 + 1 / 4096)
+                parts.setdefault("dequantize_bf16", []).append(
+                    {"n": n, "k": k, "us_per_call": us, "GBps": byt / (us * 1e-6) / 1e9,
+                     "frac_hbm_peak": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
+                log(f"[bench] dequantize {n}x{k}: {us:.2f} us  {byt / (us * 1e-6) / 1e9:.0f} GB/s")
+                del g, out
+            del pool
+            torch.cuda.empty_cache()
+        parts["decode_gemv"] = dec
+
+    if want("quant"):
+        qres = []
+        for (n, k) in shapes:
+            w = torch.from_numpy(synth.weight(synth.DECODE_7B, synth.DECODE_7B.layers[0 if n == 4096 else 1])).to(dev)
+            copies = max(2, int(1.2e9 // (4 * n * k)))
+            ws_pool = [w.clone() for _ in range(copies)]
+            codes = torch.empty(n * k // 2, dtype=torch.uint8, device=dev)
+            sc = torch.empty(n * k // 64, dtype=torch.uint8, device=dev)
+            gs = torch.empty(-(-(n * k // 64) // 256), dtype=torch.float32, device=dev)
+            lib = qn.load()
+            P = qn.binding._ptr
+
+            def qcall(src):
+                qn.binding._check(lib.qlora_nf4_quantize(P(src), n * k, 1, P(codes), P(sc), P(gs), None,
+                                                         qn.binding._stream()), "quantize")
+            qcall(ws_pool[0])
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record()
+            for src in ws_pool:
+                qcall(src)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / len(ws_pool)
+            byt = n * k * (4 + 0.5 + 1 / 64 + 1 / 4096)
+            qres.append({"n": n, "k": k, "us_per_call": us, "GBps": byt / (us * 1e-6) / 1e9,
+                         "frac_hbm_peak": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
+            log(f"[bench] quantize {n}x{k}: {us:.2f} us  {byt / (us * 1e-6) / 1e9:.0f} GB/s")
+            del ws_pool, w
+            torch.cuda.empty_cache()
+        parts["quantize_dq"] = qres
+
+    # -------------------------------------------------------- CPU baseline
+    cpu = None
+    if want("cpu") and not args.no_cpu:
+        cpu = cpu_baseline(layers, M, R, ALPHA, wl)
+        log(f"[bench] cpu oracle: {cpu['value']:.4f} {cpu['unit']} on {cpu['cores']} threads")
+
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b_layer_set_fwd_bwd", "layers": "q/k/v/o 4096x4096, gate/up 11008x4096, "
+                   "down 4096x11008", "tokens": M, "lora_r": R, "lora_alpha": ALPHA, "nf4_block": 64,
+                   "double_quant_block": 256, "global_batch": 4, "seq_len": 512, "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "parts": parts,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def step_fwd_base(layers, M):
+    return sum(2.0 * M * L["lay"].n * L["lay"].k for L in layers)
+
+
+def cpu_baseline(layers, M, R, ALPHA, wl):
+    """The oracle, untouched, on a bounded sample of the same step: for every
+    linear, the first 1024 weight rows (output features) and the first 128
+    token rows; oracle quantization (not timed), then oracle dequantization,
+    float64 forward and backward (timed). Scaled to the metric's unit with the
+    sample's algorithmic flops."""
+    import numpy as np
+
+    import synth
+    from oracle import linear as OL
+    from oracle import nf4 as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    ms, ns = 128, 1024
+    flops = 0.0
+    t_total = 0.0
+    for L in layers:
+        lay = L["lay"]
+        w = synth.weight(wl, lay)[:ns]
+        x = L["x"][:ms].float().cpu().numpy().astype(np.float64)
+        dy = L["dy"][:ms, :ns].float().cpu().numpy().astype(np.float64)
+        a = L["a"].float().cpu().numpy().astype(np.float64)
+        b = L["b"][:ns].float().cpu().numpy().astype(np.float64)
+        q = O.quantize(w.reshape(-1), True)
+        t0 = time.perf_counter()
+        _, bits = O.dequantize(q)
+        w16 = O.bf16_bits_to_f32(bits).reshape(ns, lay.k)
+        OL.linear_fwd(x, w16, a, b, ALPHA, R)
+        OL.linear_bwd(x, w16, a, b, dy, ALPHA, R)
+        t_total += time.perf_counter() - t0
+        flops += fwd_flops(ms, ns, lay.k, R) + bwd_flops(ms, ns, lay.k, R)
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"7B layer set: per linear the first {ns} weight rows and {ms} of {M} token rows; "
+                      f"oracle dequantization + float64 forward and backward timed "
+                      f"({flops / 1e9:.2f} GFLOP in {t_total:.2f} s), oracle quantization untimed"}
+
+
+if __name__ == "__main__":
+    main()

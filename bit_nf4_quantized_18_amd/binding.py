@@ -168,16 +168,22 @@ def _workspace(m, n, k, r, device):
     return (torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None), nbytes
 
 
-def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool = True, out=None):
-    """Y = X W16^T + (alpha/r) (X A^T) B^T. x: bf16 (m, k). Returns (y, h)."""
+def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool = True, out=None, h_out=None,
+               ws=None):
+    """Y = X W16^T + (alpha/r) (X A^T) B^T. x: bf16 (m, k). Returns (y, h).
+    ``out``, ``h_out`` and ``ws`` (uint8 workspace) may be preallocated."""
     import torch
 
     m = x.shape[0]
     r = 0 if a is None else a.shape[0]
     dev = x.device
     y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=dev)
-    h = torch.empty((m, r), dtype=torch.float32, device=dev) if (want_h and r > 0) else None
-    ws, nbytes = _workspace(m, q.n, q.k, r, dev)
+    h = h_out if h_out is not None else (
+        torch.empty((m, r), dtype=torch.float32, device=dev) if (want_h and r > 0) else None)
+    if ws is None:
+        ws, nbytes = _workspace(m, q.n, q.k, r, dev)
+    else:
+        nbytes = ws.numel()
     wc = q.c_struct()
     st = load().qlora_linear_fwd(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(y), _ptr(h),
                                  _ptr(ws), nbytes, _stream())
@@ -185,17 +191,25 @@ def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool
     return y, h
 
 
-def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, need_dx: bool = True):
-    """Returns (dx bf16 (m,k) or None, dA float32 (r,k), dB float32 (n,r))."""
+def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, need_dx: bool = True,
+               dx=None, da=None, db=None, ws=None):
+    """Returns (dx bf16 (m,k) or None, dA float32 (r,k), dB float32 (n,r)).
+    Outputs and the workspace may be preallocated."""
     import torch
 
     m = dy.shape[0]
     r = 0 if a is None else a.shape[0]
     dev = dy.device
-    dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev) if need_dx else None
-    da = torch.empty((r, q.k), dtype=torch.float32, device=dev) if r else None
-    db = torch.empty((q.n, r), dtype=torch.float32, device=dev) if r else None
-    ws, nbytes = _workspace(m, q.n, q.k, r, dev)
+    if dx is None and need_dx:
+        dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev)
+    if r and da is None:
+        da = torch.empty((r, q.k), dtype=torch.float32, device=dev)
+    if r and db is None:
+        db = torch.empty((q.n, r), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws, nbytes = _workspace(m, q.n, q.k, r, dev)
+    else:
+        nbytes = ws.numel()
     wc = q.c_struct()
     st = load().qlora_linear_bwd(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(h),
                                  _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes, _stream())
