@@ -72,6 +72,8 @@ qlora_status check_weight(const qlora_nf4_weight* w, bool linear) {
   if (w->n < 1 || w->k < 1) return QLORA_ERR_SHAPE;
   if (w->n > (INT64_C(1) << 40) / w->k) return QLORA_ERR_SHAPE;
   if (linear && ((w->k % QLORA_BLOCK) != 0 || (w->n % 16) != 0)) return QLORA_ERR_SHAPE;
+  // the matmul kernels address a weight with 32-bit offsets
+  if (linear && w->n * w->k > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
 

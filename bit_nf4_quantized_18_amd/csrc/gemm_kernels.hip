@@ -5,20 +5,35 @@
 // the LoRA path, and the backward computes gradients through the dequantized
 // weights. Here the dequantization happens inside the K-loop of the GEMM:
 // packed codes are read from HBM, turned into bf16 tiles in registers and
-// staged in LDS for the matrix cores; the bf16 copy of W never exists in HBM.
+// staged in LDS for the matrix cores; a bf16 copy of W never exists in HBM.
 //
 //   forward  (kTransW = false): Y[m][n]  = sum_k X[m][k]  W[n][k] + sum_j Hs[m][j] B[n][j]
 //   backward (kTransW = true):  dX[m][k] = sum_n dY[m][n] W[n][k] + sum_j dHs[m][j] At[k][j]
 //
-// Workgroup tile: 256 token rows x 128 output columns x 64 contraction (one
-// NF4 block per weight row and step), 4 waves as 2 x 2, each wave 128 x 64 =
-// 8 x 4 tiles of the 16x16x32 bf16 MFMA. The token tile is tall so that the
-// per-weight unpacking cost (table build + byte-permute lookups) is shared by
-// 256 rows. LDS holds two stages (A and dequantized W), rows padded to 144 B
-// so that 16 lanes reading 16 B each hit 64 distinct banks. One barrier per
-// step: the next stage is unpacked into the other buffer while the current
-// one feeds the MFMAs, and its global loads were issued a step earlier.
-// The rank-r LoRA term is one more pass of MFMAs over the r-wide operands.
+// Workgroup: 512 threads, a 256 (tokens) x 128 (outputs) tile, 64-deep
+// contraction steps (one NF4 block per weight row and step).
+//   * Waves 0-3 (consumers) each own a 128 x 64 sub-tile, 8 x 4 tiles of the
+//     16x16x32 bf16 MFMA. They only read LDS and issue MFMAs; the fragments
+//     of the next half-step are read while the current MFMAs run.
+//   * Waves 4-7 (producers) stream the A tile (two steps of register
+//     prefetch) and the packed codes and scales (four steps), build each
+//     block's bf16 lookup table (nf4_lut.h), unpack the codes and write both
+//     tiles into LDS two steps ahead of the consumers.
+//   With one consumer and one producer wave per SIMD, unpacking (VALU) and
+//   LDS writes overlap the consumers' matrix-core work. LDS holds a ring of
+//   three stages (3 x 48 KB), so a buffer is written two steps before it is
+//   read and one barrier per step suffices.
+// All global reads go through buffer resources: rows past M or N and blocks
+// past the end read as zeros in hardware, with no branch, clamp or select
+// (a guarded load would make the compiler wait for every outstanding load);
+// per-thread offsets are computed once, a step adds one constant.
+// LDS rows are 128 B without padding; the 16-byte chunk c of row r is stored
+// at chunk c ^ ((r >> 1) & 7), so 16 lanes reading one chunk of 16
+// consecutive rows hit 64 distinct banks. The MFMA computes the transposed
+// product (weights as the first operand): each lane ends with 4 consecutive
+// output columns of one token row and stores 8 contiguous bytes. Tiles are
+// ordered so that the workgroups on one XCD (ids congruent mod 8) share token
+// rows in that XCD's L2. The rank-r LoRA term is one more pass of MFMAs.
 #include "internal.h"
 #include "mfma.h"
 #include "nf4_lut.h"
@@ -27,174 +42,241 @@ namespace qlora {
 namespace {
 
 constexpr int kBM = 256, kBP = 128, kBQ = 64;
-constexpr int kPitch = kBQ + 8;  // bf16 elements per LDS row (144 B)
+constexpr int kStages = 3;
 constexpr int kGroup = 256;
+constexpr int kXcds = 8;
+constexpr int kAStage = kBM * kBQ;  // bf16 elements
+constexpr int kBStage = kBP * kBQ;
 
-struct Stage {
-  u32x4 a[8];   // 8 x 16 B of the A tile
-  u32x4 codes;  // 32 codes of one weight row (half a block)
-  float scale;
-};
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(lim),
+                                           0x00020000);
+}
 
-template <bool kTransW>
-__global__ __launch_bounds__(256) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,
+// element offset of (row, 16-byte chunk) in a swizzled 64-wide LDS tile
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kBQ + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+template <bool kTransW, bool kDQ>
+__global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,
                                                        int64_t P, int64_t Qn, const uint16_t* __restrict__ ep_a,
                                                        const uint16_t* __restrict__ ep_b, int64_t ep_ld, int ep_lim,
                                                        int rpad, uint16_t* __restrict__ out, Levels L) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][kBM * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kBP * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t As[kStages * kAStage];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[kStages * kBStage];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  const int wm = wave >> 1, wp = wave & 1;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kBP;
+
+  // --- tile of this workgroup (XCD-aware order) ----------------------------
+  const int64_t tiles_p = (P + kBP - 1) / kBP;
+  const int64_t tiles_m = (M + kBM - 1) / kBM;
+  const int64_t T = tiles_p * tiles_m;
+  const int64_t id = blockIdx.x;
+  const int64_t xcd = id % kXcds, local = id / kXcds;
+  const int64_t start = xcd * (T / kXcds) + (xcd < T % kXcds ? xcd : T % kXcds);
+  const int64_t lin = start + local;  // bijection of [0, T)
+  const int64_t m0 = (lin / tiles_p) * kBM;
+  const int64_t p0 = (lin % tiles_p) * kBP;
+
   const int64_t K = w.k;
   const int64_t nbk = K / 64;
-  const int64_t nk = (Qn + kBQ - 1) / kBQ;
+  const int nk = static_cast<int>((Qn + kBQ - 1) / kBQ);
 
-  // --- per-thread roles in the tile loads ---------------------------------
-  // A tile: chunks t + 256 u -> row t/8 + 32 u, 16-byte column t % 8.
-  const int a_row = tid >> 3, a_col = (tid & 7) * 8;
-  // W tile. Forward: weight row p0 + tid/2, k-half tid%2 of the step.
-  // Backward: weight row q0 + tid%64, k-quarter tid/64 of the output tile.
-  const int w_r = kTransW ? (tid & 63) : (tid >> 1);
-  const int w_c = kTransW ? (tid >> 6) * 32 : (tid & 1) * 32;
+  if (wave >= 4) {
+    // ======================= producers =======================
+    const int pt = tid - 256;
+    // A tile: chunks pt + 256 u -> row pt/8 + 32 u, 16-byte chunk pt % 8
+    const int a_row = pt >> 3, a_chunk = pt & 7;
+    // W: forward -> weight row p0 + pt/2, k-half pt%2 of the step;
+    //    backward -> weight row q0 + pt%64, k-quarter pt/64 of the output tile
+    const int w_r = kTransW ? (pt & 63) : (pt >> 1);
+    const int w_c = kTransW ? (pt >> 6) * 32 : (pt & 1) * 32;
+    // A resource: this tile's rows only (rows past M read as zeros)
+    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A + m0 * Qn, (M - m0 < kBM ? M - m0 : kBM) * Qn * 2);
+    const __amdgpu_buffer_rsrc_t crsrc = make_rsrc(w.codes, w.n * K / 2);
+    const __amdgpu_buffer_rsrc_t srsrc =
+        kDQ ? make_rsrc(w.scale_codes, w.n * nbk) : make_rsrc(w.absmax, w.n * nbk * 4);
+    const __amdgpu_buffer_rsrc_t grsrc = make_rsrc(w.group_scale, ((w.n * nbk + kGroup - 1) / kGroup) * 4);
+    int a_voff[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a_voff[u] = static_cast<int>(((a_row + 32 * u) * Qn + a_chunk * 8) * 2);
+    // per-step byte offsets: A moves by 64 columns; the weight moves along k
+    // (forward) or by 64 rows (backward)
+    const int64_t wrow0 = kTransW ? w_r : p0 + w_r;
+    const int64_t wk0 = kTransW ? p0 + w_c : w_c;
+    const int c_voff = static_cast<int>((wrow0 * K + wk0) / 2);
+    const int s_voff = static_cast<int>(wrow0 * nbk + wk0 / 64);
+    const int c_step = kTransW ? static_cast<int>(kBQ * K / 2) : kBQ / 2;
+    const int s_step = kTransW ? static_cast<int>(kBQ * nbk) : 1;
+    const bool wk_ok = wk0 < K;  // backward: the output tile may pass K
 
-  auto load_stage = [&](int64_t kt, Stage& st) {
-    const int64_t q0 = kt * kBQ;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t m = m0 + a_row + 32 * u;
-      const int64_t q = q0 + a_col;
-      st.a[u] = u32x4{0, 0, 0, 0};
-      if (m < M && q < Qn) st.a[u] = ld16(A + m * Qn + q);
-    }
-    int64_t wrow, wk;
-    if (kTransW) {
-      wrow = q0 + w_r;
-      wk = p0 + w_c;
-    } else {
-      wrow = p0 + w_r;
-      wk = q0 + w_c;
-    }
-    st.codes = u32x4{0, 0, 0, 0};
-    st.scale = 0.0f;
-    if (wrow < w.n && wk < K) {
-      st.codes = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(w.codes + (wrow * K + wk) / 2));
-      const int64_t bi = wrow * nbk + wk / 64;
-      st.scale = w.dq ? (static_cast<float>(w.scale_codes[bi]) / 255.0f) * w.group_scale[bi / kGroup] : w.absmax[bi];
-    }
-  };
+    u32x4 ra[2][8];  // A ring (2 stages)
+    u32x4 rc[4];     // codes ring (4 stages)
+    uint32_t rs[4];  // scale code ring (double quant)
+    float rg[4];     // group max (double quant) or absmax ring
 
-  auto store_stage = [&](int buf, const Stage& st) {
-    uint16_t* as = As[buf];
+    auto load_a = [&](int kt, u32x4(&dst)[8]) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) st16(as + (a_row + 32 * u) * kPitch + a_col, st.a[u]);
-    const BlockLut lut = make_block_lut(L.v, st.scale);
-    uint16_t* bs = Bs[buf];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t wv[4];
-      lut8_natural_order(lut, st.codes[j], wv);
-      if (kTransW) {
-        // element (n = w_r, k = w_c + 8 j + e) goes to Bs[k][n]
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t word = wv[e >> 1];
-          bs[(w_c + 8 * j + e) * kPitch + w_r] = static_cast<uint16_t>((e & 1) ? (word >> 16) : word);
-        }
+      for (int u = 0; u < 8; ++u) dst[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_voff[u] + kt * kBQ * 2, 0, 0);
+    };
+    auto load_w = [&](int kt, u32x4& c, uint32_t& sc, float& gs) {
+      c = __builtin_amdgcn_raw_buffer_load_b128(crsrc, c_voff + kt * c_step, 0, 0);
+      const int soff = s_voff + kt * s_step;
+      if (kDQ) {
+        sc = __builtin_amdgcn_raw_buffer_load_b8(srsrc, soff, 0, 0);
+        gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grsrc, (soff / kGroup) * 4, 0, 0));
       } else {
-        st16(bs + w_r * kPitch + w_c + 8 * j, u32x4{wv[0], wv[1], wv[2], wv[3]});
+        sc = 0;
+        gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff * 4, 0, 0));
       }
+    };
+    auto store = [&](int kt, const u32x4(&a)[8], u32x4 c, uint32_t sc, float gs) {
+      uint16_t* as = As + (kt % kStages) * kAStage;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) st16(as + swz(a_row + 32 * u, a_chunk), a[u]);
+      const float s = kDQ ? (static_cast<float>(sc) / 255.0f) * gs : gs;
+      const BlockLut lut = make_block_lut(L.v, wk_ok ? s : 0.0f);
+      uint16_t* bs = Bs + (kt % kStages) * kBStage;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t wv[4];
+        lut8_natural_order(lut, c[j], wv);
+        if (kTransW) {
+          // element (n = w_r, k = w_c + 8 j + e) goes to row k, column n
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int krow = w_c + 8 * j + e;
+            const uint32_t word = wv[e >> 1];
+            bs[swz(krow, w_r >> 3) + (w_r & 7)] = static_cast<uint16_t>((e & 1) ? (word >> 16) : word);
+          }
+        } else {
+          st16(bs + swz(w_r, (w_c >> 3) + j), u32x4{wv[0], wv[1], wv[2], wv[3]});
+        }
+      }
+    };
+
+    // prologue: stages 0 and 1 into LDS; A of stages 2, 3 and codes of
+    // stages 2..5 in flight
+    load_a(0, ra[0]);
+    load_a(1, ra[1]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) load_w(s, rc[s], rs[s], rg[s]);
+    store(0, ra[0], rc[0], rs[0], rg[0]);
+    load_a(2, ra[0]);
+    load_w(4, rc[0], rs[0], rg[0]);
+    if (nk > 1) store(1, ra[1], rc[1], rs[1], rg[1]);
+    load_a(3, ra[1]);
+    load_w(5, rc[1], rs[1], rg[1]);
+    __syncthreads();
+    // step kt: write stage kt+2 (A slot (kt+2)%2, codes slot (kt+2)%4), then
+    // refill those slots with stage kt+4 (A) and kt+6 (codes). Loads past the
+    // last stage read zeros (out of the buffer resources) and are never used.
+    auto step = [&](int kt, u32x4(&a)[8], int cs) {
+      if (kt + 2 < nk) store(kt + 2, a, rc[cs], rs[cs], rg[cs]);
+      load_a(kt + 4, a);
+      load_w(kt + 6, rc[cs], rs[cs], rg[cs]);
+      __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 4) {
+      step(kt, ra[0], 2);
+      if (kt + 1 < nk) step(kt + 1, ra[1], 3);
+      if (kt + 2 < nk) step(kt + 2, ra[0], 0);
+      if (kt + 3 < nk) step(kt + 3, ra[1], 1);
     }
+    return;
+  }
+
+  // ======================= consumers =======================
+  const int i = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wp = wave & 1;
+  const int sw = (i >> 1) & 7;
+  // element offsets (within a stage row) of this lane's fragment chunk, per half-step
+  const int col0 = ((0 + g) ^ sw) << 3, col1 = ((4 + g) ^ sw) << 3;
+  const int arow = (wm * 128 + i) * kBQ, brow = (wp * 64 + i) * kBQ;
+
+  f32x4 acc[4][8];  // [weight tile nt][token tile mt]: acc = W x^T tile
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // two register sets of fragments: while the MFMAs of one half-step run,
+  // the other set is filled from LDS
+  u32x4 fa0[8], fb0[4], fa1[8], fb1[4];
+  auto read = [&](int kt, int col, u32x4(&xa)[8], u32x4(&xb)[4]) {
+    const uint16_t* as = As + (kt % kStages) * kAStage + arow + col;
+    const uint16_t* bs = Bs + (kt % kStages) * kBStage + brow + col;
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) xa[mt] = ld16(as + 16 * mt * kBQ);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) xb[nt] = ld16(bs + 16 * nt * kBQ);
+  };
+  auto mma = [&](const u32x4(&xa)[8], const u32x4(&xb)[4]) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = mfma_16x16x32(xb[nt], xa[mt], acc[nt][mt]);
   };
 
-  f32x4 acc[8][4];
-#pragma unroll
-  for (int a = 0; a < 8; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](int buf) {
-    const uint16_t* as = As[buf] + (wm * 128 + i) * kPitch + 8 * g;
-    const uint16_t* bs = Bs[buf] + (wp * 64 + i) * kPitch + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 fa[8], fb[4];
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) fa[mt] = ld16(as + 16 * mt * kPitch + 32 * ks);
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) fb[nt] = ld16(bs + 16 * nt * kPitch + 32 * ks);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(fa[mt], fb[nt], acc[mt][nt]);
-    }
-  };
-
-  Stage st;
-  load_stage(0, st);
-  store_stage(0, st);
-  if (nk > 1) load_stage(1, st);
   __syncthreads();
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = static_cast<int>(kt & 1);
-    compute(buf);
-    if (kt + 1 < nk) store_stage(buf ^ 1, st);
-    if (kt + 2 < nk) load_stage(kt + 2, st);
+  read(0, col0, fa0, fb0);
+  for (int kt = 0; kt < nk; ++kt) {
+    read(kt, col1, fa1, fb1);                           // second half of this step
+    mma(fa0, fb0);                                      // first half
+    if (kt + 1 < nk) read(kt + 1, col0, fa0, fb0);      // next step, written two steps ago
+    mma(fa1, fb1);                                      // second half
     __syncthreads();
   }
 
-  // LoRA term: rpad more contraction slots.
+  // LoRA term: rpad more contraction slots, operands straight from global memory.
   for (int ks = 0; ks < rpad / 32; ++ks) {
-    u32x4 fa[8], fb[4];
+    u32x4 xa[8], xb[4];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
       const int64_t m = m0 + wm * 128 + 16 * mt + i;
-      fa[mt] = (m < M) ? ld16(ep_a + m * rpad + 32 * ks + 8 * g) : u32x4{0, 0, 0, 0};
+      xa[mt] = ld16(ep_a + (m < M ? m : M - 1) * rpad + 32 * ks + 8 * g);  // rows past M are never stored
     }
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int64_t p = p0 + wp * 64 + 16 * nt + i;
-      fb[nt] = (p < P) ? ld8_bf16_guarded(ep_b + p * ep_ld, 32 * ks + 8 * g, ep_lim, (ep_ld % 8) == 0)
+      xb[nt] = (p < P) ? ld8_bf16_guarded(ep_b + p * ep_ld, 32 * ks + 8 * g, ep_lim, (ep_ld % 8) == 0)
                        : u32x4{0, 0, 0, 0};
     }
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_16x16x32(fa[mt], fb[nt], acc[mt][nt]);
+    mma(xa, xb);
   }
 
+  // lane holds out[m = .. + i][p = .. + 4g .. 4g+3]
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) {
+    const int64_t m = m0 + wm * 128 + 16 * mt + i;
+    if (m >= M) continue;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int64_t p = p0 + wp * 64 + 16 * nt + i;
-      if (p >= P) continue;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t m = m0 + wm * 128 + 16 * mt + 4 * g + v;
-        if (m < M) out[m * P + p] = f32_to_bf16_rne(acc[mt][nt][v]);
-      }
+      const int64_t p = p0 + wp * 64 + 16 * nt + 4 * g;
+      if (p >= P) continue;  // P % 16 == 0: a run of 4 is whole
+      const f32x4 c = acc[nt][mt];
+      const u32x2 v = {cvt_bf16x2(c[0], c[1]), cvt_bf16x2(c[2], c[3])};
+      *reinterpret_cast<u32x2*>(out + m * P + p) = v;
     }
   }
 }
+
+unsigned tiles(int64_t m, int64_t p) { return static_cast<unsigned>(((m + kBM - 1) / kBM) * ((p + kBP - 1) / kBP)); }
 
 }  // namespace
 
 hipError_t launch_gemm_fwd(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* hs, const uint16_t* b,
                            int r, int rpad, uint16_t* y, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((w.n + kBP - 1) / kBP), static_cast<unsigned>((m + kBM - 1) / kBM));
-  hipLaunchKernelGGL(nf4_gemm_kernel<false>, grid, dim3(256), 0, st, w, x, m, w.n, w.k, hs, b,
-                     static_cast<int64_t>(r), r, rpad, y, nf4_table());
+  auto kern = w.dq ? nf4_gemm_kernel<false, true> : nf4_gemm_kernel<false, false>;
+  hipLaunchKernelGGL(kern, dim3(tiles(m, w.n)), dim3(512), 0, st, w, x, m, w.n, w.k, hs, b, static_cast<int64_t>(r), r,
+                     rpad, y, nf4_table());
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dx(const PackedW& w, const uint16_t* dy, int64_t m, const uint16_t* dhs, const uint16_t* at,
                           int rpad, uint16_t* dx, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((w.k + kBP - 1) / kBP), static_cast<unsigned>((m + kBM - 1) / kBM));
-  hipLaunchKernelGGL(nf4_gemm_kernel<true>, grid, dim3(256), 0, st, w, dy, m, w.k, w.n, dhs, at,
+  auto kern = w.dq ? nf4_gemm_kernel<true, true> : nf4_gemm_kernel<true, false>;
+  hipLaunchKernelGGL(kern, dim3(tiles(m, w.k)), dim3(512), 0, st, w, dy, m, w.k, w.n, dhs, at,
                      static_cast<int64_t>(rpad), rpad, rpad, dx, nf4_table());
   return hipGetLastError();
 }

@@ -8,7 +8,11 @@
 // weight), so the kernel is built around that stream:
 //   * a workgroup owns 16 weight rows; its WAVES x 4 lane groups split the
 //     row's 64-blocks round-robin, so every lane loads whole blocks (32 B of
-//     codes, two 16-byte loads) and all loads of a lane are independent;
+//     codes, two 16-byte loads); all loads of a pass are issued
+//     unconditionally (clamped addresses, out-of-range lanes zeroed at the
+//     MFMA operand) before the first is used, so a pass costs one memory
+//     round trip -- a guarded load would make the compiler wait for every
+//     outstanding load at the guard;
 //   * per block a lane decodes the scale, builds a 16-entry bf16 table in
 //     registers (nf4_lut.h) and looks up 8 weights per table access;
 //   * the dot products run on the matrix cores (16x16x32 bf16 MFMA with the
@@ -24,7 +28,7 @@ namespace {
 
 constexpr int kGroup = 256;
 
-template <int WAVES>
+template <int WAVES, bool kDQ>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ xp, int M,
                                                           const float* __restrict__ hpart, int hsplits,
                                                           const uint16_t* __restrict__ b, int r, float s,
@@ -33,6 +37,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   constexpr int kLaneGroups = WAVES * 4;
   __shared__ f32x4 red[WAVES][64];
   __shared__ float h_lds[16 * QLORA_MAX_RANK];
+  __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int G = wave * 4 + g;
@@ -40,43 +45,58 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   const int64_t nbk = K / 64;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t n = n0 + i;
-  const bool nvalid = n < N;
-  const bool mvalid = i < M;
+  const int64_t n_c = n < N ? n : N - 1;    // clamped: every load is unconditional
+  const int64_t xrow = i < M ? i : M - 1;
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Wave-uniform trip count: block kb = G + kLaneGroups * t.
-  for (int64_t kb0 = wave * 4; kb0 < nbk; kb0 += kLaneGroups) {
-    const int64_t kb = kb0 + g;
-    const bool valid = nvalid && kb < nbk;
-    u32x4 c0 = u32x4{0, 0, 0, 0}, c1 = u32x4{0, 0, 0, 0};
-    float sc = 0.0f;
-    if (valid) {
-      const uint8_t* cp = w.codes + (n * K + kb * 64) / 2;
-      c0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp));
-      c1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cp) + 1);
-      const int64_t bi = n * nbk + kb;
-      sc = w.dq ? (static_cast<float>(w.scale_codes[bi]) / 255.0f) * w.group_scale[bi / kGroup] : w.absmax[bi];
+  // One block per lane group per pass. All loads of a pass (codes, scale,
+  // X) are issued unconditionally from clamped addresses before any is used;
+  // out-of-range lanes are zeroed at the MFMA operand.
+  for (int64_t base = 0; base < nbk; base += kLaneGroups) {
+    const int64_t kb = base + G;
+    const int64_t kb_c = kb < nbk ? kb : nbk - 1;
+    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * K + kb_c * 64) / 2);
+    const u32x4 c0 = __builtin_nontemporal_load(cp);
+    const u32x4 c1 = __builtin_nontemporal_load(cp + 1);
+    const int64_t bi = n_c * nbk + kb_c;
+    uint32_t scode = 0;
+    float gsc;
+    if (kDQ) {
+      scode = w.scale_codes[bi];
+      gsc = w.group_scale[bi / kGroup];
+    } else {
+      gsc = w.absmax[bi];
     }
-    const BlockLut lut = make_block_lut(L.v, sc);
-    const uint16_t* xrow = xp + static_cast<int64_t>(i) * K + kb * 64;
+    u32x4 xa[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
-      uint32_t wv[4];
-      lut8_decode_order(lut, cw, wv);
-      u32x4 a = u32x4{0, 0, 0, 0};
-      if (valid && mvalid) a = ld16(xrow + 8 * j);
-      acc = mfma_16x16x32(a, u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
+    for (int j = 0; j < 8; ++j) xa[j] = ld16(xp + xrow * K + kb_c * 64 + 8 * j);
+    // wave-uniform: skip a pass slot no lane group of this wave uses
+    if (base + wave * 4 < nbk) {
+      const bool ok = (n < N) && (kb < nbk) && (i < M);
+      const float sc = kDQ ? (static_cast<float>(scode) / 255.0f) * gsc : gsc;
+      const BlockLut lut = make_block_lut(L.v, sc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
+        uint32_t wv[4];
+        lut8_decode_order(lut, cw, wv);
+        acc = mfma_16x16x32(ok ? xa[j] : u32x4{0, 0, 0, 0}, u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
+      }
     }
   }
 
+  // Epilogue operands: H = sum of the LoRA-down partials in a fixed order,
+  // and this workgroup's 16 rows of B.
   red[wave][lane] = acc;
-  // H = sum of the LoRA-down partials (fixed order).
   for (int idx = tid; idx < M * r; idx += WAVES * 64) {
     float hv = 0.0f;
     for (int sp = 0; sp < hsplits; ++sp) hv += hpart[static_cast<int64_t>(sp) * M * r + idx];
     h_lds[idx] = hv;
     if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
+  }
+  for (int idx = tid; idx < 16 * r; idx += WAVES * 64) {
+    const int64_t row = n0 + idx / r;
+    b_lds[idx] = b[(row < N ? row : N - 1) * r + idx % r];
   }
   __syncthreads();
   if (tid >= 256) return;
@@ -89,7 +109,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   for (int wv = 0; wv < WAVES; ++wv) sum += red[wv][l2][v];
   if (r > 0) {
     float lo = 0.0f;
-    const uint16_t* brow = b + no * r;
+    const uint16_t* brow = b_lds + (l2 & 15) * r;
     for (int j = 0; j < r; ++j) lo = fmaf(h_lds[mo * r + j], __uint_as_float(static_cast<uint32_t>(brow[j]) << 16), lo);
     sum = fmaf(s, lo, sum);
   }
@@ -100,10 +120,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
 
 hipError_t launch_gemv(const PackedW& w, const uint16_t* xp, int64_t m, const float* hpart, int hsplits,
                        const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
-  constexpr int kWaves = 8;
+  constexpr int kWaves = 16;
   const unsigned grid = static_cast<unsigned>((w.n + 15) / 16);
-  hipLaunchKernelGGL(gemv_kernel<kWaves>, dim3(grid), dim3(kWaves * 64), 0, st, w, xp, static_cast<int>(m), hpart,
-                     hsplits, b, r, s, y, h_out, nf4_table());
+  auto kern = w.dq ? gemv_kernel<kWaves, true> : gemv_kernel<kWaves, false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, xp, static_cast<int>(m), hpart, hsplits, b, r, s,
+                     y, h_out, nf4_table());
   return hipGetLastError();
 }
 

@@ -40,22 +40,39 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int t = 0; t < kRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t c = c_begin + wave; c < c_end; c += 4) {
-    const int64_t q = c * 32 + 8 * g;
-    const bool qvalid = q < qn;  // qn % 8 == 0, so a valid run is whole
-    u32x4 a = u32x4{0, 0, 0, 0};
-    if (mvalid && qvalid) a = ld16(P + m * qn + q);
-    if (p_perm != nullptr && mvalid && qvalid) {
-      uint32_t in[4] = {a[0], a[1], a[2], a[3]}, o[4];
-      to_decode_order(in, o);
-      st16(p_perm + m * qn + q, u32x4{o[0], o[1], o[2], o[3]});
+  // U chunks per wave per trip. Loads are unconditional from clamped
+  // addresses (a guarded load makes the compiler wait for all outstanding
+  // loads); chunks past the split and ranks past r are zeroed at the operand.
+  constexpr int U = (RT <= 2) ? 4 : (RT <= 4 ? 2 : 1);
+  const int64_t m_c = m < M ? m : M - 1;
+  for (int64_t c0 = c_begin + wave; c0 < c_end; c0 += 4 * U) {
+    u32x4 a[U], b[U][kRT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t q = (c0 + 4 * u) * 32 + 8 * g;
+      const int64_t q_c = q < qn - 8 ? q : qn - 8;
+      a[u] = ld16(P + m_c * qn + q_c);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int j = 16 * t + i;
+        b[u][t] = ld16(Q + static_cast<int64_t>(j < r ? j : r - 1) * qn + q_c);
+      }
     }
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int j = 16 * t + i;
-      u32x4 b = u32x4{0, 0, 0, 0};
-      if (j < r && qvalid) b = ld16(Q + static_cast<int64_t>(j) * qn + q);
-      acc[t] = mfma_16x16x32(a, b, acc[t]);
+    for (int u = 0; u < U; ++u) {
+      const int64_t q = (c0 + 4 * u) * 32 + 8 * g;
+      const bool qvalid = (c0 + 4 * u < c_end) && q < qn;  // qn % 8 == 0: a valid run is whole
+      const u32x4 av = qvalid ? a[u] : u32x4{0, 0, 0, 0};
+      if (p_perm != nullptr && mvalid && qvalid) {
+        uint32_t in[4] = {av[0], av[1], av[2], av[3]}, o[4];
+        to_decode_order(in, o);
+        st16(p_perm + m * qn + q, u32x4{o[0], o[1], o[2], o[3]});
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int j = 16 * t + i;
+        acc[t] = mfma_16x16x32(av, j < r ? b[u][t] : u32x4{0, 0, 0, 0}, acc[t]);
+      }
     }
   }
   if (RT == 0) return;
@@ -101,38 +118,59 @@ __global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint
 }
 
 // part[s][j][c] = sum over rows m of split s of U[m][j] * V[m][c] (float32
-// U, bf16 V). Each thread owns two adjacent columns c and 16 ranks j; the
-// U row slice is uniform across the workgroup.
+// U, bf16 V). A workgroup owns 128 columns (two per lane) and 16 ranks; its
+// four waves take interleaved rows of the split and are summed in LDS in a
+// fixed order. The U row slice is uniform across the workgroup (scalar
+// loads); rows are taken four at a time with all loads issued first.
 __global__ __launch_bounds__(256) void rank_partial_kernel(const float* __restrict__ U, const uint16_t* __restrict__ V,
                                                            int64_t M, int64_t cn, int r, int splits,
                                                            float* __restrict__ part) {
-  const int64_t c = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 2;
+  __shared__ float red[4][16][128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 128 + 2 * lane;
   const int j0 = blockIdx.y * 16;
   const int s = blockIdx.z;
   const int64_t per = (M + splits - 1) / splits;
   const int64_t mb = s * per;
   const int64_t me = (mb + per < M) ? mb + per : M;
+  const bool cvalid = c < cn;
   float acc[16][2];
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) acc[jj][0] = acc[jj][1] = 0.0f;
-  if (c < cn) {
-    for (int64_t m = mb; m < me; ++m) {
-      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(V + m * cn + c);
-      const float v0 = __uint_as_float(v2 << 16), v1 = __uint_as_float(v2 & 0xFFFF0000u);
+  const int64_t c_c = cvalid ? c : cn - 2;  // columns past cn are computed but never stored
+  for (int64_t m0 = mb + wave; m0 < me; m0 += 16) {
+    uint32_t v2[4];
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const float u = (j0 + jj < r) ? U[m * r + j0 + jj] : 0.0f;
-        acc[jj][0] = fmaf(u, v0, acc[jj][0]);
-        acc[jj][1] = fmaf(u, v1, acc[jj][1]);
-      }
+    for (int u = 0; u < 4; ++u) {
+      const int64_t m = m0 + 4 * u;
+      v2[u] = *reinterpret_cast<const uint32_t*>(V + (m < me ? m : me - 1) * cn + c_c);
     }
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      if (j0 + jj < r) {
-        float* dst = part + (static_cast<int64_t>(s) * r + j0 + jj) * cn + c;
-        dst[0] = acc[jj][0];
-        dst[1] = acc[jj][1];
+    for (int u = 0; u < 4; ++u) {
+      const int64_t m = m0 + 4 * u;
+      if (m >= me) break;  // uniform across the wave
+      const float v0 = __uint_as_float(v2[u] << 16), v1 = __uint_as_float(v2[u] & 0xFFFF0000u);
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj) {
+        const int jc = (j0 + jj < r) ? j0 + jj : r - 1;  // ranks past r are never stored
+        const float uu = U[m * r + jc];
+        acc[jj][0] = fmaf(uu, v0, acc[jj][0]);
+        acc[jj][1] = fmaf(uu, v1, acc[jj][1]);
       }
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    red[wave][jj][2 * lane] = acc[jj][0];
+    red[wave][jj][2 * lane + 1] = acc[jj][1];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * 128; idx += 256) {
+    const int jj = idx >> 7, cc = idx & 127;
+    const int64_t col = static_cast<int64_t>(blockIdx.x) * 128 + cc;
+    if (j0 + jj < r && col < cn) {
+      const float sum = ((red[0][jj][cc] + red[1][jj][cc]) + red[2][jj][cc]) + red[3][jj][cc];
+      part[(static_cast<int64_t>(s) * r + j0 + jj) * cn + col] = sum;
     }
   }
 }
@@ -166,7 +204,7 @@ void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16
 }  // namespace
 
 int rank_reduce_splits(int64_t m) {
-  int64_t s = m / 128;
+  int64_t s = m / 256;
   if (s < 1) s = 1;
   if (s > 16) s = 16;
   return static_cast<int>(s);
@@ -203,7 +241,7 @@ hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n
 
 hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int64_t cn, int r, float scale,
                               int splits, float* part, float* out, int c_major, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((cn / 2 + 255) / 256), static_cast<unsigned>((r + 15) / 16),
+  const dim3 grid(static_cast<unsigned>((cn + 127) / 128), static_cast<unsigned>((r + 15) / 16),
                   static_cast<unsigned>(splits));
   hipLaunchKernelGGL(rank_partial_kernel, grid, dim3(256), 0, st, U, V, m, cn, r, splits, part);
   const int64_t total = static_cast<int64_t>(r) * cn;

@@ -76,13 +76,17 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
   const int64_t g = blockIdx.x;
   const int sub = lane >> 3, part = lane & 7;
 
+  // Vector loads are unconditional from clamped addresses (a guarded load
+  // makes the compiler wait for all outstanding loads); only the lanes that
+  // straddle the end of the array redo theirs with element loads.
   float v[8][8];
+  const int64_t last8 = numel >= 8 ? numel - 8 : 0;
 #pragma unroll
   for (int it = 0; it < 8; ++it) {
     const int64_t b = g * kGroup + wave * 64 + it * 8 + sub;
     const int64_t e0 = b * kBlock + part * 8;
-    if (e0 + 8 <= numel) {
-      const f32x4* p = reinterpret_cast<const f32x4*>(w + e0);
+    if (numel >= 8) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(w + (e0 < last8 ? e0 : (last8 & ~INT64_C(3))));
       const f32x4 a = __builtin_nontemporal_load(p);
       const f32x4 c = __builtin_nontemporal_load(p + 1);
 #pragma unroll
@@ -90,7 +94,13 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
         v[it][j] = a[j];
         v[it][4 + j] = c[j];
       }
-    } else {
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int64_t b = g * kGroup + wave * 64 + it * 8 + sub;
+    const int64_t e0 = b * kBlock + part * 8;
+    if (e0 + 8 > numel) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[it][j] = (e0 + j < numel) ? w[e0 + j] : 0.0f;
     }
@@ -145,36 +155,54 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
   if (dq && tid == 0) group_scale[g] = mg;
 }
 
-__device__ __forceinline__ float block_scale(const PackedW& w, int64_t b) {
-  if (w.dq) return u8_level(w.scale_codes[b]) * w.group_scale[b / kGroup];
-  return w.absmax[b];
-}
-
 // Dequantize: each lane turns one 32-bit word of codes (8 weights) into 8
 // outputs per step; a wave covers 256 contiguous code bytes -> 1 KB of bf16
 // (or 2 KB of fp32) contiguous. Four steps per lane, all loads first.
-template <bool kF32>
+template <bool kF32, bool kDQ>
 __global__ __launch_bounds__(256) void nf4_dequantize_kernel(PackedW w, void* __restrict__ out, Levels L) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = L.v[threadIdx.x];
   __syncthreads();
   const int64_t numel = w.n * w.k;
   const int64_t nwords = (numel + 7) / 8;  // 8 codes per 32-bit word
+  const int64_t nbytes_total = (numel + 1) / 2;
+  const int64_t nfull = nbytes_total / 4;  // words lying wholly inside the buffer
   const int64_t base = static_cast<int64_t>(blockIdx.x) * 1024 + threadIdx.x;
-  uint32_t cw[4];
+  // Whole words: unconditional loads from clamped addresses (a guarded load
+  // makes the compiler wait for all outstanding loads). The one partial
+  // word at the end is assembled from bytes by the lane that owns it.
+  uint32_t cw[4] = {0, 0, 0, 0};
+  if (nfull > 0) {  // uniform
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t q = base + j * 256;
+      cw[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(w.codes) + (q < nfull - 1 ? q : nfull - 1));
+    }
+  }
+  // per-word block scales, also unconditional (clamped block index)
+  const int64_t nb = (numel + kBlock - 1) / kBlock;
+  uint32_t sc8[4];
+  float sc32[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t bq = (base + j * 256) * 8 / kBlock;
+    const int64_t bc = bq < nb - 1 ? bq : nb - 1;
+    if (kDQ) {
+      sc8[j] = w.scale_codes[bc];
+      sc32[j] = w.group_scale[bc / kGroup];
+    } else {
+      sc8[j] = 0;
+      sc32[j] = w.absmax[bc];
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t q = base + j * 256;
-    cw[j] = 0;
-    if (q < nwords) {
-      const int64_t byte0 = q * 4;
-      const int64_t nbytes_total = (numel + 1) / 2;
-      if (byte0 + 4 <= nbytes_total) {
-        cw[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(w.codes) + q);
-      } else {
-        for (int i = 0; i < 4; ++i)
-          if (byte0 + i < nbytes_total) cw[j] |= static_cast<uint32_t>(w.codes[byte0 + i]) << (8 * i);
-      }
+    if (q >= nfull && q < nwords) {
+      uint32_t word = 0;
+      for (int i = 0; i < 4; ++i)
+        if (q * 4 + i < nbytes_total) word |= static_cast<uint32_t>(w.codes[q * 4 + i]) << (8 * i);
+      cw[j] = word;
     }
   }
 #pragma unroll
@@ -182,7 +210,7 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(PackedW w, void* __
     const int64_t q = base + j * 256;
     if (q >= nwords) continue;
     const int64_t e0 = q * 8;
-    const float s = block_scale(w, e0 / kBlock);
+    const float s = kDQ ? u8_level(sc8[j]) * sc32[j] : sc32[j];
     float f[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = lv[(cw[j] >> (4 * i)) & 0xF] * s;
@@ -229,11 +257,9 @@ hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream
   const int64_t numel = w.n * w.k;
   const int64_t nwords = (numel + 7) / 8;
   const unsigned grid = static_cast<unsigned>((nwords + 1023) / 1024);
-  if (out_f32) {
-    hipLaunchKernelGGL(nf4_dequantize_kernel<true>, dim3(grid), dim3(256), 0, s, w, out, nf4_table());
-  } else {
-    hipLaunchKernelGGL(nf4_dequantize_kernel<false>, dim3(grid), dim3(256), 0, s, w, out, nf4_table());
-  }
+  auto kern = out_f32 ? (w.dq ? nf4_dequantize_kernel<true, true> : nf4_dequantize_kernel<true, false>)
+                      : (w.dq ? nf4_dequantize_kernel<false, true> : nf4_dequantize_kernel<false, false>);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, w, out, nf4_table());
   return hipGetLastError();
 }
 

@@ -49,7 +49,10 @@
  *     launch (hipGetLastError). Nothing is thrown across the ABI. Calls are
  *     thread-safe; calls that write the same buffers must be ordered by the
  *     caller.
- *   - Weights must be finite; non-finite weights give undefined codes.
+ *   - Weights must be finite; non-finite weights give undefined codes. X, dY,
+ *     A and B must be finite as well: the matmul kernels may multiply
+ *     elements past a ragged edge of X or dY by exact zeros, so a non-finite
+ *     value there could reach a neighbouring output.
  */
 #ifndef QLORA_NF4_H_
 #define QLORA_NF4_H_
@@ -123,7 +126,7 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dty
 /* Forward: Y = X W16^T + s (X A^T) B^T with s = fl32(alpha / r).
  * Ultralytics glossary "QLoRA", "Come funziona QLoRA" (forward paragraph);
  * "LoRA y QLoRA en Profundidad", "La Idea Central" / "Alpha".
- *   w     : packed NF4 weight, n x k, k % 64 == 0 and n % 16 == 0.
+ *   w     : packed NF4 weight, n x k, k % 64 == 0, n % 16 == 0, n * k <= 2^31.
  *   x     : bf16 (uint16 bit patterns) m x k.
  *   a     : bf16 r x k; b : bf16 n x r. r = 0 (a, b NULL) means base only.
  *   y     : bf16 m x n output.
