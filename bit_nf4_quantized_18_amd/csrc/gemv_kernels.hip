@@ -9,9 +9,9 @@
 //   * a workgroup owns 16 weight rows; its WAVES x 4 lane groups split the
 //     row's 64-blocks round-robin, so every lane loads whole blocks (32 B of
 //     codes, two 16-byte loads); all loads of a pass are issued
-//     unconditionally (clamped addresses, out-of-range lanes zeroed at the
-//     MFMA operand) before the first is used, so a pass costs one memory
-//     round trip -- a guarded load would make the compiler wait for every
+//     unconditionally (clamped addresses; an out-of-range block gets a zero
+//     scale) before the first is used, so a pass costs one memory round
+//     trip -- a guarded load would make the compiler wait for every
 //     outstanding load at the guard;
 //   * per block a lane decodes the scale, builds a 16-entry bf16 table in
 //     registers (nf4_lut.h) and looks up 8 weights per table access;
@@ -41,24 +41,25 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int G = wave * 4 + g;
-  const int64_t K = w.k, N = w.n;
-  const int64_t nbk = K / 64;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t n = n0 + i;
-  const int64_t n_c = n < N ? n : N - 1;    // clamped: every load is unconditional
-  const int64_t xrow = i < M ? i : M - 1;
+  // 32-bit offsets: the host guarantees n * k <= 2^31
+  const int K = static_cast<int>(w.k), N = static_cast<int>(w.n);
+  const int nbk = K / 64;
+  const int n0 = blockIdx.x * 16;
+  const int n = n0 + i;
+  const int n_c = n < N ? n : N - 1;     // clamped: every load is unconditional
+  const int xrow = i < M ? i : M - 1;    // rows past M feed outputs that are never stored
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   // One block per lane group per pass. All loads of a pass (codes, scale,
   // X) are issued unconditionally from clamped addresses before any is used;
-  // out-of-range lanes are zeroed at the MFMA operand.
-  for (int64_t base = 0; base < nbk; base += kLaneGroups) {
-    const int64_t kb = base + G;
-    const int64_t kb_c = kb < nbk ? kb : nbk - 1;
-    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * K + kb_c * 64) / 2);
+  // a block past the row or past K gets a zero scale, so its weights are 0.
+  for (int base = 0; base < nbk; base += kLaneGroups) {
+    const int kb = base + G;
+    const int kb_c = kb < nbk ? kb : nbk - 1;
+    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_c * 32));
     const u32x4 c0 = __builtin_nontemporal_load(cp);
     const u32x4 c1 = __builtin_nontemporal_load(cp + 1);
-    const int64_t bi = n_c * nbk + kb_c;
+    const int bi = n_c * nbk + kb_c;
     uint32_t scode = 0;
     float gsc;
     if (kDQ) {
@@ -68,41 +69,47 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
       gsc = w.absmax[bi];
     }
     u32x4 xa[8];
+    const uint16_t* xr = xp + xrow * K + kb_c * 64;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = ld16(xp + xrow * K + kb_c * 64 + 8 * j);
+    for (int j = 0; j < 8; ++j) xa[j] = ld16(xr + 8 * j);
+    if (base == 0) {
+      // Epilogue operands, fetched while the weight loads are in flight: H =
+      // sum of the LoRA-down partials (fixed order) and this workgroup's 16
+      // rows of B (contiguous in memory).
+      const int mr = M * r;
+      for (int idx = tid; idx < mr; idx += WAVES * 64) {
+        float hv = 0.0f;
+        for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
+        h_lds[idx] = hv;
+        if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
+      }
+      const int blast = N * r - 1;
+      for (int idx = tid; idx < 16 * r; idx += WAVES * 64) {
+        const int e = n0 * r + idx;
+        b_lds[idx] = b[e < blast ? e : blast];  // rows past N are never stored
+      }
+    }
     // wave-uniform: skip a pass slot no lane group of this wave uses
     if (base + wave * 4 < nbk) {
-      const bool ok = (n < N) && (kb < nbk) && (i < M);
+      const bool ok = (n < N) && (kb < nbk);
       const float sc = kDQ ? (static_cast<float>(scode) / 255.0f) * gsc : gsc;
-      const BlockLut lut = make_block_lut(L.v, sc);
+      const BlockLut lut = make_block_lut(L.v, ok ? sc : 0.0f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
         uint32_t wv[4];
         lut8_decode_order(lut, cw, wv);
-        acc = mfma_16x16x32(ok ? xa[j] : u32x4{0, 0, 0, 0}, u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
+        acc = mfma_16x16x32(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
       }
     }
   }
 
-  // Epilogue operands: H = sum of the LoRA-down partials in a fixed order,
-  // and this workgroup's 16 rows of B.
   red[wave][lane] = acc;
-  for (int idx = tid; idx < M * r; idx += WAVES * 64) {
-    float hv = 0.0f;
-    for (int sp = 0; sp < hsplits; ++sp) hv += hpart[static_cast<int64_t>(sp) * M * r + idx];
-    h_lds[idx] = hv;
-    if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
-  }
-  for (int idx = tid; idx < 16 * r; idx += WAVES * 64) {
-    const int64_t row = n0 + idx / r;
-    b_lds[idx] = b[(row < N ? row : N - 1) * r + idx % r];
-  }
   __syncthreads();
   if (tid >= 256) return;
   const int l2 = tid & 63, v = tid >> 6;
   const int mo = 4 * (l2 >> 4) + v;
-  const int64_t no = n0 + (l2 & 15);
+  const int no = n0 + (l2 & 15);
   if (mo >= M || no >= N) return;
   float sum = 0.0f;
 #pragma unroll
@@ -110,10 +117,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   if (r > 0) {
     float lo = 0.0f;
     const uint16_t* brow = b_lds + (l2 & 15) * r;
-    for (int j = 0; j < r; ++j) lo = fmaf(h_lds[mo * r + j], __uint_as_float(static_cast<uint32_t>(brow[j]) << 16), lo);
+    const float* hrow = h_lds + mo * r;
+    for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], __uint_as_float(static_cast<uint32_t>(brow[j]) << 16), lo);
     sum = fmaf(s, lo, sum);
   }
-  y[static_cast<int64_t>(mo) * N + no] = f32_to_bf16_rne(sum);
+  y[mo * N + no] = f32_to_bf16_rne(sum);
 }
 
 }  // namespace

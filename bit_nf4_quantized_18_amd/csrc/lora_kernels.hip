@@ -14,18 +14,20 @@
 namespace qlora {
 namespace {
 
-// out[m][j] = scale * sum_q P[m][q] Q[j][q]. One workgroup (4 waves) per 16
-// rows of P and one contraction split; waves take interleaved 32-wide chunks
-// of q and are summed in a fixed order through LDS. RT = rpad / 16 output
-// column tiles (0: only the reordered copy of P is produced).
-template <int RT>
-__global__ __launch_bounds__(256) void skinny_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
+// out[m][j] = scale * sum_q P[m][q] Q[j][q]. One workgroup (WAVES waves) per
+// 16 rows of P and one contraction split; waves take interleaved 32-wide
+// chunks of q and are summed in a fixed order through LDS. RT = rpad / 16
+// output column tiles (0: only the reordered copy of P is produced). Narrow
+// ranks get more waves per row block, so that each wave makes only one or
+// two trips to memory.
+template <int RT, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
                                                      int64_t M, int64_t qn, int r, int rpad, float scale,
                                                      float scale2, float* __restrict__ out_f32,
                                                      uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ p_perm,
                                                      int splits) {
   constexpr int kRT = RT > 0 ? RT : 1;
-  __shared__ f32x4 red[4][kRT][64];
+  __shared__ f32x4 red[WAVES][kRT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, g = lane >> 4;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int split = blockIdx.y;
@@ -43,13 +45,13 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t* __restrict_
   // U chunks per wave per trip. Loads are unconditional from clamped
   // addresses (a guarded load makes the compiler wait for all outstanding
   // loads); chunks past the split and ranks past r are zeroed at the operand.
-  constexpr int U = (RT <= 2) ? 4 : (RT <= 4 ? 2 : 1);
+  constexpr int U = (RT <= 2) ? 4 : (RT <= 4 ? 8 : 4);
   const int64_t m_c = m < M ? m : M - 1;
-  for (int64_t c0 = c_begin + wave; c0 < c_end; c0 += 4 * U) {
+  for (int64_t c0 = c_begin + wave; c0 < c_end; c0 += WAVES * U) {
     u32x4 a[U], b[U][kRT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t q = (c0 + 4 * u) * 32 + 8 * g;
+      const int64_t q = (c0 + WAVES * u) * 32 + 8 * g;
       const int64_t q_c = q < qn - 8 ? q : qn - 8;
       a[u] = ld16(P + m_c * qn + q_c);
 #pragma unroll
@@ -60,8 +62,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t* __restrict_
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t q = (c0 + 4 * u) * 32 + 8 * g;
-      const bool qvalid = (c0 + 4 * u < c_end) && q < qn;  // qn % 8 == 0: a valid run is whole
+      const int64_t q = (c0 + WAVES * u) * 32 + 8 * g;
+      const bool qvalid = (c0 + WAVES * u < c_end) && q < qn;  // qn % 8 == 0: a valid run is whole
       const u32x4 av = qvalid ? a[u] : u32x4{0, 0, 0, 0};
       if (p_perm != nullptr && mvalid && qvalid) {
         uint32_t in[4] = {av[0], av[1], av[2], av[3]}, o[4];
@@ -80,13 +82,16 @@ __global__ __launch_bounds__(256) void skinny_kernel(const uint16_t* __restrict_
 #pragma unroll
   for (int t = 0; t < RT; ++t) red[wave][t][lane] = acc[t];
   __syncthreads();
+  if (tid >= 256) return;
   const int l2 = tid & 63, v = tid >> 6;
   const int64_t mo = m0 + 4 * (l2 >> 4) + v;
   if (mo >= M) return;
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     const int j = 16 * t + (l2 & 15);
-    const float sum = ((red[0][t][l2][v] + red[1][t][l2][v]) + red[2][t][l2][v]) + red[3][t][l2][v];
+    float sum = 0.0f;
+#pragma unroll
+    for (int wv = 0; wv < WAVES; ++wv) sum += red[wv][t][l2][v];
     if (splits > 1) {
       if (j < r) out_f32[(split * M + mo) * r + j] = sum;
     } else {
@@ -118,14 +123,17 @@ __global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint
 }
 
 // part[s][j][c] = sum over rows m of split s of U[m][j] * V[m][c] (float32
-// U, bf16 V). A workgroup owns 128 columns (two per lane) and 16 ranks; its
-// four waves take interleaved rows of the split and are summed in LDS in a
-// fixed order. The U row slice is uniform across the workgroup (scalar
-// loads); rows are taken four at a time with all loads issued first.
-__global__ __launch_bounds__(256) void rank_partial_kernel(const float* __restrict__ U, const uint16_t* __restrict__ V,
-                                                           int64_t M, int64_t cn, int r, int splits,
-                                                           float* __restrict__ part) {
-  __shared__ float red[4][16][128];
+// U, bf16 V). A workgroup (16 waves) owns 128 columns (two per lane) and 16
+// ranks; its waves take interleaved rows of the split, 8 rows per trip with
+// all V loads issued first, and are summed in LDS in a fixed order. The
+// 16-rank slice of a U row is the same for every lane, so it is fetched with
+// scalar loads. kFull: r is a multiple of 16 (no rank tail).
+template <bool kFull>
+__global__ __launch_bounds__(1024) void rank_partial_kernel(const float* __restrict__ U, const uint16_t* __restrict__ V,
+                                                            int64_t M, int64_t cn, int r, int splits,
+                                                            float* __restrict__ part) {
+  constexpr int kWaves = 16, kRows = kFull ? 8 : 2;
+  __shared__ float red[kWaves][16][128];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c = static_cast<int64_t>(blockIdx.x) * 128 + 2 * lane;
   const int j0 = blockIdx.y * 16;
@@ -138,24 +146,38 @@ __global__ __launch_bounds__(256) void rank_partial_kernel(const float* __restri
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) acc[jj][0] = acc[jj][1] = 0.0f;
   const int64_t c_c = cvalid ? c : cn - 2;  // columns past cn are computed but never stored
-  for (int64_t m0 = mb + wave; m0 < me; m0 += 16) {
-    uint32_t v2[4];
+  for (int64_t m0 = mb + wave; m0 < me; m0 += kWaves * kRows) {
+    uint32_t v2[kRows];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t m = m0 + 4 * u;
+    for (int u = 0; u < kRows; ++u) {
+      const int64_t m = m0 + kWaves * u;
       v2[u] = *reinterpret_cast<const uint32_t*>(V + (m < me ? m : me - 1) * cn + c_c);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t m = m0 + 4 * u;
+    for (int u = 0; u < kRows; ++u) {
+      const int64_t m = m0 + kWaves * u;
       if (m >= me) break;  // uniform across the wave
       const float v0 = __uint_as_float(v2[u] << 16), v1 = __uint_as_float(v2[u] & 0xFFFF0000u);
+      float uu[16];
+      if (kFull) {
+        const f32x4* up = reinterpret_cast<const f32x4*>(U + __builtin_amdgcn_readfirstlane(static_cast<int>(m)) *
+                                                                 static_cast<int64_t>(r) + j0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 t = up[q];
+          uu[4 * q] = t[0];
+          uu[4 * q + 1] = t[1];
+          uu[4 * q + 2] = t[2];
+          uu[4 * q + 3] = t[3];
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) uu[jj] = U[m * r + ((j0 + jj < r) ? j0 + jj : r - 1)];  // tail never stored
+      }
 #pragma unroll
       for (int jj = 0; jj < 16; ++jj) {
-        const int jc = (j0 + jj < r) ? j0 + jj : r - 1;  // ranks past r are never stored
-        const float uu = U[m * r + jc];
-        acc[jj][0] = fmaf(uu, v0, acc[jj][0]);
-        acc[jj][1] = fmaf(uu, v1, acc[jj][1]);
+        acc[jj][0] = fmaf(uu[jj], v0, acc[jj][0]);
+        acc[jj][1] = fmaf(uu[jj], v1, acc[jj][1]);
       }
     }
   }
@@ -165,11 +187,13 @@ __global__ __launch_bounds__(256) void rank_partial_kernel(const float* __restri
     red[wave][jj][2 * lane + 1] = acc[jj][1];
   }
   __syncthreads();
-  for (int idx = tid; idx < 16 * 128; idx += 256) {
+  for (int idx = tid; idx < 16 * 128; idx += kWaves * 64) {
     const int jj = idx >> 7, cc = idx & 127;
     const int64_t col = static_cast<int64_t>(blockIdx.x) * 128 + cc;
     if (j0 + jj < r && col < cn) {
-      const float sum = ((red[0][jj][cc] + red[1][jj][cc]) + red[2][jj][cc]) + red[3][jj][cc];
+      float sum = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < kWaves; ++wv) sum += red[wv][jj][cc];
       part[(static_cast<int64_t>(s) * r + j0 + jj) * cn + col] = sum;
     }
   }
@@ -197,14 +221,15 @@ template <int RT>
 void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r,
                       int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, uint16_t* p_perm,
                       int splits) {
-  hipLaunchKernelGGL(skinny_kernel<RT>, grid, dim3(256), 0, st, P, Q, m, qn, r, rpad, scale, scale2, out_f32,
-                     out_bf16, p_perm, splits);
+  constexpr int kWaves = (RT <= 2) ? 16 : (RT <= 4 ? 8 : 4);
+  hipLaunchKernelGGL((skinny_kernel<RT, kWaves>), grid, dim3(kWaves * 64), 0, st, P, Q, m, qn, r, rpad, scale, scale2,
+                     out_f32, out_bf16, p_perm, splits);
 }
 
 }  // namespace
 
 int rank_reduce_splits(int64_t m) {
-  int64_t s = m / 256;
+  int64_t s = (m + 511) / 512;  // ~32 rows per wave of a 16-wave workgroup
   if (s < 1) s = 1;
   if (s > 16) s = 16;
   return static_cast<int>(s);
@@ -243,7 +268,11 @@ hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int6
                               int splits, float* part, float* out, int c_major, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((cn + 127) / 128), static_cast<unsigned>((r + 15) / 16),
                   static_cast<unsigned>(splits));
-  hipLaunchKernelGGL(rank_partial_kernel, grid, dim3(256), 0, st, U, V, m, cn, r, splits, part);
+  if (r % 16 == 0) {
+    hipLaunchKernelGGL(rank_partial_kernel<true>, grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+  } else {
+    hipLaunchKernelGGL(rank_partial_kernel<false>, grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+  }
   const int64_t total = static_cast<int64_t>(r) * cn;
   hipLaunchKernelGGL(rank_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, part, cn,
                      r, splits, scale, out, c_major);
