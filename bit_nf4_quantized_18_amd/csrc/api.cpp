@@ -72,8 +72,10 @@ qlora_status check_weight(const qlora_nf4_weight* w, bool linear) {
   if (w->n < 1 || w->k < 1) return QLORA_ERR_SHAPE;
   if (w->n > (INT64_C(1) << 40) / w->k) return QLORA_ERR_SHAPE;
   if (linear && ((w->k % QLORA_BLOCK) != 0 || (w->n % 16) != 0)) return QLORA_ERR_SHAPE;
-  // the matmul kernels address a weight with 32-bit offsets
+  // the matmul kernels address a weight, and a 256-row tile of the
+  // activations (m x k forward, m x n backward), with 32-bit offsets
   if (linear && w->n * w->k > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
+  if (linear && (w->n > (INT64_C(1) << 22) || w->k > (INT64_C(1) << 22))) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
 
@@ -90,6 +92,9 @@ PackedW view(const qlora_nf4_weight* w) {
 }
 
 qlora_status hip_status(hipError_t e) { return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP; }
+
+// The fused GEMM numbers its 256 x 128 output tiles with 32-bit integers.
+bool gemm_tiles_fit(int64_t m, int64_t p) { return ((m + 255) / 256) * ((p + 127) / 128) < (INT64_C(1) << 31); }
 
 #define QLORA_TRY(expr)                       \
   do {                                        \
@@ -160,6 +165,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int6
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
   if (r < 0) return QLORA_ERR_SHAPE;
   if (r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
+  if (!gemm_tiles_fit(m, w->n)) return QLORA_ERR_SHAPE;
   if (m == 0) return QLORA_OK;
   if (x == nullptr || y == nullptr) return QLORA_ERR_NULL;
   if (r > 0 && (a == nullptr || b == nullptr)) return QLORA_ERR_NULL;
@@ -202,6 +208,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
   if (r < 0) return QLORA_ERR_SHAPE;
   if (r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
   const int64_t n = w->n, k = w->k;
+  if (!gemm_tiles_fit(m, k)) return QLORA_ERR_SHAPE;
   if (r > 0) {
     if (a == nullptr || b == nullptr || da == nullptr || db == nullptr) return QLORA_ERR_NULL;
     if (!aligned16(a) || !aligned16(b) || !aligned16(da) || !aligned16(db)) return QLORA_ERR_ALIGN;

@@ -15,14 +15,17 @@
 //   * Waves 0-3 (consumers) each own a 128 x 64 sub-tile, 8 x 4 tiles of the
 //     16x16x32 bf16 MFMA. They only read LDS and issue MFMAs; the fragments
 //     of the next half-step are read while the current MFMAs run.
-//   * Waves 4-7 (producers) stream the A tile (two steps of register
-//     prefetch) and the packed codes and scales (four steps), build each
-//     block's bf16 lookup table (nf4_lut.h), unpack the codes and write both
-//     tiles into LDS two steps ahead of the consumers.
+//   * Waves 4-7 (producers) copy the A tile from global memory straight
+//     into LDS (buffer loads with the LDS-destination bit: no registers, no
+//     LDS write instructions), and stream the packed codes and scales two
+//     steps ahead, build each block's bf16 lookup table (nf4_lut.h), unpack
+//     the codes and write the weight tile into LDS.
 //   With one consumer and one producer wave per SIMD, unpacking (VALU) and
-//   LDS writes overlap the consumers' matrix-core work. LDS holds a ring of
-//   three stages (3 x 48 KB), so a buffer is written two steps before it is
-//   read and one barrier per step suffices.
+//   LDS traffic overlap the consumers' matrix-core work. LDS holds a ring of
+//   three stages (3 x 48 KB): stage kt+2 is filled during step kt, and one
+//   barrier per step suffices; before it every producer waits until its own
+//   copies for stage kt+2 have landed (loads complete in issue order, so one
+//   counter wait covers them).
 // All global reads go through buffer resources: rows past M or N and blocks
 // past the end read as zeros in hardware, with no branch, clamp or select
 // (a guarded load would make the compiler wait for every outstanding load);
@@ -57,6 +60,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 // element offset of (row, 16-byte chunk) in a swizzled 64-wide LDS tile
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBQ + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <bool kTransW, bool kDQ>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,
                                                        int64_t P, int64_t Qn, const uint16_t* __restrict__ ep_a,
@@ -68,15 +81,18 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   // --- tile of this workgroup (XCD-aware order) ----------------------------
-  const int64_t tiles_p = (P + kBP - 1) / kBP;
-  const int64_t tiles_m = (M + kBM - 1) / kBM;
-  const int64_t T = tiles_p * tiles_m;
-  const int64_t id = blockIdx.x;
-  const int64_t xcd = id % kXcds, local = id / kXcds;
-  const int64_t start = xcd * (T / kXcds) + (xcd < T % kXcds ? xcd : T % kXcds);
-  const int64_t lin = start + local;  // bijection of [0, T)
-  const int64_t m0 = (lin / tiles_p) * kBM;
-  const int64_t p0 = (lin % tiles_p) * kBP;
+  // 32-bit tile arithmetic (the host bounds the tile count by 2^31); the tile
+  // origin is made explicitly wave-uniform so that addresses and buffer
+  // resources derived from it stay in scalar registers.
+  const uint32_t tiles_p = static_cast<uint32_t>((P + kBP - 1) / kBP);
+  const uint32_t tiles_m = static_cast<uint32_t>((M + kBM - 1) / kBM);
+  const uint32_t T = tiles_p * tiles_m;
+  const uint32_t id = blockIdx.x;
+  const uint32_t xcd = id % kXcds, local = id / kXcds;
+  const uint32_t start = xcd * (T / kXcds) + (xcd < T % kXcds ? xcd : T % kXcds);
+  const uint32_t lin = start + local;  // bijection of [0, T)
+  const int64_t m0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(lin / tiles_p)) * kBM;
+  const int64_t p0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(lin % tiles_p)) * kBP;
 
   const int64_t K = w.k;
   const int64_t nbk = K / 64;
@@ -85,8 +101,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   if (wave >= 4) {
     // ======================= producers =======================
     const int pt = tid - 256;
-    // A tile: chunks pt + 256 u -> row pt/8 + 32 u, 16-byte chunk pt % 8
-    const int a_row = pt >> 3, a_chunk = pt & 7;
+    const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
     // W: forward -> weight row p0 + pt/2, k-half pt%2 of the step;
     //    backward -> weight row q0 + pt%64, k-quarter pt/64 of the output tile
     const int w_r = kTransW ? (pt & 63) : (pt >> 1);
@@ -97,9 +112,17 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     const __amdgpu_buffer_rsrc_t srsrc =
         kDQ ? make_rsrc(w.scale_codes, w.n * nbk) : make_rsrc(w.absmax, w.n * nbk * 4);
     const __amdgpu_buffer_rsrc_t grsrc = make_rsrc(w.group_scale, ((w.n * nbk + kGroup - 1) / kGroup) * 4);
+    // A tile, global -> LDS without registers: load u of producer wave pw
+    // fills the 1 KB of LDS rows 8 (8 pw + u) .. +7, lane l writing the 16
+    // bytes of row l / 8, stored chunk l % 8, so it fetches the logical chunk
+    // that the swizzle puts there. Offsets fit 32 bits: the host bounds Qn.
     int a_voff[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) a_voff[u] = static_cast<int>(((a_row + 32 * u) * Qn + a_chunk * 8) * 2);
+    for (int u = 0; u < 8; ++u) {
+      const int row = (pw * 8 + u) * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ ((row >> 1) & 7);
+      a_voff[u] = static_cast<int>((row * Qn + chunk * 8) * 2);
+    }
     // per-step byte offsets: A moves by 64 columns; the weight moves along k
     // (forward) or by 64 rows (backward)
     const int64_t wrow0 = kTransW ? w_r : p0 + w_r;
@@ -110,14 +133,16 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     const int s_step = kTransW ? static_cast<int>(kBQ * nbk) : 1;
     const bool wk_ok = wk0 < K;  // backward: the output tile may pass K
 
-    u32x4 ra[2][8];  // A ring (2 stages)
-    u32x4 rc[4];     // codes ring (4 stages)
-    uint32_t rs[4];  // scale code ring (double quant)
-    float rg[4];     // group max (double quant) or absmax ring
+    u32x4 rc[2];     // codes ring (2 stages)
+    uint32_t rs[2];  // scale code ring (double quant)
+    float rg[2];     // group max (double quant) or absmax ring
 
-    auto load_a = [&](int kt, u32x4(&dst)[8]) {
+    auto dma_a = [&](int kt) {
+      uint16_t* as = As + (kt % kStages) * kAStage + pw * (8 * 512);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) dst[u] = __builtin_amdgcn_raw_buffer_load_b128(arsrc, a_voff[u] + kt * kBQ * 2, 0, 0);
+      for (int u = 0; u < 8; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(as + u * 512), 16,
+                                                 a_voff[u] + kt * kBQ * 2, 0, 0, 0);
     };
     auto load_w = [&](int kt, u32x4& c, uint32_t& sc, float& gs) {
       c = __builtin_amdgcn_raw_buffer_load_b128(crsrc, c_voff + kt * c_step, 0, 0);
@@ -130,11 +155,8 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
         gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff * 4, 0, 0));
       }
     };
-    auto store = [&](int kt, const u32x4(&a)[8], u32x4 c, uint32_t sc, float gs) {
-      uint16_t* as = As + (kt % kStages) * kAStage;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) st16(as + swz(a_row + 32 * u, a_chunk), a[u]);
-      const float s = kDQ ? (static_cast<float>(sc) / 255.0f) * gs : gs;
+    auto store_w = [&](int kt, u32x4 c, uint32_t sc, float gs) {
+      const float s = kDQ ? u8_unit(sc) * gs : gs;
       const BlockLut lut = make_block_lut(L.v, wk_ok ? s : 0.0f);
       uint16_t* bs = Bs + (kt % kStages) * kBStage;
 #pragma unroll
@@ -154,35 +176,48 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
         }
       }
     };
+    // Loads complete in issue order, so "at most the last kWLoads loads
+    // outstanding" means that everything issued before this step's weight
+    // loads -- in particular this step's A tile -- has landed in LDS.
+    constexpr int kWLoads = kDQ ? 3 : 2;
 
-    // prologue: stages 0 and 1 into LDS; A of stages 2, 3 and codes of
-    // stages 2..5 in flight
-    load_a(0, ra[0]);
-    load_a(1, ra[1]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) load_w(s, rc[s], rs[s], rg[s]);
-    store(0, ra[0], rc[0], rs[0], rg[0]);
-    load_a(2, ra[0]);
-    load_w(4, rc[0], rs[0], rg[0]);
-    if (nk > 1) store(1, ra[1], rc[1], rs[1], rg[1]);
-    load_a(3, ra[1]);
-    load_w(5, rc[1], rs[1], rg[1]);
+    // prologue: A of stages 0 and 1 and unpacked W of stages 0 and 1 in LDS;
+    // codes of stage 2 loaded, of stage 3 in flight
+    dma_a(0);
+    dma_a(1);
+    load_w(0, rc[0], rs[0], rg[0]);
+    load_w(1, rc[1], rs[1], rg[1]);
+    store_w(0, rc[0], rs[0], rg[0]);
+    load_w(2, rc[0], rs[0], rg[0]);
+    store_w(1, rc[1], rs[1], rg[1]);
+    load_w(3, rc[1], rs[1], rg[1]);
+    // same state at the loop head from here and from the loop's back edge:
+    // only the codes of the next stage outstanding
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<kWLoads>();
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    // step kt: write stage kt+2 (A slot (kt+2)%2, codes slot (kt+2)%4), then
-    // refill those slots with stage kt+4 (A) and kt+6 (codes). Loads past the
-    // last stage read zeros (out of the buffer resources) and are never used.
-    auto step = [&](int kt, u32x4(&a)[8], int cs) {
-      if (kt + 2 < nk) store(kt + 2, a, rc[cs], rs[cs], rg[cs]);
-      load_a(kt + 4, a);
-      load_w(kt + 6, rc[cs], rs[cs], rg[cs]);
+    // step kt: stage kt+2 into LDS (A by DMA, W unpacked from the codes
+    // loaded two steps ago), then the codes of stage kt+4. Every step does
+    // the same work, so the compiler sees one fixed sequence of loads: near
+    // the end the stages past the last one are filled too, from zeros (reads
+    // outside the buffer resources) or from unused in-range bytes, into LDS
+    // slots that are read neither now nor later.
+    auto step = [&](int kt, int cs) {
+      dma_a(kt + 2);
+      store_w(kt + 2, rc[cs], rs[cs], rg[cs]);
+      load_w(kt + 4, rc[cs], rs[cs], rg[cs]);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<kWLoads>();
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     };
-    for (int kt = 0; kt < nk; kt += 4) {
-      step(kt, ra[0], 2);
-      if (kt + 1 < nk) step(kt + 1, ra[1], 3);
-      if (kt + 2 < nk) step(kt + 2, ra[0], 0);
-      if (kt + 3 < nk) step(kt + 3, ra[1], 1);
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(kt, 0);
+      if (kt + 1 < nk) step(kt + 1, 1);
     }
+    // no load may still be writing LDS when the wave ends
+    wait_vmcnt<0>();
     return;
   }
 

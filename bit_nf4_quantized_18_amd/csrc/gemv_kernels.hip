@@ -92,7 +92,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     // wave-uniform: skip a pass slot no lane group of this wave uses
     if (base + wave * 4 < nbk) {
       const bool ok = (n < N) && (kb < nbk);
-      const float sc = kDQ ? (static_cast<float>(scode) / 255.0f) * gsc : gsc;
+      const float sc = kDQ ? u8_unit(scode) * gsc : gsc;
       const BlockLut lut = make_block_lut(L.v, ok ? sc : 0.0f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {

@@ -81,6 +81,20 @@ __host__ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 #endif
 }
 
+// fl32(k / 255) for an 8-bit scale code k, the double-quantization level
+// (Ultralytics glossary "QLoRA", "Come funziona QLoRA": the block scales are
+// themselves stored as 8-bit codes). One multiply by fl32(1/255) and one FMA
+// correction with the exact residual k - 255 q0 give the correctly rounded
+// quotient for every k in 0..255 (checked exhaustively on the host), at 3
+// instructions instead of a full IEEE division.
+__host__ __device__ __forceinline__ float u8_unit(uint32_t k) {
+  const float kf = static_cast<float>(k);
+  const float c = 1.0f / 255.0f;
+  const float q0 = kf * c;
+  const float r = fmaf(-q0, 255.0f, kf);
+  return fmaf(r, c, q0);
+}
+
 struct BlockLut {
   uint32_t tl[4];  // low bytes of T[0..15], 4 per dword
   uint32_t th[4];  // high bytes of T[0..15]

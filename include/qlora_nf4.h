@@ -126,8 +126,9 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dty
 /* Forward: Y = X W16^T + s (X A^T) B^T with s = fl32(alpha / r).
  * Ultralytics glossary "QLoRA", "Come funziona QLoRA" (forward paragraph);
  * "LoRA y QLoRA en Profundidad", "La Idea Central" / "Alpha".
- *   w     : packed NF4 weight, n x k, k % 64 == 0, n % 16 == 0, n * k <= 2^31.
- *   x     : bf16 (uint16 bit patterns) m x k.
+ *   w     : packed NF4 weight, n x k, k % 64 == 0, n % 16 == 0, n * k <= 2^31,
+ *           n <= 2^22 and k <= 2^22.
+ *   x     : bf16 (uint16 bit patterns) m x k, m <= 2^31.
  *   a     : bf16 r x k; b : bf16 n x r. r = 0 (a, b NULL) means base only.
  *   y     : bf16 m x n output.
  *   h_out : optional float32 m x r output of H = X A^T (pass it to the

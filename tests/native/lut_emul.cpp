@@ -18,3 +18,8 @@ extern "C" int decode_order_emul(const uint32_t* in, int n, uint32_t* out) {
   for (int i = 0; i < n; ++i) qlora::to_decode_order(in + 4 * i, out + 4 * i);
   return 0;
 }
+
+extern "C" int u8_unit_emul(float* out) {
+  for (uint32_t k = 0; k < 256; ++k) out[k] = qlora::u8_unit(k);
+  return 256;
+}

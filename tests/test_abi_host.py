@@ -108,6 +108,13 @@ def test_linear_argument_errors():
     assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, None, P, ws_need - 1, None) == -5
     assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, None, None, 0, None) == -5
     assert f(ctypes.byref(ok), P, 0, None, None, 8, 16.0, None, None, None, 0, None) == 0  # m = 0: no-op
+    # 32-bit offsets inside the kernels: n, k <= 2^22 and fewer than 2^31 output tiles
+    assert f(ctypes.byref(wstruct(n=(1 << 22) + 16, k=64)), P, 32, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
+    assert f(ctypes.byref(wstruct(n=16, k=(1 << 22) + 64)), P, 32, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
+    big = wstruct(n=1 << 20, k=64)
+    assert f(ctypes.byref(big), P, 1 << 31, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
+    assert b(ctypes.byref(wstruct(n=64, k=1 << 20)), P, P, 1 << 31, P, P, 8, 16.0, None, P, P, P, P, ws_need,
+             None) == -2
     # backward
     assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, None, P, None, P, P, ws_need, None) == -1
     assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, None, P, P, P, P, 16, None) == -5

@@ -60,3 +60,13 @@ def test_decode_order_permutation(emul):
     f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     f(x.ctypes.data, 100, out.ctypes.data)
     assert np.array_equal(out.reshape(-1, 8), x.reshape(-1, 8)[:, [0, 2, 4, 6, 1, 3, 5, 7]])
+
+
+def test_scale_code_unit_is_correctly_rounded(emul):
+    """The kernels' 3-instruction k/255 equals the oracle's double-quant
+    levels fl32(k/255) for every 8-bit code."""
+    out = np.zeros(256, np.float32)
+    f = emul.u8_unit_emul
+    f.argtypes = [ctypes.c_void_p]
+    assert f(out.ctypes.data) == 256
+    assert np.array_equal(out.view(np.uint32), O.u8_scale_levels().astype(np.float32).view(np.uint32))
