@@ -57,7 +57,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run (train,gemm,decode,dequant,quant,cpu)")
+    ap.add_argument("--only", default="", help="comma list of parts to run (train,gemm,copy,decode,dequant,quant,cpu)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -177,11 +177,32 @@ def main():
                          "frac": ach / BF16_PEAK_TFLOPS, "avg_launch_ms": tot_ms / len(layers), "per_layer": per}
             log(f"[bench] gemm {kind}: {ach:.1f} TFLOP/s ({100 * ach / BF16_PEAK_TFLOPS:.1f}% of bf16 peak)")
         parts["fused_gemm"] = res
+        traffic, traffic_src = measured_traffic()
         roofline = {"bound": "mfma", "achieved": res["fwd"]["achieved_tflops"], "peak": BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": res["fwd"]["frac"], "traffic": None,
+                    "unit": "TFLOP/s", "frac": res["fwd"]["frac"], "traffic": traffic,
+                    "traffic_unit": "bytes per launch (HBM fetch + write, calibrated)", "traffic_source": traffic_src,
                     "kernel": res["fwd"]["kernel"],
                     "per_launch_gflop": step_fwd_base(layers, M) / len(layers) / 1e9,
                     "avg_launch_ms": res["fwd"]["avg_launch_ms"]}
+
+    # ------------------------------------- plain copy (counter calibration)
+    if want("copy"):
+        nbytes = 1 << 30
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 5
+        parts["plain_copy"] = {"bytes_read": nbytes, "bytes_written": nbytes, "us": us,
+                               "GBps_read_plus_write": 2 * nbytes / (us * 1e-6) / 1e9}
+        log(f"[bench] plain 1 GiB device copy: {us:.1f} us  {2 * nbytes / (us * 1e-6) / 1e9:.0f} GB/s (read+write)")
+        del src, dst
 
     # ---------------------------------------------------------- decode GEMV
     shapes = [(4096, 4096), (11008, 4096)]
@@ -305,16 +326,51 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "nf4_gemm_fwd_7b_layers_traffic.md")
+GEMM_SOURCES = ["gemm_kernels.hip", "nf4_lut.h", "mfma.h", "internal.h"]
+
+
+def gemm_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "bit_nf4_quantized_18_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward fused GEMM from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source
+    (its sha256 is recorded there); otherwise None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None, "no counter summary"
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            key, _, v = line[2:].partition(": ")
+            vals[key.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != gemm_source_hash():
+        return None, "kernel source changed since the counters were taken"
+    try:
+        return float(vals["traffic_bytes_per_launch"]), os.path.relpath(TRAFFIC_FILE, ROOT)
+    except (KeyError, ValueError):
+        return None, "counter summary unreadable"
+
+
 def step_fwd_base(layers, M):
     return sum(2.0 * M * L["lay"].n * L["lay"].k for L in layers)
 
 
 def cpu_baseline(layers, M, R, ALPHA, wl):
     """The oracle, untouched, on a bounded sample of the same step: for every
-    linear, the first 1024 weight rows (output features) and the first 128
-    token rows; oracle quantization (not timed), then oracle dequantization,
-    float64 forward and backward (timed). Scaled to the metric's unit with the
-    sample's algorithmic flops."""
+    linear, the first 2048 weight rows (output features) and all 2048 token
+    rows; oracle quantization (not timed), then oracle dequantization,
+    float64 forward and backward (timed, about 10-20 s on a 16-core host).
+    Scaled to the metric's unit with the sample's algorithmic flops."""
     import numpy as np
 
     import synth
@@ -326,7 +382,7 @@ def cpu_baseline(layers, M, R, ALPHA, wl):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
-    ms, ns = 128, 1024
+    ms, ns = 2048, 2048
     flops = 0.0
     t_total = 0.0
     for L in layers:
