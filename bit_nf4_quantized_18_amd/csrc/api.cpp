@@ -27,15 +27,20 @@ struct Carve {
 };
 
 struct FwdLayout {
-  int64_t h32, hs, xp, total;
+  int64_t h32, hs, total;
 };
 FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r) {
   (void)n;
   Carve c;
   FwdLayout L{};
-  L.h32 = c.take((m <= kGemvMaxM ? qlora::skinny_splits(m, k) : 1) * m * r * 4);
-  L.hs = c.take(m <= kGemvMaxM ? 0 : m * rank_pad(r) * 2);
-  L.xp = c.take(m <= kGemvMaxM ? m * k * 2 : 0);
+  if (m <= kGemvMaxM) {
+    // decode: H partial sums, unless the GEMV computes H itself
+    L.h32 = c.take(qlora::gemv_fuses_h(k, r) ? 0 : qlora::skinny_splits(m, k) * m * r * 4);
+    L.hs = c.take(0);
+  } else {
+    L.h32 = c.take(m * r * 4);
+    L.hs = c.take(m * rank_pad(r) * 2);
+  }
   L.total = c.off;
   return L;
 }
@@ -184,16 +189,19 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int6
   const PackedW pw = view(w);
 
   if (m <= kGemvMaxM) {
-    // H as per-split partial sums in the workspace; the GEMV sums them.
-    uint16_t* xp = reinterpret_cast<uint16_t*>(base + L.xp);
-    float* hpart = (r == 0) ? nullptr : reinterpret_cast<float*>(base + L.h32);
-    QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, hpart, nullptr, xp,
-                                   qlora::skinny_splits(m, k), stream));
-    QLORA_TRY(qlora::launch_gemv(pw, xp, m, hpart, qlora::skinny_splits(m, k), b, r, s, y, h_out, stream));
+    // One launch when the GEMV computes H itself; otherwise H as per-split
+    // partial sums in the workspace, which the GEMV sums.
+    float* hpart = nullptr;
+    const int splits = qlora::skinny_splits(m, k);
+    if (r > 0 && !qlora::gemv_fuses_h(k, r)) {
+      hpart = reinterpret_cast<float*>(base + L.h32);
+      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, hpart, nullptr, splits, stream));
+    }
+    QLORA_TRY(qlora::launch_gemv(pw, x, m, a, hpart, splits, b, r, s, y, h_out, stream));
   } else {
     float* h32 = (r == 0) ? nullptr : (h_out != nullptr ? h_out : reinterpret_cast<float*>(base + L.h32));
     uint16_t* hs = (r == 0) ? nullptr : reinterpret_cast<uint16_t*>(base + L.hs);
-    if (r > 0) QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, s, h32, hs, nullptr, 1, stream));
+    if (r > 0) QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, s, h32, hs, 1, stream));
     QLORA_TRY(qlora::launch_gemm_fwd(pw, x, m, hs, b, r, rp, y, stream));
   }
   return QLORA_OK;
@@ -246,12 +254,12 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
     const float* h = h_saved;
     if (h == nullptr) {
       float* h32 = reinterpret_cast<float*>(base + L.h32);
-      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, h32, nullptr, nullptr, 1, stream));
+      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, h32, nullptr, 1, stream));
       h = h32;
     }
     QLORA_TRY(qlora::launch_lora_transpose(a, b, n, k, r, rp, at, bt, stream));
     // dH = s dY B  (contraction over n, with B^T as the r x n operand)
-    QLORA_TRY(qlora::launch_skinny(dy, bt, m, n, r, rp, s, 1.0f, dh32, dhs, nullptr, 1, stream));
+    QLORA_TRY(qlora::launch_skinny(dy, bt, m, n, r, rp, s, 1.0f, dh32, dhs, 1, stream));
     const int splits = qlora::rank_reduce_splits(m);
     // dA = dH^T X  (r x k)
     QLORA_TRY(qlora::launch_rank_reduce(dh32, x, m, k, r, 1.0f, splits, part, da, 0, stream));

@@ -1,11 +1,13 @@
 // Decode path (m <= 16 tokens): Y = X W16^T + s H B^T with W read straight
-// from its packed NF4 form.
+// from its packed NF4 form, in one launch.
 //
 // Ultralytics glossary "QLoRA", section "Come funziona QLoRA": each frozen
 // layer dequantizes its NF4 weights to bfloat16 right before the matmul and
-// adds the LoRA path output. At a handful of tokens the layer is bound by the
-// HBM stream of the packed weight (0.5 B of codes + 1/64 B of scale codes per
-// weight), so the kernel is built around that stream:
+// adds the LoRA path output ("LoRA y QLoRA en Profundidad", "La Idea Central":
+// H = X A^T, then (alpha / r) H B^T). At a handful of tokens the layer is
+// bound by the HBM stream of the packed weight (0.5 B of codes + 1/64 B of
+// scale codes per weight) and by the latency of one trip to memory, so the
+// kernel is built around that stream:
 //   * a workgroup owns 16 weight rows; its WAVES x 4 lane groups split the
 //     row's 64-blocks round-robin, so every lane loads whole blocks (32 B of
 //     codes, two 16-byte loads); all loads of a pass are issued
@@ -14,11 +16,21 @@
 //     trip -- a guarded load would make the compiler wait for every
 //     outstanding load at the guard;
 //   * per block a lane decodes the scale, builds a 16-entry bf16 table in
-//     registers (nf4_lut.h) and looks up 8 weights per table access;
+//     registers (nf4_lut.h) and looks up 8 weights per table access, in
+//     natural order, so X is used as it lies in memory;
 //   * the dot products run on the matrix cores (16x16x32 bf16 MFMA with the
-//     tokens padded to 16 rows), so the vector ALU only unpacks;
-//   * X is pre-arranged by the LoRA-down kernel in the lookup's output order,
-//     and partial sums of the waves are reduced in a fixed order in LDS.
+//     tokens padded to 16), so the vector ALU only unpacks;
+//   * with kFuseH every workgroup computes H = X A^T for itself, so the
+//     LoRA-down product needs no launch of its own: in each pass a wave
+//     multiplies 8 consecutive 32-wide chunks of X and A (lanes of one
+//     16-byte load cover 16 rows x 64 contiguous bytes, so a cache line is
+//     consumed by two neighbouring loads). The first 4 chunks are loaded
+//     before the weight codes and multiplied while the codes are still in
+//     flight; the other 4 are loaded behind the codes and multiplied after
+//     the main product. Without kFuseH (large r * k), H arrives as partial
+//     sums from the skinny kernel;
+//   * partial sums of the waves are reduced in a fixed order in LDS, so
+//     results do not depend on scheduling.
 #include "internal.h"
 #include "mfma.h"
 #include "nf4_lut.h"
@@ -28,16 +40,36 @@ namespace {
 
 constexpr int kGroup = 256;
 
-template <int WAVES, bool kDQ>
-__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ xp, int M,
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int WAVES, bool kDQ, bool kFuseH>
+__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
+                                                          const uint16_t* __restrict__ a,
                                                           const float* __restrict__ hpart, int hsplits,
                                                           const uint16_t* __restrict__ b, int r, float s,
                                                           uint16_t* __restrict__ y, float* __restrict__ h_out,
                                                           Levels L) {
+  static_assert(WAVES == 16, "one pass covers 64 blocks; A is staged as 16 rows x 64 blocks");
   constexpr int kLaneGroups = WAVES * 4;
-  __shared__ f32x4 red[WAVES][64];
+  // With kFuseH, the pass's slice of A (16 ranks x 4096 k, bf16) lives in LDS;
+  // after the last pass the same bytes hold the cross-wave reductions.
+  constexpr int kARow = kLaneGroups * 64 * 2;  // bytes of one rank row of the slice
+  constexpr int kRedBytes = (kFuseH ? 2 : 1) * WAVES * 64 * 16;
+  constexpr int kStage = kFuseH ? 16 * kARow : kRedBytes;
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage > kRedBytes ? kStage : kRedBytes];
   __shared__ float h_lds[16 * QLORA_MAX_RANK];
   __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
+  f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(stage);
+  f32x4(*hred)[64] = reinterpret_cast<f32x4(*)[64]>(stage + WAVES * 64 * 16);
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
   const int G = wave * 4 + g;
@@ -46,14 +78,52 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   const int nbk = K / 64;
   const int n0 = blockIdx.x * 16;
   const int n = n0 + i;
-  const int n_c = n < N ? n : N - 1;     // clamped: every load is unconditional
-  const int xrow = i < M ? i : M - 1;    // rows past M feed outputs that are never stored
+  const int n_c = n < N ? n : N - 1;  // clamped: every load is unconditional
+  // X through a buffer resource sized to its M rows: the lanes of padding
+  // tokens (i >= M) read zeros without touching memory (with one token, 15 of
+  // every 16 lanes). A likewise with its r rows.
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), static_cast<short>(0),
+                                                                        M * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), static_cast<short>(0),
+                                                                        kFuseH ? r * K * 2 : 0, 0x00020000);
+  const int wv_u = __builtin_amdgcn_readfirstlane(wave);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 hacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int kBPer = (16 * QLORA_MAX_RANK + WAVES * 64 - 1) / (WAVES * 64);  // B values per thread
+  uint16_t bv[kBPer];
+  const int blast = N * r - 1;
+
   // One block per lane group per pass. All loads of a pass (codes, scale,
   // X) are issued unconditionally from clamped addresses before any is used;
   // a block past the row or past K gets a zero scale, so its weights are 0.
   for (int base = 0; base < nbk; base += kLaneGroups) {
+    if (base == 0 && r > 0) {
+      // this workgroup's 16 rows of B (contiguous in memory), into registers
+      // now and into LDS after the main product, so that no wait for them
+      // holds up the weight loads (indices clamped to the last element of B;
+      // rows past N are never stored). With r = 0 there is no B to read.
+#pragma unroll
+      for (int u = 0; u < kBPer; ++u) {
+        const int e = n0 * r + tid + u * WAVES * 64;
+        bv[u] = b[e < blast ? e : blast];
+      }
+    }
+    if (kFuseH) {
+      // Rank row `wave` of the pass's slice of A, global -> LDS in 8 copies
+      // of 1 KB (contiguous in memory: whole cache lines). Lane l of copy t
+      // fetches 16-byte piece 64 t + (l ^ wave) of the row into LDS slot l,
+      // so the 16 ranks of one piece land in 16 different bank groups.
+      // Bytes past the end of the row's k range are never multiplied.
+      if (base > 0) __syncthreads();  // the previous slice has been read
+      const int roff = (wv_u * K + base * 64) * 2 + 16 * (lane ^ wave);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(stage + wv_u * kARow + t * 1024), 16,
+                                                 roff + t * 1024, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int kb = base + G;
     const int kb_c = kb < nbk ? kb : nbk - 1;
     const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_c * 32));
@@ -69,24 +139,17 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
       gsc = w.absmax[bi];
     }
     u32x4 xa[8];
-    const uint16_t* xr = xp + xrow * K + kb_c * 64;
+    const int xoff = (i * K + kb_c * 64) * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = ld16(xr + 8 * j);
-    if (base == 0) {
-      // Epilogue operands, fetched while the weight loads are in flight: H =
-      // sum of the LoRA-down partials (fixed order) and this workgroup's 16
-      // rows of B (contiguous in memory).
+    for (int j = 0; j < 8; ++j) xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0);
+    if (base == 0 && !kFuseH) {
+      // H = sum of the LoRA-down partials (fixed order)
       const int mr = M * r;
       for (int idx = tid; idx < mr; idx += WAVES * 64) {
         float hv = 0.0f;
         for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
         h_lds[idx] = hv;
         if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
-      }
-      const int blast = N * r - 1;
-      for (int idx = tid; idx < 16 * r; idx += WAVES * 64) {
-        const int e = n0 * r + idx;
-        b_lds[idx] = b[e < blast ? e : blast];  // rows past N are never stored
       }
     }
     // wave-uniform: skip a pass slot no lane group of this wave uses
@@ -98,17 +161,56 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
       for (int j = 0; j < 8; ++j) {
         const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
         uint32_t wv[4];
-        lut8_decode_order(lut, cw, wv);
+        lut8_natural_order(lut, cw, wv);
         acc = mfma_16x16x32(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
       }
     }
+    if (kFuseH) {
+      // H product of the pass, after the main one so that the copies of A
+      // overlap it. All loads are consumed by now; wait for the copies, and
+      // for every wave's through the barrier.
+      wait_vmcnt<0>();
+      __syncthreads();
+      if (base + wave * 4 < nbk) {
+        const bool kval = kb < nbk;
+        // this lane's A fragments: rank i, pieces 8 G + j of the slice
+        const unsigned char* arow = stage + i * kARow;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = 8 * G + j;
+          const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
+          hacc = mfma_16x16x32(xa[j], kval ? af : u32x4{0, 0, 0, 0}, hacc);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kBPer; ++u) {
+    const int idx = tid + u * WAVES * 64;
+    if (idx < 16 * r) b_lds[idx] = bv[u];  // r = 0: never, bv unset
   }
 
+  if (kFuseH) __syncthreads();  // the last slice of A has been read
   red[wave][lane] = acc;
+  if (kFuseH) hred[wave][lane] = hacc;
   __syncthreads();
+  const int l2 = tid & 63, v = tid >> 6;  // used by the first 256 threads
+  const int mo = 4 * (l2 >> 4) + v;       // token row of the 16 x 16 tile
+  if (kFuseH) {
+    // H[mo][j] of the (token, rank) tile, j = l2 & 15
+    if (tid < 256) {
+      const int j = l2 & 15;
+      float hv = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < WAVES; ++wv) hv += hred[wv][l2][v];
+      if (mo < M && j < r) {
+        h_lds[mo * r + j] = hv;
+        if (h_out != nullptr && blockIdx.x == 0) h_out[mo * r + j] = hv;
+      }
+    }
+    __syncthreads();
+  }
   if (tid >= 256) return;
-  const int l2 = tid & 63, v = tid >> 6;
-  const int mo = 4 * (l2 >> 4) + v;
   const int no = n0 + (l2 & 15);
   if (mo >= M || no >= N) return;
   float sum = 0.0f;
@@ -126,13 +228,20 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
 
 }  // namespace
 
-hipError_t launch_gemv(const PackedW& w, const uint16_t* xp, int64_t m, const float* hpart, int hsplits,
-                       const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
+bool gemv_fuses_h(int64_t k, int r) {
+  (void)k;
+  return r > 0 && r <= 16;
+}
+
+hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
+                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
   constexpr int kWaves = 16;
   const unsigned grid = static_cast<unsigned>((w.n + 15) / 16);
-  auto kern = w.dq ? gemv_kernel<kWaves, true> : gemv_kernel<kWaves, false>;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, xp, static_cast<int>(m), hpart, hsplits, b, r, s,
-                     y, h_out, nf4_table());
+  const bool fuse = gemv_fuses_h(w.k, r);
+  auto kern = w.dq ? (fuse ? gemv_kernel<kWaves, true, true> : gemv_kernel<kWaves, true, false>)
+                   : (fuse ? gemv_kernel<kWaves, false, true> : gemv_kernel<kWaves, false, false>);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a, hpart, hsplits, b, r,
+                     s, y, h_out, nf4_table());
   return hipGetLastError();
 }
 

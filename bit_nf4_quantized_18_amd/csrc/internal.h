@@ -46,18 +46,17 @@ hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream
 // out_bf16 (m x rpad, zero-padded for j >= r, may be null) holding
 // bf16(scale2 * scale * sum). With several splits (m <= 16, see
 // skinny_splits, decode path only) it writes raw partial sums to out_f32 as splits x m x r.
-// If p_perm is non-null it receives P with every group of 8 consecutive
-// elements reordered as (0,2,4,6,1,3,5,7) (the decode kernel's operand order).
 hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
-                         float scale, float scale2, float* out_f32, uint16_t* out_bf16, uint16_t* p_perm,
-                         int splits, hipStream_t s);
+                         float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s);
 int skinny_splits(int64_t m, int64_t qn);
 
-// Decode GEMV, m <= 16: y = x W16^T + s * h B^T. xp is x in decode operand
-// order, hpart holds hsplits partial sums of H (hsplits x m x r float32,
-// ignored when r = 0); h_out (m x r, may be null) receives H.
-hipError_t launch_gemv(const PackedW& w, const uint16_t* xp, int64_t m, const float* hpart, int hsplits,
-                       const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st);
+// Decode GEMV, m <= 16: y = x W16^T + s * h B^T in one launch when
+// gemv_fuses_h(k, r) (H = x A^T computed in the kernel from a); otherwise
+// hpart holds hsplits partial sums of H (hsplits x m x r float32, from
+// launch_skinny). r = 0: base only. h_out (m x r, may be null) receives H.
+bool gemv_fuses_h(int64_t k, int r);
+hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
+                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st);
 
 // Fused dequant-GEMM, forward: y = x W16^T + hs B^T where hs is bf16 m x rpad
 // (already scaled by s), b is n x r bf16.

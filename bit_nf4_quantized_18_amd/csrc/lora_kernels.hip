@@ -24,15 +24,13 @@ template <int RT, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
                                                      int64_t M, int64_t qn, int r, int rpad, float scale,
                                                      float scale2, float* __restrict__ out_f32,
-                                                     uint16_t* __restrict__ out_bf16, uint16_t* __restrict__ p_perm,
-                                                     int splits) {
+                                                     uint16_t* __restrict__ out_bf16, int splits) {
   constexpr int kRT = RT > 0 ? RT : 1;
   __shared__ f32x4 red[WAVES][kRT][64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, i = lane & 15, g = lane >> 4;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int split = blockIdx.y;
   const int64_t m = m0 + i;
-  const bool mvalid = m < M;
   const int64_t nchunks = (qn + 31) / 32;
   const int64_t per = (nchunks + splits - 1) / splits;
   const int64_t c_begin = split * per;
@@ -65,11 +63,6 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
       const int64_t q = (c0 + WAVES * u) * 32 + 8 * g;
       const bool qvalid = (c0 + WAVES * u < c_end) && q < qn;  // qn % 8 == 0: a valid run is whole
       const u32x4 av = qvalid ? a[u] : u32x4{0, 0, 0, 0};
-      if (p_perm != nullptr && mvalid && qvalid) {
-        uint32_t in[4] = {av[0], av[1], av[2], av[3]}, o[4];
-        to_decode_order(in, o);
-        st16(p_perm + m * qn + q, u32x4{o[0], o[1], o[2], o[3]});
-      }
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int j = 16 * t + i;
@@ -219,11 +212,10 @@ __global__ void rank_final_kernel(const float* __restrict__ part, int64_t cn, in
 
 template <int RT>
 void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r,
-                      int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, uint16_t* p_perm,
-                      int splits) {
+                      int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits) {
   constexpr int kWaves = (RT <= 2) ? 16 : (RT <= 4 ? 8 : 4);
   hipLaunchKernelGGL((skinny_kernel<RT, kWaves>), grid, dim3(kWaves * 64), 0, st, P, Q, m, qn, r, rpad, scale, scale2,
-                     out_f32, out_bf16, p_perm, splits);
+                     out_f32, out_bf16, splits);
 }
 
 }  // namespace
@@ -242,15 +234,14 @@ int skinny_splits(int64_t m, int64_t qn) {
 }
 
 hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad, float scale,
-                         float scale2, float* out_f32, uint16_t* out_bf16, uint16_t* p_perm, int splits,
-                         hipStream_t s) {
+                         float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((m + 15) / 16), static_cast<unsigned>(splits));
   switch (rpad / 16) {
-    case 0: launch_skinny_rt<0>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
-    case 2: launch_skinny_rt<2>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
-    case 4: launch_skinny_rt<4>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
-    case 6: launch_skinny_rt<6>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
-    case 8: launch_skinny_rt<8>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, p_perm, splits); break;
+    case 0: launch_skinny_rt<0>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
+    case 2: launch_skinny_rt<2>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
+    case 4: launch_skinny_rt<4>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
+    case 6: launch_skinny_rt<6>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
+    case 8: launch_skinny_rt<8>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

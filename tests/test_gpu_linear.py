@@ -26,6 +26,10 @@ FWD_BWD_CASES = [
     ("no_dq", 96, 384, 448, 16, 32.0, False),
     ("decode_no_dq_m3", 3, 384, 448, 16, 32.0, False),
     ("decode_m16_r0", 16, 256, 256, 0, 0.0, True),
+    ("decode_rank5_m2", 2, 96, 192, 5, 10.0, True),              # H inside the GEMV, ragged rank
+    ("decode_k8192_r4_m5", 5, 48, 8192, 4, 8.0, True),           # H inside the GEMV, two passes over k
+    ("decode_rank24_m8", 8, 128, 256, 24, 48.0, True),           # r > 16: H from the skinny kernel
+    ("decode_long_k_m2", 2, 64, 16384, 16, 32.0, True),          # r * k > 2^17: H from the skinny kernel
 ]
 
 
