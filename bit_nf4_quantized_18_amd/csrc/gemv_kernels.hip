@@ -226,6 +226,195 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   y[mo * N + no] = f32_to_bf16_rne(sum);
 }
 
+// Persistent form for k <= 4096 (one pass covers a row): a workgroup takes
+// row groups rg = blockIdx.x, + gridDim.x, ... (grid = number of CUs) and
+// software-pipelines them: the codes, scales and B rows of the next row group
+// are in flight while the current one is unpacked and multiplied. X is loaded
+// once (the same fragments serve every row group) and, with kFuseH, H is
+// computed once per workgroup, in its first row group, from A copied into LDS.
+template <bool kDQ, bool kFuseH>
+__global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
+                                                               const uint16_t* __restrict__ a,
+                                                               const float* __restrict__ hpart, int hsplits,
+                                                               const uint16_t* __restrict__ b, int r, float s,
+                                                               uint16_t* __restrict__ y, float* __restrict__ h_out,
+                                                               Levels L) {
+  constexpr int WAVES = 16, kLaneGroups = 64;
+  constexpr int kARow = kLaneGroups * 64 * 2;  // bytes of one rank row of A (k <= 4096)
+  constexpr int kRedBytes = (kFuseH ? 2 : 1) * WAVES * 64 * 16;
+  constexpr int kStage = kFuseH ? 16 * kARow : kRedBytes;
+  constexpr int kBPer = (16 * QLORA_MAX_RANK + WAVES * 64 - 1) / (WAVES * 64);  // B values per thread
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage > kRedBytes ? kStage : kRedBytes];
+  __shared__ float h_lds[16 * QLORA_MAX_RANK];
+  __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
+  f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(stage);
+  f32x4(*hred)[64] = reinterpret_cast<f32x4(*)[64]>(stage + WAVES * 64 * 16);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, g = lane >> 4;
+  const int G = wave * 4 + g;  // this lane group's block of every row group
+  const int K = static_cast<int>(w.k), N = static_cast<int>(w.n);
+  const int nbk = K / 64;  // <= 64
+  const int nrg = (N + 15) / 16;
+  const bool kval = G < nbk;
+  const int kb_c = kval ? G : nbk - 1;
+  const int wv_u = __builtin_amdgcn_readfirstlane(wave);
+  const int blast = N * r - 1;
+  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), static_cast<short>(0),
+                                                                        M * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), static_cast<short>(0),
+                                                                        kFuseH ? r * K * 2 : 0, 0x00020000);
+
+  struct Loads {
+    u32x4 c0, c1;
+    uint32_t scode;
+    float gsc;
+    uint16_t bv[kBPer];
+  };
+  // loads of row group rg < nrg
+  auto issue = [&](int rgc, Loads& T) {
+    const int n = rgc * 16 + i;
+    const int n_c = n < N ? n : N - 1;
+    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_c * 32));
+    T.c0 = __builtin_nontemporal_load(cp);
+    T.c1 = __builtin_nontemporal_load(cp + 1);
+    const int bi = n_c * nbk + kb_c;
+    if (kDQ) {
+      T.scode = w.scale_codes[bi];
+      T.gsc = w.group_scale[bi / kGroup];
+    } else {
+      T.scode = 0;
+      T.gsc = w.absmax[bi];
+    }
+    if (r > 0) {
+#pragma unroll
+      for (int u = 0; u < kBPer; ++u) {
+        const int e = rgc * 16 * r + tid + u * WAVES * 64;
+        T.bv[u] = b[e < blast ? e : blast];
+      }
+    }
+  };
+  constexpr int kTaskLoads = 2 + (kDQ ? 2 : 1) + kBPer;  // per issue() with r > 0
+
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 hacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  Loads T0, T1;
+  const int rg0 = blockIdx.x;
+  issue(rg0, T0);
+  u32x4 xa[8];  // X fragments of this lane's block: the same for every row group
+  {
+    const int xoff = (i * K + kb_c * 64) * 2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0);
+  }
+  if (kFuseH) {
+    // rank row `wave` of A, global -> LDS in 8 copies of 1 KB (whole cache
+    // lines); lane l of copy t fetches piece 64 t + (l ^ wave) into slot l,
+    // so the 16 ranks of one piece land in 16 different bank groups
+    __builtin_amdgcn_sched_barrier(0);
+    const int roff = wv_u * K * 2 + 16 * (lane ^ wave);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(stage + wv_u * kARow + t * 1024), 16,
+                                               roff + t * 1024, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  } else if (r > 0) {
+    // H = sum of the LoRA-down partials (fixed order)
+    const int mr = M * r;
+    for (int idx = tid; idx < mr; idx += WAVES * 64) {
+      float hv = 0.0f;
+      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
+      h_lds[idx] = hv;
+      if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
+    }
+  }
+
+  auto step = [&](int rg, Loads& Tc, Loads& Tn) {
+    const bool has_next = rg + static_cast<int>(gridDim.x) < nrg;  // uniform
+    if (has_next) issue(rg + gridDim.x, Tn);
+    // wave-uniform guard; lane groups past the row's blocks get a zero scale
+    if (wave * 4 < nbk) {
+      const int n = rg * 16 + i;
+      const bool ok = (n < N) && kval;
+      const float sc = kDQ ? u8_unit(Tc.scode) * Tc.gsc : Tc.gsc;
+      const BlockLut lut = make_block_lut(L.v, ok ? sc : 0.0f);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t cw = (j < 4) ? Tc.c0[j] : Tc.c1[j - 4];
+        uint32_t wv[4];
+        lut8_natural_order(lut, cw, wv);
+        acc = mfma_16x16x32(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
+      }
+    }
+    const bool first = rg == rg0;
+    if (kFuseH && first) {
+      // H product, once: wait for this wave's copies of A (everything issued
+      // after them is the next row group's loads), then for every wave's
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_next) {
+        wait_vmcnt<kTaskLoads>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      if (wave * 4 < nbk) {
+        const unsigned char* arow = stage + i * kARow;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = 8 * G + j;
+          const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
+          hacc = mfma_16x16x32(xa[j], kval ? af : u32x4{0, 0, 0, 0}, hacc);
+        }
+      }
+    }
+    // epilogue of row group rg
+    __syncthreads();  // LDS free: the previous epilogue's reads (and the A slice's) are done
+    red[wave][lane] = acc;
+    if (kFuseH && first) hred[wave][lane] = hacc;
+#pragma unroll
+    for (int u = 0; u < kBPer; ++u) {
+      const int idx = tid + u * WAVES * 64;
+      if (idx < 16 * r) b_lds[idx] = Tc.bv[u];
+    }
+    __syncthreads();
+    const int l2 = tid & 63, v = tid >> 6;
+    const int mo = 4 * (l2 >> 4) + v;
+    if (kFuseH && first) {
+      if (tid < 256) {
+        const int j = l2 & 15;
+        float hv = 0.0f;
+#pragma unroll
+        for (int wv = 0; wv < WAVES; ++wv) hv += hred[wv][l2][v];
+        if (mo < M && j < r) {
+          h_lds[mo * r + j] = hv;
+          if (h_out != nullptr && blockIdx.x == 0) h_out[mo * r + j] = hv;
+        }
+      }
+      __syncthreads();
+    }
+    const int no = rg * 16 + (l2 & 15);
+    if (tid < 256 && mo < M && no < N) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int wv = 0; wv < WAVES; ++wv) sum += red[wv][l2][v];
+      if (r > 0) {
+        float lo = 0.0f;
+        const uint16_t* brow = b_lds + (l2 & 15) * r;
+        const float* hrow = h_lds + mo * r;
+        for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], __uint_as_float(static_cast<uint32_t>(brow[j]) << 16), lo);
+        sum = fmaf(s, lo, sum);
+      }
+      y[mo * N + no] = f32_to_bf16_rne(sum);
+    }
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  for (int rg = rg0; rg < nrg; rg += 2 * gridDim.x) {
+    step(rg, T0, T1);
+    if (rg + gridDim.x < nrg) step(rg + gridDim.x, T1, T0);
+  }
+}
+
 }  // namespace
 
 bool gemv_fuses_h(int64_t k, int r) {
@@ -233,15 +422,35 @@ bool gemv_fuses_h(int64_t k, int r) {
   return r > 0 && r <= 16;
 }
 
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
 hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
                        int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
   constexpr int kWaves = 16;
-  const unsigned grid = static_cast<unsigned>((w.n + 15) / 16);
+  const int64_t nrg = (w.n + 15) / 16;
   const bool fuse = gemv_fuses_h(w.k, r);
+  if (w.k <= 4096) {
+    const unsigned grid = static_cast<unsigned>(nrg < device_cus() ? nrg : device_cus());
+    auto kern = w.dq ? (fuse ? gemv_persistent_kernel<true, true> : gemv_persistent_kernel<true, false>)
+                     : (fuse ? gemv_persistent_kernel<false, true> : gemv_persistent_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a, hpart, hsplits, b,
+                       r, s, y, h_out, nf4_table());
+    return hipGetLastError();
+  }
   auto kern = w.dq ? (fuse ? gemv_kernel<kWaves, true, true> : gemv_kernel<kWaves, true, false>)
                    : (fuse ? gemv_kernel<kWaves, false, true> : gemv_kernel<kWaves, false, false>);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a, hpart, hsplits, b, r,
-                     s, y, h_out, nf4_table());
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nrg)), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a,
+                     hpart, hsplits, b, r, s, y, h_out, nf4_table());
   return hipGetLastError();
 }
 
