@@ -27,7 +27,7 @@ struct Carve {
 };
 
 struct FwdLayout {
-  int64_t h32, hs, total;
+  int64_t h32, hs, part, total;
 };
 FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r) {
   (void)n;
@@ -40,24 +40,29 @@ FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r) {
   } else {
     L.h32 = c.take(m * r * 4);
     L.hs = c.take(m * rank_pad(r) * 2);
+    L.part = c.take(static_cast<int64_t>(qlora::skinny_prefill_splits(m, k)) * m * r * 4);
   }
   L.total = c.off;
   return L;
 }
 
 struct BwdLayout {
-  int64_t h32, dh32, dhs, at, bt, part, total;
+  int64_t h32, dh32, dhs, at, bt, part, spart, total;
 };
 BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r) {
   Carve c;
   BwdLayout L{};
   const int rp = rank_pad(r);
-  const int splits = qlora::rank_reduce_splits(m);
+  const int splits = qlora::rank_reduce_splits(m, n, k, r);
   L.h32 = c.take(m * r * 4);
   L.dh32 = c.take(m * r * 4);
   L.dhs = c.take(m * rp * 2);
   L.at = c.take(k * rp * 2);
   L.bt = c.take(n * rp * 2);
+  {
+    const int sk = qlora::skinny_prefill_splits(m, k), sn = qlora::skinny_prefill_splits(m, n);
+    L.spart = c.take(static_cast<int64_t>(sk > sn ? sk : sn) * m * r * 4);
+  }
   L.part = c.take(r == 0 ? 0 : static_cast<int64_t>(splits) * r * (k > n ? k : n) * 4);
   L.total = c.off;
   return L;
@@ -201,7 +206,9 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int6
   } else {
     float* h32 = (r == 0) ? nullptr : (h_out != nullptr ? h_out : reinterpret_cast<float*>(base + L.h32));
     uint16_t* hs = (r == 0) ? nullptr : reinterpret_cast<uint16_t*>(base + L.hs);
-    if (r > 0) QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, s, h32, hs, 1, stream));
+    if (r > 0)
+      QLORA_TRY(qlora::launch_skinny_prefill(x, a, m, k, r, rp, 1.0f, s, reinterpret_cast<float*>(base + L.part), h32,
+                                             hs, stream));
     QLORA_TRY(qlora::launch_gemm_fwd(pw, x, m, hs, b, r, rp, y, stream));
   }
   return QLORA_OK;
@@ -251,16 +258,17 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
     float* dh32 = reinterpret_cast<float*>(base + L.dh32);
     dhs = reinterpret_cast<uint16_t*>(base + L.dhs);
     float* part = reinterpret_cast<float*>(base + L.part);
+    float* spart = reinterpret_cast<float*>(base + L.spart);
     const float* h = h_saved;
     if (h == nullptr) {
       float* h32 = reinterpret_cast<float*>(base + L.h32);
-      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, h32, nullptr, 1, stream));
+      QLORA_TRY(qlora::launch_skinny_prefill(x, a, m, k, r, rp, 1.0f, 1.0f, spart, h32, nullptr, stream));
       h = h32;
     }
     QLORA_TRY(qlora::launch_lora_transpose(a, b, n, k, r, rp, at, bt, stream));
     // dH = s dY B  (contraction over n, with B^T as the r x n operand)
-    QLORA_TRY(qlora::launch_skinny(dy, bt, m, n, r, rp, s, 1.0f, dh32, dhs, 1, stream));
-    const int splits = qlora::rank_reduce_splits(m);
+    QLORA_TRY(qlora::launch_skinny_prefill(dy, bt, m, n, r, rp, s, 1.0f, spart, dh32, dhs, stream));
+    const int splits = qlora::rank_reduce_splits(m, n, k, r);
     // dA = dH^T X  (r x k)
     QLORA_TRY(qlora::launch_rank_reduce(dh32, x, m, k, r, 1.0f, splits, part, da, 0, stream));
     // dB = s dY^T H  (n x r)

@@ -50,6 +50,15 @@ hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_
                          float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s);
 int skinny_splits(int64_t m, int64_t qn);
 
+// Prefill (m > 16) form of the same projection, split over the contraction
+// for parallelism: raw partials in part (skinny_prefill_splits(m, qn) x m x r
+// float32), then out_f32 (m x r, may be null) = scale * sum and out_bf16
+// (m x rpad, may be null) = bf16(scale2 * scale * sum), zero-padded.
+int skinny_prefill_splits(int64_t m, int64_t qn);
+hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
+                                 float scale, float scale2, float* part, float* out_f32, uint16_t* out_bf16,
+                                 hipStream_t st);
+
 // Decode GEMV, m <= 16: y = x W16^T + s * h B^T in one launch when
 // gemv_fuses_h(k, r) (H = x A^T computed in the kernel from a); otherwise
 // hpart holds hsplits partial sums of H (hsplits x m x r float32, from
@@ -80,6 +89,6 @@ hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int6
 
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
-int rank_reduce_splits(int64_t m);
+int rank_reduce_splits(int64_t m, int64_t n, int64_t k, int r);
 
 }  // namespace qlora

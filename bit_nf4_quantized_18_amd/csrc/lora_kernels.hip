@@ -95,6 +95,24 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
   }
 }
 
+// Second half of the split prefill projection: out_f32 = scale * sum of the
+// split partials (summed in split order), out_bf16 = bf16(scale2 * that),
+// zero-padded from r to rpad columns.
+__global__ void skinny_final_kernel(const float* __restrict__ part, int64_t M, int r, int rpad, int splits,
+                                    float scale, float scale2, float* __restrict__ out_f32,
+                                    uint16_t* __restrict__ out_bf16) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= M * rpad) return;
+  const int64_t mo = idx / rpad;
+  const int j = static_cast<int>(idx % rpad);
+  float sum = 0.0f;
+  if (j < r)
+    for (int sp = 0; sp < splits; ++sp) sum += part[(static_cast<int64_t>(sp) * M + mo) * r + j];
+  const float val = scale * sum;
+  if (out_f32 != nullptr && j < r) out_f32[mo * r + j] = val;
+  if (out_bf16 != nullptr) out_bf16[idx] = f32_to_bf16_rne(scale2 * val);
+}
+
 // at (k x rpad) = A^T zero-padded; bt (rpad x n) = B^T zero-padded.
 __global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int64_t n,
                                       int64_t k, int r, int rpad, uint16_t* __restrict__ at,
@@ -220,11 +238,40 @@ void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16
 
 }  // namespace
 
-int rank_reduce_splits(int64_t m) {
-  int64_t s = (m + 511) / 512;  // ~32 rows per wave of a 16-wave workgroup
+int rank_reduce_splits(int64_t m, int64_t n, int64_t k, int r) {
+  // enough workgroups for two per CU on the narrower of the two reductions
+  // (dA over k columns, dB over n columns), with at least 64 rows per split
+  const int64_t cn = n < k ? n : k;
+  const int64_t wg = ((cn + 127) / 128) * ((r + 15) / 16);
+  if (wg <= 0) return 1;  // r = 0: no reduction
+  int64_t s = (512 + wg - 1) / wg;
+  const int64_t by_rows = m / 64;
+  if (s > by_rows) s = by_rows;
+  if (s > 32) s = 32;
   if (s < 1) s = 1;
-  if (s > 16) s = 16;
   return static_cast<int>(s);
+}
+
+int skinny_prefill_splits(int64_t m, int64_t qn) {
+  // about two workgroups per CU, at least 256 contraction elements per split
+  const int64_t tiles = (m + 15) / 16;
+  int64_t s = (512 + tiles - 1) / tiles;
+  if (s > qn / 256) s = qn / 256;
+  if (s > 8) s = 8;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
+                                 float scale, float scale2, float* part, float* out_f32, uint16_t* out_bf16,
+                                 hipStream_t st) {
+  const int splits = skinny_prefill_splits(m, qn);
+  hipError_t e = launch_skinny(P, Q, m, qn, r, rpad, 1.0f, 1.0f, part, nullptr, splits, st);
+  if (e != hipSuccess) return e;
+  const int64_t total = m * rpad;
+  hipLaunchKernelGGL(skinny_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, part, m,
+                     r, rpad, splits, scale, scale2, out_f32, out_bf16);
+  return hipGetLastError();
 }
 
 int skinny_splits(int64_t m, int64_t qn) {
