@@ -91,8 +91,22 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   const uint32_t xcd = id % kXcds, local = id / kXcds;
   const uint32_t start = xcd * (T / kXcds) + (xcd < T % kXcds ? xcd : T % kXcds);
   const uint32_t lin = start + local;  // bijection of [0, T)
-  const int64_t m0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(lin / tiles_p)) * kBM;
-  const int64_t p0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(lin % tiles_p)) * kBP;
+  // Pairs of token-row tiles are interleaved along the output tiles, so a
+  // run of consecutive tiles (one XCD's) covers 2 token rows x half as many
+  // weight-row tiles: each weight tile and each token tile it reads is
+  // shared by 2 or more workgroups of the XCD.
+  const uint32_t full = (tiles_m / 2) * 2 * tiles_p;
+  uint32_t mt, pt;
+  if (lin < full) {
+    const uint32_t rem = lin % (2 * tiles_p);
+    mt = 2 * (lin / (2 * tiles_p)) + (rem & 1);
+    pt = rem >> 1;
+  } else {
+    mt = (tiles_m / 2) * 2 + (lin - full) / tiles_p;
+    pt = (lin - full) % tiles_p;
+  }
+  const int64_t m0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(mt)) * kBM;
+  const int64_t p0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(pt)) * kBP;
 
   const int64_t K = w.k;
   const int64_t nbk = K / 64;
@@ -280,19 +294,29 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     mma(xa, xb);
   }
 
-  // lane holds out[m = .. + i][p = .. + 4g .. 4g+3]
+  // Output through LDS: the ring is free after the last step's barrier (no
+  // copy is in flight any more), so each consumer wave stages its 128 x 64
+  // bf16 sub-tile there (rows padded to 72 elements: the 16 rows of one
+  // 8-byte store land in distinct banks) and writes it back as whole
+  // 128-byte row runs, 16 bytes per lane. Lane holds out[m = .. + i][p = .. + 4g .. 4g+3].
+  constexpr int kEpRow = 72;
+  uint16_t* ep = As + wave * (128 * kEpRow);
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
-    const int64_t m = m0 + wm * 128 + 16 * mt + i;
-    if (m >= M) continue;
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
-      const int64_t p = p0 + wp * 64 + 16 * nt + 4 * g;
-      if (p >= P) continue;  // P % 16 == 0: a run of 4 is whole
       const f32x4 c = acc[nt][mt];
-      const u32x2 v = {cvt_bf16x2(c[0], c[1]), cvt_bf16x2(c[2], c[3])};
-      *reinterpret_cast<u32x2*>(out + m * P + p) = v;
+      *reinterpret_cast<u32x2*>(ep + (16 * mt + i) * kEpRow + 16 * nt + 4 * g) =
+          u32x2{cvt_bf16x2(c[0], c[1]), cvt_bf16x2(c[2], c[3])};
     }
+  const int rr = lane >> 3, cc = lane & 7;
+  const int64_t pcol = p0 + wp * 64 + 8 * cc;
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int row = 8 * it + rr;
+    const u32x4 v = ld16(ep + row * kEpRow + 8 * cc);
+    const int64_t m = m0 + wm * 128 + row;
+    if (m < M && pcol < P) *reinterpret_cast<u32x4*>(out + m * P + pcol) = v;  // P % 16 == 0: a run of 8 is whole
   }
 }
 
