@@ -63,7 +63,13 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r) {
     const int sk = qlora::skinny_prefill_splits(m, k), sn = qlora::skinny_prefill_splits(m, n);
     L.spart = c.take(static_cast<int64_t>(sk > sn ? sk : sn) * m * r * 4);
   }
-  L.part = c.take(r == 0 ? 0 : static_cast<int64_t>(splits) * r * (k > n ? k : n) * 4);
+  if (r == 0) {
+    L.part = c.take(0);
+  } else if (qlora::rank_grads_fused(r)) {
+    L.part = c.take(static_cast<int64_t>(qlora::rank_grad_splits(m, n, k, r)) * r * (k + n) * 4);
+  } else {
+    L.part = c.take(static_cast<int64_t>(splits) * r * (k > n ? k : n) * 4);
+  }
   L.total = c.off;
   return L;
 }
@@ -268,11 +274,17 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
     QLORA_TRY(qlora::launch_lora_transpose(a, b, n, k, r, rp, at, bt, stream));
     // dH = s dY B  (contraction over n, with B^T as the r x n operand)
     QLORA_TRY(qlora::launch_skinny_prefill(dy, bt, m, n, r, rp, s, 1.0f, spart, dh32, dhs, stream));
-    const int splits = qlora::rank_reduce_splits(m, n, k, r);
-    // dA = dH^T X  (r x k)
-    QLORA_TRY(qlora::launch_rank_reduce(dh32, x, m, k, r, 1.0f, splits, part, da, 0, stream));
-    // dB = s dY^T H  (n x r)
-    QLORA_TRY(qlora::launch_rank_reduce(h, dy, m, n, r, s, splits, part, db, 1, stream));
+    if (qlora::rank_grads_fused(r)) {
+      // dA = dH^T X (r x k) and dB = s dY^T H (n x r) in one pass each
+      QLORA_TRY(qlora::launch_rank_grads(dh32, x, k, h, dy, n, m, r, s, qlora::rank_grad_splits(m, n, k, r), part,
+                                         da, db, stream));
+    } else {
+      const int splits = qlora::rank_reduce_splits(m, n, k, r);
+      // dA = dH^T X  (r x k)
+      QLORA_TRY(qlora::launch_rank_reduce(dh32, x, m, k, r, 1.0f, splits, part, da, 0, stream));
+      // dB = s dY^T H  (n x r)
+      QLORA_TRY(qlora::launch_rank_reduce(h, dy, m, n, r, s, splits, part, db, 1, stream));
+    }
   }
   if (dx != nullptr) QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream));
   return QLORA_OK;

@@ -37,6 +37,7 @@
 // output columns of one token row and stores 8 contiguous bytes. Tiles are
 // ordered so that the workgroups on one XCD (ids congruent mod 8) share token
 // rows in that XCD's L2. The rank-r LoRA term is one more pass of MFMAs.
+#include "bufmem.h"
 #include "internal.h"
 #include "mfma.h"
 #include "nf4_lut.h"
@@ -51,24 +52,8 @@ constexpr int kXcds = 8;
 constexpr int kAStage = kBM * kBQ;  // bf16 elements
 constexpr int kBStage = kBP * kBQ;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t lim = bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(lim),
-                                           0x00020000);
-}
-
 // element offset of (row, 16-byte chunk) in a swizzled 64-wide LDS tile
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBQ + ((chunk ^ ((row >> 1) & 7)) << 3); }
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <bool kTransW, bool kDQ>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,

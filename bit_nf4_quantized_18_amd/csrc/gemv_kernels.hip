@@ -31,6 +31,7 @@
 //     sums from the skinny kernel;
 //   * partial sums of the waves are reduced in a fixed order in LDS, so
 //     results do not depend on scheduling.
+#include "bufmem.h"
 #include "internal.h"
 #include "mfma.h"
 #include "nf4_lut.h"
@@ -39,16 +40,6 @@ namespace qlora {
 namespace {
 
 constexpr int kGroup = 256;
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
-// 3:0 and 15:14; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int WAVES, bool kDQ, bool kFuseH>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ x, int M,

@@ -91,4 +91,14 @@ hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
 int rank_reduce_splits(int64_t m, int64_t n, int64_t k, int r);
 
+// Both adapter gradients in two launches when rank_grads_fused(r)
+// (r % 16 == 0): da (r x k) = dh^T x and db (n x r) = scale * dy^T h, with
+// dh, h float32 m x r and x, dy bf16. part holds splits x r x (k + n)
+// float32 partial sums (splits = rank_grad_splits), reduced in a fixed order.
+bool rank_grads_fused(int r);
+int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r);
+hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, const float* h, const uint16_t* dy,
+                             int64_t n, int64_t m, int r, float scale, int splits, float* part, float* da, float* db,
+                             hipStream_t st);
+
 }  // namespace qlora

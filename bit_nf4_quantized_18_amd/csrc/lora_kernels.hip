@@ -7,6 +7,7 @@
 // dH = s dY B, dA = dH^T X and dB = s dY^T H.
 //
 // These are thin (r <= 128 columns) and are bounded by one pass over X or dY.
+#include "bufmem.h"
 #include "internal.h"
 #include "mfma.h"
 #include "nf4_lut.h"
@@ -228,6 +229,176 @@ __global__ void rank_final_kernel(const float* __restrict__ part, int64_t cn, in
   out[idx] = scale * sum;
 }
 
+// Both adapter gradients in one launch, for r % 16 == 0:
+//   problem 0: part0[s][j][c] = sum over rows m of split s of U0[m][j] V0[m][c]
+//              (dA: U0 = dH, V0 = X, c < k)
+//   problem 1: the same with U1 = H, V1 = dY (dB before its scale, c < n).
+// Workgroup: one 256-column block, one 16-rank tile and one row split. The
+// split's rows stream through LDS in chunks of 32 rows: a copy wave moves
+// the V tile (32 x 256 bf16, whole 512-byte row runs) and the U tile
+// (32 x 16 float32) with global->LDS buffer loads, three chunks ahead in a
+// ring of four, so each CU keeps tens of KB of reads in flight without
+// spending registers on them. Eight compute waves only read LDS and run the
+// float32 matrix-core product v_mfma_f32_16x16x4_f32 (D[16 ranks][16 cols]
+// += U^T[16 ranks][4 rows] V[4 rows][16 cols], all in float32): wave w owns
+// the 64 columns 64 (w % 4) .. +63 and every other group of 4 rows
+// (w / 4); lane (g, i) reads row g of a group, U[row][j0 + i] and the 4
+// bf16 at columns 4i .. 4i+3 of its 64, which feed 4 MFMAs (MFMA t covers
+// columns 4i + t). The two waves of a column range are summed in a fixed
+// order through LDS at the end. Rows past the split or past M and columns
+// past cn read as zeros (buffer ranges); columns past cn are never stored.
+struct RankGradProblem {
+  const float* U;     // m x r float32
+  const uint16_t* V;  // m x cn bf16
+  int64_t cn;
+  float* part;        // splits x r x cn float32
+  int blocks;         // column blocks of 256
+};
+
+constexpr int kRgCols = 256, kRgRows = 32, kRgStages = 4;
+constexpr int kRgV = kRgRows * kRgCols;  // bf16 elements per stage
+constexpr int kRgU = kRgRows * 16;       // float32 per stage
+constexpr int kRgWaves = 8;              // compute waves; one more wave copies
+
+__device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGradProblem p0, RankGradProblem p1,
+                                                                        int64_t M, int r, int splits, int64_t per) {
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kRgStages * kRgV];
+  __shared__ __attribute__((aligned(16))) float Us[kRgStages * kRgU];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rt = r / 16;
+  // workgroup -> (problem, column block, rank tile, split)
+  int id = blockIdx.x;
+  const int n0 = p0.blocks * rt * splits;
+  const bool second = id >= n0;
+  if (second) id -= n0;
+  const RankGradProblem& pb = second ? p1 : p0;
+  const int s = id % splits;
+  const int j0 = ((id / splits) % rt) * 16;
+  const int cb = id / (splits * rt);
+  const int64_t c0 = static_cast<int64_t>(cb) * kRgCols;
+  const int64_t cn = pb.cn;
+  const int64_t mb = s * per;
+  const int64_t me = (mb + per < M) ? mb + per : M;
+  const int nch = me > mb ? static_cast<int>((me - mb + kRgRows - 1) / kRgRows) : 0;
+
+  if (wave == kRgWaves) {
+    // ======================= copy wave =======================
+    // V instruction u: rows 2u, 2u+1 (lane / 32), 16 bytes at column 8 (lane % 32);
+    // U instruction q: rows 16q + lane / 4, floats j0 + 4 (lane % 4) .. +3.
+    const int v_voff = static_cast<int>(((lane >> 5) * cn + 8 * (lane & 31)) * 2);
+    const int u_voff = static_cast<int>(((lane >> 2) * r + j0 + 4 * (lane & 3)) * 4);
+    auto copy_chunk = [&](int c) {
+      const int64_t m0 = mb + static_cast<int64_t>(c) * kRgRows;
+      const int64_t rows = (m0 < me) ? (me - m0 < kRgRows ? me - m0 : kRgRows) : 0;
+      const int64_t mr = (m0 < M) ? m0 : M;
+      // rows [m0, m0 + rows) from column c0; the last row ends at cn
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(pb.V + mr * cn + c0, rows > 0 ? (rows * cn - c0) * 2 : 0);
+      const __amdgpu_buffer_rsrc_t ur = make_rsrc(pb.U + mr * r, rows > 0 ? (M - mr) * r * 4 : 0);
+      uint16_t* vs = Vs + (c % kRgStages) * kRgV;
+      float* us = Us + (c % kRgStages) * kRgU;
+      // (whole offsets in the vector operand: the scalar offset is not range checked)
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vs + u * (2 * kRgCols)), 16,
+                                                 v_voff + static_cast<int>(u * 4 * cn), 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (lds_void*)(us + q * 256), 16, u_voff + q * 64 * r, 0, 0, 0);
+    };
+    constexpr int kCopies = 18;  // per chunk
+    copy_chunk(0);
+    copy_chunk(1);
+    copy_chunk(2);
+    for (int c = 0; c < nch; ++c) {
+      copy_chunk(c + 3);
+      // loads complete in issue order: with the copies of chunks c+1 .. c+3
+      // outstanding, chunk c has landed
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<3 * kCopies>();
+      // Bare barriers: a fenced one would wait for the copies still in
+      // flight. This wave writes LDS only through the copies counted above.
+      __builtin_amdgcn_s_barrier();  // chunk c is in LDS
+      __builtin_amdgcn_s_barrier();  // its slot has been read
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // no copy may still be writing LDS when the wave ends
+    wait_vmcnt<0>();
+    return;
+  }
+
+  // ======================= compute waves =======================
+  const int i = lane & 15, g = lane >> 4;
+  const int quad = wave & 3, half = wave >> 2;
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int c = 0; c < nch; ++c) {
+    __syncthreads();  // chunk c is in LDS
+    const uint16_t* vs = Vs + (c % kRgStages) * kRgV + 64 * quad + 4 * i;
+    const float* us = Us + (c % kRgStages) * kRgU + i;
+#pragma unroll
+    for (int e = 0; e < kRgRows / 8; ++e) {
+      const int row = 4 * (2 * e + half) + g;
+      const float a = us[row * 16];
+      const u32x2 xv = *reinterpret_cast<const u32x2*>(vs + row * kRgCols);
+      acc[0] = mfma_16x16x4_f32(a, __uint_as_float(xv[0] << 16), acc[0]);
+      acc[1] = mfma_16x16x4_f32(a, __uint_as_float(xv[0] & 0xFFFF0000u), acc[1]);
+      acc[2] = mfma_16x16x4_f32(a, __uint_as_float(xv[1] << 16), acc[2]);
+      acc[3] = mfma_16x16x4_f32(a, __uint_as_float(xv[1] & 0xFFFF0000u), acc[3]);
+    }
+    __syncthreads();  // the slot may be refilled
+  }
+  // the copy wave has ended (or waits on its last copies): the ring is free
+  __syncthreads();
+
+  // acc[t][v] = sum for rank j0 + 4g + v, column c0 + 64 quad + 4i + t.
+  // Waves 4..7 hand their sums to waves 0..3 through LDS (fixed order).
+  f32x4* red = reinterpret_cast<f32x4*>(Vs);
+  if (half == 1) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) red[(quad * 4 + t) * 64 + lane] = acc[t];
+  }
+  __syncthreads();
+  if (half == 1) return;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] += red[(quad * 4 + t) * 64 + lane];
+  const int64_t col = c0 + 64 * quad + 4 * i;
+  if (col < cn) {  // cn % 16 == 0: a run of 4 is whole
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      *reinterpret_cast<f32x4*>(pb.part + (static_cast<int64_t>(s) * r + j0 + 4 * g + v) * cn + col) =
+          f32x4{acc[0][v], acc[1][v], acc[2][v], acc[3][v]};
+  }
+}
+
+// da[j][c] = sum_s part0[s][j][c] (r x k); db[c][j] = scale * sum_s part1[s][j][c]
+// (n x r), each summed in split order.
+__global__ void rank_grad_final_kernel(const float* __restrict__ part0, const float* __restrict__ part1, int64_t k,
+                                       int64_t n, int r, int splits, float scale, float* __restrict__ da,
+                                       float* __restrict__ db) {
+  int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t na = static_cast<int64_t>(r) * k;
+  if (idx < na) {
+    float sum = 0.0f;
+    for (int s = 0; s < splits; ++s) sum += part0[static_cast<int64_t>(s) * na + idx];
+    da[idx] = sum;
+    return;
+  }
+  idx -= na;
+  if (idx >= static_cast<int64_t>(r) * n) return;
+  const int64_t c = idx / r;
+  const int j = static_cast<int>(idx % r);
+  float sum = 0.0f;
+  for (int s = 0; s < splits; ++s) sum += part1[(static_cast<int64_t>(s) * r + j) * n + c];
+  db[idx] = scale * sum;
+}
+
 template <int RT>
 void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r,
                       int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits) {
@@ -314,6 +485,35 @@ hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int6
   const int64_t total = static_cast<int64_t>(r) * cn;
   hipLaunchKernelGGL(rank_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, part, cn,
                      r, splits, scale, out, c_major);
+  return hipGetLastError();
+}
+
+bool rank_grads_fused(int r) { return r > 0 && r % 16 == 0; }
+
+int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r) {
+  // about one workgroup per CU over both problems, at least one 32-row chunk per split
+  if (!rank_grads_fused(r)) return rank_reduce_splits(m, n, k, r);
+  const int64_t per_split = ((k + kRgCols - 1) / kRgCols + (n + kRgCols - 1) / kRgCols) * (r / 16);
+  int64_t s = 256 / per_split;  // at most one workgroup per CU: no second round
+  const int64_t by_rows = (m + kRgRows - 1) / kRgRows;
+  if (s > by_rows) s = by_rows;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, const float* h, const uint16_t* dy,
+                             int64_t n, int64_t m, int r, float scale, int splits, float* part, float* da, float* db,
+                             hipStream_t st) {
+  // rows per split: a multiple of the 32-row chunk
+  const int64_t per = ((m + splits - 1) / splits + kRgRows - 1) / kRgRows * kRgRows;
+  RankGradProblem p0{dh, x, k, part, static_cast<int>((k + kRgCols - 1) / kRgCols)};
+  RankGradProblem p1{h, dy, n, part + static_cast<int64_t>(splits) * r * k, static_cast<int>((n + kRgCols - 1) / kRgCols)};
+  const int64_t wgs = static_cast<int64_t>(p0.blocks + p1.blocks) * (r / 16) * splits;
+  hipLaunchKernelGGL(rank_grad_kernel, dim3(static_cast<unsigned>(wgs)), dim3((kRgWaves + 1) * 64), 0, st, p0, p1, m, r, splits, per);
+  const int64_t total = static_cast<int64_t>(r) * (k + n);
+  hipLaunchKernelGGL(rank_grad_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
+                     p0.part, p1.part, k, n, r, splits, scale, da, db);
   return hipGetLastError();
 }
 
