@@ -40,7 +40,7 @@ FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r) {
   } else {
     L.h32 = c.take(m * r * 4);
     L.hs = c.take(m * rank_pad(r) * 2);
-    L.part = c.take(static_cast<int64_t>(qlora::skinny_prefill_splits(m, k)) * m * r * 4);
+    L.part = c.take(static_cast<int64_t>(qlora::skinny_prefill_splits(m, k, r)) * m * r * 4);
   }
   L.total = c.off;
   return L;
@@ -60,7 +60,7 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r) {
   L.at = c.take(k * rp * 2);
   L.bt = c.take(n * rp * 2);
   {
-    const int sk = qlora::skinny_prefill_splits(m, k), sn = qlora::skinny_prefill_splits(m, n);
+    const int sk = qlora::skinny_prefill_splits(m, k, r), sn = qlora::skinny_prefill_splits(m, n, r);
     L.spart = c.take(static_cast<int64_t>(sk > sn ? sk : sn) * m * r * 4);
   }
   if (r == 0) {

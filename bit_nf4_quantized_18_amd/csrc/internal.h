@@ -51,10 +51,11 @@ hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_
 int skinny_splits(int64_t m, int64_t qn);
 
 // Prefill (m > 16) form of the same projection, split over the contraction
-// for parallelism: raw partials in part (skinny_prefill_splits(m, qn) x m x r
+// for parallelism: raw partials in part (skinny_prefill_splits(m, qn, r) x m x r
 // float32), then out_f32 (m x r, may be null) = scale * sum and out_bf16
-// (m x rpad, may be null) = bf16(scale2 * scale * sum), zero-padded.
-int skinny_prefill_splits(int64_t m, int64_t qn);
+// (m x rpad, may be null) = bf16(scale2 * scale * sum), zero-padded. For
+// r <= 16 the partials come from a streaming kernel (LDS ring, MFMA).
+int skinny_prefill_splits(int64_t m, int64_t qn, int r);
 hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
                                  float scale, float scale2, float* part, float* out_f32, uint16_t* out_bf16,
                                  hipStream_t st);

@@ -96,6 +96,106 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
   }
 }
 
+// Prefill projection for r <= 16 (one rank tile): part[s][m][j] = sum over
+// the columns q of split s of P[m][q] Q[j][q], P bf16 M x qn, Q bf16 r x qn.
+// Workgroup: 64 rows of P and one split of the columns. A copy wave streams
+// chunks of 128 columns -- the P tile (64 x 128) and the Q tile (16 x 128),
+// whole 256-byte row runs -- into a ring of four LDS stages with
+// global->LDS buffer loads, three chunks ahead. Four compute waves (16 rows
+// each) read 16-byte fragments and run 16x16x32 bf16 MFMAs (Q as the first
+// operand: a lane ends with 4 ranks of one row). In LDS the 16-byte chunk c
+// of row t is stored at chunk c ^ (t % 16), so the 16 lanes that read one
+// chunk of 16 rows hit distinct banks. Rows past M and Q columns past qn
+// read as zeros; a column of P past qn meets a zero of Q.
+constexpr int kPjRows = 64, kPjCols = 128, kPjStages = 4;
+constexpr int kPjP = kPjRows * kPjCols, kPjQ = 16 * kPjCols;  // bf16 elements per stage
+
+__global__ __launch_bounds__(320) void proj_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
+                                                   int64_t M, int64_t qn, int r, int splits, int64_t per,
+                                                   float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ps[kPjStages * kPjP];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kPjStages * kPjQ];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = blockIdx.y;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kPjRows;
+  const int64_t qb = s * per;
+  const int64_t qe = (qb + per < qn) ? qb + per : qn;
+  const int nch = qe > qb ? static_cast<int>((qe - qb + kPjCols - 1) / kPjCols) : 0;
+
+  if (wave == 4) {
+    // ======================= copy wave =======================
+    // instruction u: rows 4u + lane / 16 of the tile, the logical chunk that
+    // the swizzle stores at position lane % 16
+    const int64_t rows = (M - m0 < kPjRows) ? M - m0 : kPjRows;
+    const int trow = lane >> 4;
+    auto copy_chunk = [&](int c) {
+      const int64_t qc = qb + static_cast<int64_t>(c) * kPjCols;
+      const bool live = qc < qe;
+      const int64_t qcl = live ? qc : 0;
+      const __amdgpu_buffer_rsrc_t pr = make_rsrc(P + m0 * qn + qcl, live ? (rows * qn - qcl) * 2 : 0);
+      const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + qcl, live ? (r * qn - qcl) * 2 : 0);
+      uint16_t* ps = Ps + (c % kPjStages) * kPjP;
+      uint16_t* qs = Qs + (c % kPjStages) * kPjQ;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int row = 4 * u + trow;
+        const int chunk = (lane & 15) ^ (row & 15);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_void*)(ps + u * 512), 16,
+                                                 static_cast<int>((row * qn + 8 * chunk) * 2), 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int row = 4 * u + trow;
+        const int chunk = (lane & 15) ^ (row & 15);
+        // columns past the split's end (or qn) must read zero: offset out of range
+        const bool in = qc + 8 * chunk < qe;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(qs + u * 512), 16,
+                                                 in ? static_cast<int>((row * qn + 8 * chunk) * 2) : 0x7FFFFFF0, 0,
+                                                 0, 0);
+      }
+    };
+    constexpr int kCopies = 20;  // per chunk
+    copy_chunk(0);
+    copy_chunk(1);
+    copy_chunk(2);
+    for (int c = 0; c < nch; ++c) {
+      copy_chunk(c + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<3 * kCopies>();  // chunk c has landed (loads complete in issue order)
+      // bare barriers: a fenced one would wait for the copies still in flight
+      __builtin_amdgcn_s_barrier();  // chunk c is in LDS
+      __builtin_amdgcn_s_barrier();  // its slot has been read
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vmcnt<0>();  // no copy may still be writing LDS when the wave ends
+    return;
+  }
+
+  // ======================= compute waves =======================
+  const int i = lane & 15, g = lane >> 4;
+  const int prow = (16 * wave + i) * kPjCols, qrow = i * kPjCols;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nch; ++c) {
+    __syncthreads();  // chunk c is in LDS
+    const uint16_t* ps = Ps + (c % kPjStages) * kPjP + prow;
+    const uint16_t* qs = Qs + (c % kPjStages) * kPjQ + qrow;
+#pragma unroll
+    for (int kk = 0; kk < kPjCols / 32; ++kk) {
+      const int off = ((4 * kk + g) ^ i) * 8;  // rows 16 w + i and i: the swizzle key is i
+      acc = mfma_16x16x32(ld16(qs + off), ld16(ps + off), acc);
+    }
+    __syncthreads();  // the slot may be refilled
+  }
+  // acc[v] = sum for rank 4g + v of row m0 + 16 wave + i
+  const int64_t m = m0 + 16 * wave + i;
+  if (m < M) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (4 * g + v < r) part[(static_cast<int64_t>(s) * M + m) * r + 4 * g + v] = acc[v];
+  }
+}
+
 // Second half of the split prefill projection: out_f32 = scale * sum of the
 // split partials (summed in split order), out_bf16 = bf16(scale2 * that),
 // zero-padded from r to rpad columns.
@@ -423,7 +523,21 @@ int rank_reduce_splits(int64_t m, int64_t n, int64_t k, int r) {
   return static_cast<int>(s);
 }
 
-int skinny_prefill_splits(int64_t m, int64_t qn) {
+bool proj_fast(int r) { return r > 0 && r <= 16; }
+
+int proj_splits(int64_t m, int64_t qn) {
+  // about one workgroup per CU, at least one 128-column chunk per split
+  const int64_t blocks = (m + kPjRows - 1) / kPjRows;
+  int64_t s = 256 / blocks;
+  const int64_t by_cols = (qn + kPjCols - 1) / kPjCols;
+  if (s > by_cols) s = by_cols;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+int skinny_prefill_splits(int64_t m, int64_t qn, int r) {
+  if (proj_fast(r)) return proj_splits(m, qn);
   // about two workgroups per CU, at least 256 contraction elements per split
   const int64_t tiles = (m + 15) / 16;
   int64_t s = (512 + tiles - 1) / tiles;
@@ -436,9 +550,16 @@ int skinny_prefill_splits(int64_t m, int64_t qn) {
 hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
                                  float scale, float scale2, float* part, float* out_f32, uint16_t* out_bf16,
                                  hipStream_t st) {
-  const int splits = skinny_prefill_splits(m, qn);
-  hipError_t e = launch_skinny(P, Q, m, qn, r, rpad, 1.0f, 1.0f, part, nullptr, splits, st);
-  if (e != hipSuccess) return e;
+  const int splits = skinny_prefill_splits(m, qn, r);
+  if (proj_fast(r)) {
+    // columns per split: a multiple of the 128-column chunk
+    const int64_t per = ((qn + splits - 1) / splits + kPjCols - 1) / kPjCols * kPjCols;
+    hipLaunchKernelGGL(proj_kernel, dim3(static_cast<unsigned>((m + kPjRows - 1) / kPjRows), splits), dim3(320), 0,
+                       st, P, Q, m, qn, r, splits, per, part);
+  } else {
+    hipError_t e = launch_skinny(P, Q, m, qn, r, rpad, 1.0f, 1.0f, part, nullptr, splits, st);
+    if (e != hipSuccess) return e;
+  }
   const int64_t total = m * rpad;
   hipLaunchKernelGGL(skinny_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, part, m,
                      r, rpad, splits, scale, scale2, out_f32, out_bf16);
