@@ -32,7 +32,11 @@
 // per-thread offsets are computed once, a step adds one constant.
 // LDS rows are 128 B without padding; the 16-byte chunk c of row r is stored
 // at chunk c ^ ((r >> 1) & 7), so 16 lanes reading one chunk of 16
-// consecutive rows hit 64 distinct banks. The MFMA computes the transposed
+// consecutive rows hit 64 distinct banks. In the backward the weight tile
+// keeps the weight's own orientation (64 contraction rows x 128 output
+// columns, so the producers write whole 16-byte runs as in the forward), and
+// the consumers read their fragments with the transposing LDS load
+// ds_read_b64_tr_b16 (two per fragment). The MFMA computes the transposed
 // product (weights as the first operand): each lane ends with 4 consecutive
 // output columns of one token row and stores 8 contiguous bytes. Tiles are
 // ordered so that the workgroups on one XCD (ids congruent mod 8) share token
@@ -54,6 +58,20 @@ constexpr int kBStage = kBP * kBQ;
 
 // element offset of (row, 16-byte chunk) in a swizzled 64-wide LDS tile
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBQ + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+// Backward weight tile: 64 contraction rows n x 128 output columns, the
+// weight's own orientation. Chunk c of row n is stored at c ^ swz_t_key(n):
+// the transposed fragment reads below then hit every bank once per 32 lanes.
+__device__ __forceinline__ int swz_t_key(int n) { return 2 * (n & 3) + 8 * ((n >> 3) & 1); }
+__device__ __forceinline__ int swz_t(int n, int chunk) { return n * kBP + ((chunk ^ swz_t_key(n)) << 3); }
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 4p + e receives element
+// e of the 8-byte rows addressed by lanes p, p + 4, p + 8 and p + 12.
+__device__ __forceinline__ u32x2 ld_tr4(const uint16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <bool kTransW, bool kDQ>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,
@@ -163,13 +181,8 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
         uint32_t wv[4];
         lut8_natural_order(lut, c[j], wv);
         if (kTransW) {
-          // element (n = w_r, k = w_c + 8 j + e) goes to row k, column n
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int krow = w_c + 8 * j + e;
-            const uint32_t word = wv[e >> 1];
-            bs[swz(krow, w_r >> 3) + (w_r & 7)] = static_cast<uint16_t>((e & 1) ? (word >> 16) : word);
-          }
+          // row n = w_r of the tile keeps the weight's orientation
+          st16(bs + swz_t(w_r, (w_c >> 3) + j), u32x4{wv[0], wv[1], wv[2], wv[3]});
         } else {
           st16(bs + swz(w_r, (w_c >> 3) + j), u32x4{wv[0], wv[1], wv[2], wv[3]});
         }
@@ -227,6 +240,18 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   // element offsets (within a stage row) of this lane's fragment chunk, per half-step
   const int col0 = ((0 + g) ^ sw) << 3, col1 = ((4 + g) ^ sw) << 3;
   const int arow = (wm * 128 + i) * kBQ, brow = (wp * 64 + i) * kBQ;
+  // backward: the first operand of the MFMA is column k0 + i of the [n][k]
+  // tile, contraction slots n = 32 half + 8g + e'. Lane 16g + 4t + p supplies
+  // the address of row 32 half + 8g + t (then + 4) at columns k0 + 4p .. +3
+  // (k0 = 64 wp + 16 nt): with swz_t_key(n) = 2t + 8 (g & 1), the stored chunk
+  // is (p / 2) | ((nt ^ t) << 1) | ((wp ^ (g & 1)) << 3).
+  int toff[4] = {0, 0, 0, 0};
+  if (kTransW) {
+    const int tp = i & 3, tt = i >> 2;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      toff[nt] = (8 * g + tt) * kBP + 8 * ((tp >> 1) | ((nt ^ tt) << 1) | ((wp ^ (g & 1)) << 3)) + 4 * (tp & 1);
+  }
 
   f32x4 acc[4][8];  // [weight tile nt][token tile mt]: acc = W x^T tile
 #pragma unroll
@@ -237,13 +262,23 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   // two register sets of fragments: while the MFMAs of one half-step run,
   // the other set is filled from LDS
   u32x4 fa0[8], fb0[4], fa1[8], fb1[4];
-  auto read = [&](int kt, int col, u32x4(&xa)[8], u32x4(&xb)[4]) {
+  auto read = [&](int kt, int half, u32x4(&xa)[8], u32x4(&xb)[4]) {
+    const int col = half ? col1 : col0;
     const uint16_t* as = As + (kt % kStages) * kAStage + arow + col;
-    const uint16_t* bs = Bs + (kt % kStages) * kBStage + brow + col;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) xa[mt] = ld16(as + 16 * mt * kBQ);
+    if (kTransW) {
+      const uint16_t* bs = Bs + (kt % kStages) * kBStage + half * (32 * kBP);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) xb[nt] = ld16(bs + 16 * nt * kBQ);
+      for (int nt = 0; nt < 4; ++nt) {
+        const u32x2 lo = ld_tr4(bs + toff[nt]), hi = ld_tr4(bs + toff[nt] + 4 * kBP);
+        xb[nt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+    } else {
+      const uint16_t* bs = Bs + (kt % kStages) * kBStage + brow + col;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) xb[nt] = ld16(bs + 16 * nt * kBQ);
+    }
   };
   auto mma = [&](const u32x4(&xa)[8], const u32x4(&xb)[4]) {
 #pragma unroll
@@ -253,11 +288,11 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   };
 
   __syncthreads();
-  read(0, col0, fa0, fb0);
+  read(0, 0, fa0, fb0);
   for (int kt = 0; kt < nk; ++kt) {
-    read(kt, col1, fa1, fb1);                           // second half of this step
+    read(kt, 1, fa1, fb1);                              // second half of this step
     mma(fa0, fb0);                                      // first half
-    if (kt + 1 < nk) read(kt + 1, col0, fa0, fb0);      // next step, written two steps ago
+    if (kt + 1 < nk) read(kt + 1, 0, fa0, fb0);         // next step, written two steps ago
     mma(fa1, fb1);                                      // second half
     __syncthreads();
   }
