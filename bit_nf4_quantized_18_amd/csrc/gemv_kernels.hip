@@ -41,6 +41,16 @@ namespace {
 
 constexpr int kGroup = 256;
 
+// 8 consecutive bf16 (x0x1, x2x3, x4x5, x6x7) -> the order lut8_decode_order
+// produces weights in, (x0x2, x4x6, x1x3, x5x7): an MFMA pairs operand slots
+// by position, so both operands only need the same order.
+__device__ __forceinline__ u32x4 decode_order(u32x4 v) {
+  const uint32_t in[4] = {v[0], v[1], v[2], v[3]};
+  uint32_t out[4];
+  to_decode_order(in, out);
+  return u32x4{out[0], out[1], out[2], out[3]};
+}
+
 template <int WAVES, bool kDQ, bool kFuseH>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
                                                           const uint16_t* __restrict__ a,
@@ -60,6 +70,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
   f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(stage);
   f32x4(*hred)[64] = reinterpret_cast<f32x4(*)[64]>(stage + WAVES * 64 * 16);
+  // the same buffers as floats: the reduction reads one component per lane
+  const float* redf = reinterpret_cast<const float*>(stage);
+  const float* hredf = reinterpret_cast<const float*>(stage + WAVES * 64 * 16);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
@@ -125,14 +138,14 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     float gsc;
     if (kDQ) {
       scode = w.scale_codes[bi];
-      gsc = w.group_scale[bi / kGroup];
+      gsc = w.group_scale[static_cast<uint32_t>(bi) / kGroup];
     } else {
       gsc = w.absmax[bi];
     }
     u32x4 xa[8];
     const int xoff = (i * K + kb_c * 64) * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0);
+    for (int j = 0; j < 8; ++j) xa[j] = decode_order(__builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0));
     if (base == 0 && !kFuseH) {
       // H = sum of the LoRA-down partials (fixed order)
       const int mr = M * r;
@@ -152,7 +165,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
       for (int j = 0; j < 8; ++j) {
         const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
         uint32_t wv[4];
-        lut8_natural_order(lut, cw, wv);
+        lut8_decode_order(lut, cw, wv);
         acc = mfma_16x16x32(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
       }
     }
@@ -170,7 +183,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
         for (int j = 0; j < 8; ++j) {
           const int p = 8 * G + j;
           const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
-          hacc = mfma_16x16x32(xa[j], kval ? af : u32x4{0, 0, 0, 0}, hacc);
+          hacc = mfma_16x16x32(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
         }
       }
     }
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
       const int j = l2 & 15;
       float hv = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < WAVES; ++wv) hv += hred[wv][l2][v];
+      for (int wv = 0; wv < WAVES; ++wv) hv += hredf[(wv * 64 + l2) * 4 + v];
       if (mo < M && j < r) {
         h_lds[mo * r + j] = hv;
         if (h_out != nullptr && blockIdx.x == 0) h_out[mo * r + j] = hv;
@@ -206,7 +219,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   if (mo >= M || no >= N) return;
   float sum = 0.0f;
 #pragma unroll
-  for (int wv = 0; wv < WAVES; ++wv) sum += red[wv][l2][v];
+  for (int wv = 0; wv < WAVES; ++wv) sum += redf[(wv * 64 + l2) * 4 + v];
   if (r > 0) {
     float lo = 0.0f;
     const uint16_t* brow = b_lds + (l2 & 15) * r;
@@ -240,6 +253,9 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
   __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
   f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(stage);
   f32x4(*hred)[64] = reinterpret_cast<f32x4(*)[64]>(stage + WAVES * 64 * 16);
+  // the same buffers as floats: the reduction reads one component per lane
+  const float* redf = reinterpret_cast<const float*>(stage);
+  const float* hredf = reinterpret_cast<const float*>(stage + WAVES * 64 * 16);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, g = lane >> 4;
@@ -272,7 +288,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
     const int bi = n_c * nbk + kb_c;
     if (kDQ) {
       T.scode = w.scale_codes[bi];
-      T.gsc = w.group_scale[bi / kGroup];
+      T.gsc = w.group_scale[static_cast<uint32_t>(bi) / kGroup];
     } else {
       T.scode = 0;
       T.gsc = w.absmax[bi];
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
   {
     const int xoff = (i * K + kb_c * 64) * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = __builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0);
+    for (int j = 0; j < 8; ++j) xa[j] = decode_order(__builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0));
   }
   if (kFuseH) {
     // rank row `wave` of A, global -> LDS in 8 copies of 1 KB (whole cache
@@ -333,7 +349,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
       for (int j = 0; j < 8; ++j) {
         const uint32_t cw = (j < 4) ? Tc.c0[j] : Tc.c1[j - 4];
         uint32_t wv[4];
-        lut8_natural_order(lut, cw, wv);
+        lut8_decode_order(lut, cw, wv);
         acc = mfma_16x16x32(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
       }
     }
@@ -355,7 +371,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
         for (int j = 0; j < 8; ++j) {
           const int p = 8 * G + j;
           const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
-          hacc = mfma_16x16x32(xa[j], kval ? af : u32x4{0, 0, 0, 0}, hacc);
+          hacc = mfma_16x16x32(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
         }
       }
     }
@@ -376,7 +392,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
         const int j = l2 & 15;
         float hv = 0.0f;
 #pragma unroll
-        for (int wv = 0; wv < WAVES; ++wv) hv += hred[wv][l2][v];
+        for (int wv = 0; wv < WAVES; ++wv) hv += hredf[(wv * 64 + l2) * 4 + v];
         if (mo < M && j < r) {
           h_lds[mo * r + j] = hv;
           if (h_out != nullptr && blockIdx.x == 0) h_out[mo * r + j] = hv;
@@ -388,7 +404,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
     if (tid < 256 && mo < M && no < N) {
       float sum = 0.0f;
 #pragma unroll
-      for (int wv = 0; wv < WAVES; ++wv) sum += red[wv][l2][v];
+      for (int wv = 0; wv < WAVES; ++wv) sum += redf[(wv * 64 + l2) * 4 + v];
       if (r > 0) {
         float lo = 0.0f;
         const uint16_t* brow = b_lds + (l2 & 15) * r;
