@@ -96,25 +96,30 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
   }
 }
 
-// Prefill projection for r <= 16 (one rank tile): part[s][m][j] = sum over
-// the columns q of split s of P[m][q] Q[j][q], P bf16 M x qn, Q bf16 r x qn.
-// Workgroup: 64 rows of P and one split of the columns. A copy wave streams
-// chunks of 128 columns -- the P tile (64 x 128) and the Q tile (16 x 128),
-// whole 256-byte row runs -- into a ring of four LDS stages with
-// global->LDS buffer loads, three chunks ahead. Four compute waves (16 rows
-// each) read 16-byte fragments and run 16x16x32 bf16 MFMAs (Q as the first
-// operand: a lane ends with 4 ranks of one row). In LDS the 16-byte chunk c
-// of row t is stored at chunk c ^ (t % 16), so the 16 lanes that read one
-// chunk of 16 rows hit distinct banks. Rows past M and Q columns past qn
-// read as zeros; a column of P past qn meets a zero of Q.
+// Prefill projection for r <= 64 (RT = 1, 2 or 4 rank tiles of 16):
+// part[s][m][j] = sum over the columns q of split s of P[m][q] Q[j][q], P bf16
+// M x qn, Q bf16 r x qn. Workgroup: 64 rows of P and one split of the
+// columns. Two copy waves stream chunks of 128 columns -- one the P tile
+// (64 x 128), the other the Q tile (16 RT x 128), whole 256-byte row runs --
+// into a ring of four LDS stages with global->LDS buffer loads, three chunks
+// ahead. Four compute waves (16 rows each) read 16-byte fragments and run
+// 16x16x32 bf16 MFMAs (Q as the first operand: a lane ends with 4 ranks of
+// one row per rank tile). In LDS the 16-byte chunk c of row t is stored at
+// chunk c ^ (t % 16), so the 16 lanes that read one chunk of 16 rows hit
+// distinct banks. Rows past M and Q rows past r read as zeros, Q columns past
+// the split's end too; a column of P past it meets one of those zeros.
 constexpr int kPjRows = 64, kPjCols = 128, kPjStages = 4;
-constexpr int kPjP = kPjRows * kPjCols, kPjQ = 16 * kPjCols;  // bf16 elements per stage
+constexpr int kPjP = kPjRows * kPjCols;  // bf16 elements per stage
 
-__global__ __launch_bounds__(320) void proj_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
+template <int RT>
+__global__ __launch_bounds__(384) void proj_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
                                                    int64_t M, int64_t qn, int r, int splits, int64_t per,
                                                    float* __restrict__ part) {
+  // bf16 elements per Q stage: 64 rows, so that every copy instruction has
+  // rows of its own (those past 16 RT receive zeros and are never read)
+  constexpr int kQ = kPjRows * kPjCols;
   __shared__ __attribute__((aligned(16))) uint16_t Ps[kPjStages * kPjP];
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[kPjStages * kPjQ];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[kPjStages * kQ];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.y;
@@ -123,39 +128,32 @@ __global__ __launch_bounds__(320) void proj_kernel(const uint16_t* __restrict__ 
   const int64_t qe = (qb + per < qn) ? qb + per : qn;
   const int nch = qe > qb ? static_cast<int>((qe - qb + kPjCols - 1) / kPjCols) : 0;
 
-  if (wave == 4) {
-    // ======================= copy wave =======================
-    // instruction u: rows 4u + lane / 16 of the tile, the logical chunk that
-    // the swizzle stores at position lane % 16
+  if (wave >= 4) {
+    // ======================= copy waves =======================
+    // wave 4 moves P, wave 5 moves Q. Instruction u: rows 4u + lane / 16 of
+    // the tile, the logical chunk that the swizzle stores at position lane % 16.
+    const bool isq = wave == 5;
     const int64_t rows = (M - m0 < kPjRows) ? M - m0 : kPjRows;
     const int trow = lane >> 4;
+    constexpr int kCopies = 16;  // per chunk and wave: 64 rows of 128 columns
     auto copy_chunk = [&](int c) {
       const int64_t qc = qb + static_cast<int64_t>(c) * kPjCols;
       const bool live = qc < qe;
       const int64_t qcl = live ? qc : 0;
-      const __amdgpu_buffer_rsrc_t pr = make_rsrc(P + m0 * qn + qcl, live ? (rows * qn - qcl) * 2 : 0);
-      const __amdgpu_buffer_rsrc_t qr = make_rsrc(Q + qcl, live ? (r * qn - qcl) * 2 : 0);
-      uint16_t* ps = Ps + (c % kPjStages) * kPjP;
-      uint16_t* qs = Qs + (c % kPjStages) * kPjQ;
+      const __amdgpu_buffer_rsrc_t rs = isq ? make_rsrc(Q + qcl, live ? (r * qn - qcl) * 2 : 0)
+                                            : make_rsrc(P + m0 * qn + qcl, live ? (rows * qn - qcl) * 2 : 0);
+      uint16_t* dst = isq ? Qs + (c % kPjStages) * kQ : Ps + (c % kPjStages) * kPjP;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < kCopies; ++u) {
         const int row = 4 * u + trow;
         const int chunk = (lane & 15) ^ (row & 15);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(pr, (lds_void*)(ps + u * 512), 16,
-                                                 static_cast<int>((row * qn + 8 * chunk) * 2), 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int row = 4 * u + trow;
-        const int chunk = (lane & 15) ^ (row & 15);
-        // columns past the split's end (or qn) must read zero: offset out of range
-        const bool in = qc + 8 * chunk < qe;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qr, (lds_void*)(qs + u * 512), 16,
-                                                 in ? static_cast<int>((row * qn + 8 * chunk) * 2) : 0x7FFFFFF0, 0,
-                                                 0, 0);
+        // Q: rows past 16 RT and columns past the split's end read zero
+        // (offset out of range)
+        const bool in = !isq || (row < 16 * RT && qc + 8 * chunk < qe);
+        const int off = in ? static_cast<int>((row * qn + 8 * chunk) * 2) : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + u * 512), 16, off, 0, 0, 0);
       }
     };
-    constexpr int kCopies = 20;  // per chunk
     copy_chunk(0);
     copy_chunk(1);
     copy_chunk(2);
@@ -175,24 +173,32 @@ __global__ __launch_bounds__(320) void proj_kernel(const uint16_t* __restrict__ 
   // ======================= compute waves =======================
   const int i = lane & 15, g = lane >> 4;
   const int prow = (16 * wave + i) * kPjCols, qrow = i * kPjCols;
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int c = 0; c < nch; ++c) {
     __syncthreads();  // chunk c is in LDS
     const uint16_t* ps = Ps + (c % kPjStages) * kPjP + prow;
-    const uint16_t* qs = Qs + (c % kPjStages) * kPjQ + qrow;
+    const uint16_t* qs = Qs + (c % kPjStages) * kQ + qrow;
 #pragma unroll
     for (int kk = 0; kk < kPjCols / 32; ++kk) {
-      const int off = ((4 * kk + g) ^ i) * 8;  // rows 16 w + i and i: the swizzle key is i
-      acc = mfma_16x16x32(ld16(qs + off), ld16(ps + off), acc);
+      const int off = ((4 * kk + g) ^ i) * 8;  // rows 16 w + i and 16 t + i: the swizzle key is i
+      const u32x4 pf = ld16(ps + off);
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = mfma_16x16x32(ld16(qs + t * 16 * kPjCols + off), pf, acc[t]);
     }
     __syncthreads();  // the slot may be refilled
   }
-  // acc[v] = sum for rank 4g + v of row m0 + 16 wave + i
+  // acc[t][v] = sum for rank 16 t + 4g + v of row m0 + 16 wave + i
   const int64_t m = m0 + 16 * wave + i;
   if (m < M) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
-      if (4 * g + v < r) part[(static_cast<int64_t>(s) * M + m) * r + 4 * g + v] = acc[v];
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int j = 16 * t + 4 * g + v;
+        if (j < r) part[(static_cast<int64_t>(s) * M + m) * r + j] = acc[t][v];
+      }
   }
 }
 
@@ -523,7 +529,7 @@ int rank_reduce_splits(int64_t m, int64_t n, int64_t k, int r) {
   return static_cast<int>(s);
 }
 
-bool proj_fast(int r) { return r > 0 && r <= 16; }
+bool proj_fast(int r) { return r > 0 && r <= 64; }
 
 int proj_splits(int64_t m, int64_t qn) {
   // about one workgroup per CU, at least one 128-column chunk per split
@@ -554,8 +560,14 @@ hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m
   if (proj_fast(r)) {
     // columns per split: a multiple of the 128-column chunk
     const int64_t per = ((qn + splits - 1) / splits + kPjCols - 1) / kPjCols * kPjCols;
-    hipLaunchKernelGGL(proj_kernel, dim3(static_cast<unsigned>((m + kPjRows - 1) / kPjRows), splits), dim3(320), 0,
-                       st, P, Q, m, qn, r, splits, per, part);
+    const dim3 grid(static_cast<unsigned>((m + kPjRows - 1) / kPjRows), splits);
+    if (r <= 16) {
+      hipLaunchKernelGGL(proj_kernel<1>, grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+    } else if (r <= 32) {
+      hipLaunchKernelGGL(proj_kernel<2>, grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+    } else {
+      hipLaunchKernelGGL(proj_kernel<4>, grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+    }
   } else {
     hipError_t e = launch_skinny(P, Q, m, qn, r, rpad, 1.0f, 1.0f, part, nullptr, splits, st);
     if (e != hipSuccess) return e;
