@@ -23,7 +23,8 @@ STATUS = {0: "QLORA_OK", -1: "QLORA_ERR_NULL", -2: "QLORA_ERR_SHAPE", -3: "QLORA
 
 # Every symbol include/qlora_nf4.h declares.
 EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
-           "qlora_linear_workspace_bytes", "qlora_status_string", "qlora_nf4_levels")
+           "qlora_linear_workspace_bytes", "qlora_linear_fwd_grouped", "qlora_linear_bwd_grouped",
+           "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels")
 
 
 class QloraError(RuntimeError):
@@ -61,6 +62,13 @@ def load():
     lib.qlora_linear_bwd.restype = i32
     lib.qlora_linear_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.qlora_linear_workspace_bytes.restype = sz
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    lib.qlora_linear_fwd_grouped.argtypes = [wp, i32, p64, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    lib.qlora_linear_fwd_grouped.restype = i32
+    lib.qlora_linear_bwd_grouped.argtypes = [wp, i32, p64, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.qlora_linear_bwd_grouped.restype = i32
+    lib.qlora_linear_grouped_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    lib.qlora_linear_grouped_workspace_bytes.restype = sz
     lib.qlora_status_string.argtypes = [i32]
     lib.qlora_status_string.restype = ctypes.c_char_p
     lib.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
@@ -214,4 +222,63 @@ def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, 
     st = load().qlora_linear_bwd(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(h),
                                  _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes, _stream())
     _check(st, "qlora_linear_bwd")
+    return dx, da, db
+
+
+def grouped_workspace_bytes(m: int, n: int, k: int, g: int, r: int) -> int:
+    return int(load().qlora_linear_grouped_workspace_bytes(m, n, k, g, r))
+
+
+def _parts(parts):
+    arr = (ctypes.c_int64 * len(parts))(*[int(p) for p in parts])
+    return arr
+
+
+def linear_fwd_grouped(q: PackedNF4, parts, x, a, b, alpha: float, want_h: bool = True, out=None, h_out=None,
+                       ws=None):
+    """Grouped forward over a stacked weight (row counts ``parts``): y (m, n)
+    with part l's columns = X W_l^T + (alpha/r) (X A_l^T) B_l^T; a is the
+    stacked (g r, k) A, b the stacked (n, r) B. Returns (y, h (m, g r))."""
+    import torch
+
+    m, g, r = x.shape[0], len(parts), b.shape[1]
+    dev = x.device
+    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=dev)
+    h = h_out if h_out is not None else (torch.empty((m, g * r), dtype=torch.float32, device=dev) if want_h else None)
+    if ws is None:
+        nbytes = grouped_workspace_bytes(m, q.n, q.k, g, r)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    nbytes = ws.numel()
+    wc = q.c_struct()
+    pa = _parts(parts)
+    st = load().qlora_linear_fwd_grouped(ctypes.byref(wc), g, pa, _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
+                                         _ptr(y), _ptr(h), _ptr(ws), nbytes, _stream())
+    _check(st, "qlora_linear_fwd_grouped")
+    return y, h
+
+
+def linear_bwd_grouped(q: PackedNF4, parts, x, dy, a, b, alpha: float, h=None, need_dx: bool = True, dx=None,
+                       da=None, db=None, ws=None):
+    """Grouped backward: (dx (m, k) = sum over parts, dA stacked (g r, k),
+    dB stacked (n, r))."""
+    import torch
+
+    m, g, r = dy.shape[0], len(parts), b.shape[1]
+    dev = dy.device
+    if dx is None and need_dx:
+        dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev)
+    if da is None:
+        da = torch.empty((g * r, q.k), dtype=torch.float32, device=dev)
+    if db is None:
+        db = torch.empty((q.n, r), dtype=torch.float32, device=dev)
+    if ws is None:
+        nbytes = grouped_workspace_bytes(m, q.n, q.k, g, r)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    nbytes = ws.numel()
+    wc = q.c_struct()
+    pa = _parts(parts)
+    st = load().qlora_linear_bwd_grouped(ctypes.byref(wc), g, pa, _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r,
+                                         float(alpha), _ptr(h), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes,
+                                         _stream())
+    _check(st, "qlora_linear_bwd_grouped")
     return dx, da, db

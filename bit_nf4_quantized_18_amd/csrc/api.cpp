@@ -29,11 +29,11 @@ struct Carve {
 struct FwdLayout {
   int64_t h32, hs, part, total;
 };
-FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r) {
+FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r, bool grouped = false) {
   (void)n;
   Carve c;
   FwdLayout L{};
-  if (m <= kGemvMaxM) {
+  if (m <= kGemvMaxM && !grouped) {
     // decode: H partial sums, unless the GEMV computes H itself
     L.h32 = c.take(qlora::gemv_fuses_h(k, r) ? 0 : qlora::skinny_splits(m, k) * m * r * 4);
     L.hs = c.take(0);
@@ -49,7 +49,8 @@ FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r) {
 struct BwdLayout {
   int64_t h32, dh32, dhs, at, bt, part, spart, total;
 };
-BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r) {
+// r: adapter slots in total (g rpart for grouped weights)
+BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r, int rpart) {
   Carve c;
   BwdLayout L{};
   const int rp = rank_pad(r);
@@ -65,8 +66,8 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r) {
   }
   if (r == 0) {
     L.part = c.take(0);
-  } else if (qlora::rank_grads_fused(r)) {
-    L.part = c.take(static_cast<int64_t>(qlora::rank_grad_splits(m, n, k, r)) * r * (k + n) * 4);
+  } else if (qlora::rank_grads_fused(r) && qlora::rank_grads_fused(rpart)) {
+    L.part = c.take(static_cast<int64_t>(qlora::rank_grad_splits(m, n, k, r, rpart)) * (r * k + rpart * n) * 4);
   } else {
     L.part = c.take(static_cast<int64_t>(splits) * r * (k > n ? k : n) * 4);
   }
@@ -145,7 +146,14 @@ const char* qlora_status_string(qlora_status status) {
 size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
   if (m <= 0 || n <= 0 || k <= 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
   const int64_t f = fwd_layout(m, n, k, r).total;
-  const int64_t b = bwd_layout(m, n, k, r).total;
+  const int64_t b = bwd_layout(m, n, k, r, r).total;
+  return static_cast<size_t>(f > b ? f : b);
+}
+
+size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int g, int r) {
+  if (m <= 0 || n <= 0 || k <= 0 || g < 1 || g > QLORA_MAX_PARTS || r < 1 || g * r > QLORA_MAX_RANK) return 0;
+  const int64_t f = fwd_layout(m, n, k, g * r, true).total;
+  const int64_t b = bwd_layout(m, n, k, g * r, r).total;
   return static_cast<size_t>(f > b ? f : b);
 }
 
@@ -173,9 +181,15 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dty
   return hip_status(qlora::launch_dequantize(view(w), out_dtype == QLORA_F32, out, stream));
 }
 
-qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
-                              const uint16_t* b, int r, float alpha, uint16_t* y, float* h_out, void* ws,
-                              size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Both linear calls in one form: a weight of grp->g parts (grp null: one
+// part) with r adapter slots in total, rpart per part, s = alpha / rpart.
+qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x, int64_t m,
+                             const uint16_t* a, const uint16_t* b, int r, int rpart, float alpha, uint16_t* y,
+                             float* h_out, void* ws, size_t ws_bytes, hipStream_t stream) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
@@ -189,17 +203,19 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int6
   if (r > 0 && (!aligned16(a) || !aligned16(b))) return QLORA_ERR_ALIGN;
   if (h_out != nullptr && !aligned16(h_out)) return QLORA_ERR_ALIGN;
   const int64_t n = w->n, k = w->k;
-  const size_t need = qlora_linear_workspace_bytes(m, n, k, r);
+  const bool grouped = grp != nullptr;
+  const size_t need = grouped ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
+                              : qlora_linear_workspace_bytes(m, n, k, r);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
 
-  const FwdLayout L = fwd_layout(m, n, k, r);
+  const FwdLayout L = fwd_layout(m, n, k, r, grouped);
   char* base = static_cast<char*>(ws);
-  const float s = (r == 0) ? 0.0f : alpha / static_cast<float>(r);
+  const float s = (rpart == 0) ? 0.0f : alpha / static_cast<float>(rpart);
   const int rp = rank_pad(r);
   const PackedW pw = view(w);
 
-  if (m <= kGemvMaxM) {
+  if (m <= kGemvMaxM && !grouped) {
     // One launch when the GEMV computes H itself; otherwise H as per-split
     // partial sums in the workspace, which the GEMV sums.
     float* hpart = nullptr;
@@ -212,23 +228,30 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int6
   } else {
     float* h32 = (r == 0) ? nullptr : (h_out != nullptr ? h_out : reinterpret_cast<float*>(base + L.h32));
     uint16_t* hs = (r == 0) ? nullptr : reinterpret_cast<uint16_t*>(base + L.hs);
+    // H of every part at once: the parts' A matrices are stacked (r x k)
     if (r > 0)
       QLORA_TRY(qlora::launch_skinny_prefill(x, a, m, k, r, rp, 1.0f, s, reinterpret_cast<float*>(base + L.part), h32,
                                              hs, stream));
-    QLORA_TRY(qlora::launch_gemm_fwd(pw, x, m, hs, b, r, rp, y, stream));
+    qlora::LoraParts one;
+    one.g = 1;
+    one.rpart = rpart;
+    one.end[0] = static_cast<int>(n);
+    QLORA_TRY(qlora::launch_gemm_fwd(pw, x, m, hs, b, rpart, rp, grouped ? *grp : one, y, stream));
   }
   return QLORA_OK;
 }
 
-qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t m,
-                              const uint16_t* a, const uint16_t* b, int r, float alpha, const float* h_saved,
-                              uint16_t* dx, float* da, float* db, void* ws, size_t ws_bytes, hipStream_t stream) {
+qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x,
+                             const uint16_t* dy, int64_t m, const uint16_t* a, const uint16_t* b, int r, int rpart,
+                             float alpha, const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
   if (r < 0) return QLORA_ERR_SHAPE;
   if (r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
   const int64_t n = w->n, k = w->k;
+  const bool grouped = grp != nullptr;
   if (!gemm_tiles_fit(m, k)) return QLORA_ERR_SHAPE;
   if (r > 0) {
     if (a == nullptr || b == nullptr || da == nullptr || db == nullptr) return QLORA_ERR_NULL;
@@ -237,7 +260,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
   if (m == 0) {
     if (r > 0) {
       QLORA_TRY(qlora::launch_fill_zero(da, static_cast<int64_t>(r) * k, stream));
-      QLORA_TRY(qlora::launch_fill_zero(db, n * r, stream));
+      QLORA_TRY(qlora::launch_fill_zero(db, n * rpart, stream));
     }
     return QLORA_OK;
   }
@@ -246,13 +269,14 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
   if (dx == nullptr && r == 0) return QLORA_OK;  // nothing requested
   if (!aligned16(dy) || (x != nullptr && !aligned16(x)) || (dx != nullptr && !aligned16(dx))) return QLORA_ERR_ALIGN;
   if (h_saved != nullptr && !aligned16(h_saved)) return QLORA_ERR_ALIGN;
-  const size_t need = qlora_linear_workspace_bytes(m, n, k, r);
+  const size_t need = grouped ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
+                              : qlora_linear_workspace_bytes(m, n, k, r);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
 
-  const BwdLayout L = bwd_layout(m, n, k, r);
+  const BwdLayout L = bwd_layout(m, n, k, r, rpart);
   char* base = static_cast<char*>(ws);
-  const float s = (r == 0) ? 0.0f : alpha / static_cast<float>(r);
+  const float s = (rpart == 0) ? 0.0f : alpha / static_cast<float>(rpart);
   const int rp = rank_pad(r);
   const PackedW pw = view(w);
   uint16_t* dhs = nullptr;
@@ -271,14 +295,17 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
       QLORA_TRY(qlora::launch_skinny_prefill(x, a, m, k, r, rp, 1.0f, 1.0f, spart, h32, nullptr, stream));
       h = h32;
     }
-    QLORA_TRY(qlora::launch_lora_transpose(a, b, n, k, r, rp, at, bt, stream));
+    // A^T, and B^T (block diagonal for grouped weights: part l's slots see
+    // only its own output columns)
+    QLORA_TRY(qlora::launch_lora_transpose(a, b, n, k, r, rp, at, bt, stream, grp));
     // dH = s dY B  (contraction over n, with B^T as the r x n operand)
     QLORA_TRY(qlora::launch_skinny_prefill(dy, bt, m, n, r, rp, s, 1.0f, spart, dh32, dhs, stream));
-    if (qlora::rank_grads_fused(r)) {
-      // dA = dH^T X (r x k) and dB = s dY^T H (n x r) in one pass each
-      QLORA_TRY(qlora::launch_rank_grads(dh32, x, k, h, dy, n, m, r, s, qlora::rank_grad_splits(m, n, k, r), part,
-                                         da, db, stream));
+    if (qlora::rank_grads_fused(r) && qlora::rank_grads_fused(rpart)) {
+      // dA = dH^T X (r x k) and dB = s dY^T H (n x rpart) in one pass each
+      QLORA_TRY(qlora::launch_rank_grads(dh32, x, k, h, dy, n, m, r, grp, s,
+                                         qlora::rank_grad_splits(m, n, k, r, rpart), part, da, db, stream));
     } else {
+      if (grouped) return QLORA_ERR_UNSUPPORTED;  // checked by the caller
       const int splits = qlora::rank_reduce_splits(m, n, k, r);
       // dA = dH^T X  (r x k)
       QLORA_TRY(qlora::launch_rank_reduce(dh32, x, m, k, r, 1.0f, splits, part, da, 0, stream));
@@ -288,6 +315,61 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
   }
   if (dx != nullptr) QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream));
   return QLORA_OK;
+}
+
+// Parts of a grouped weight: 1..QLORA_MAX_PARTS row counts, each a positive
+// multiple of 256, summing to w->n; rank r >= 1 per part, g r <= QLORA_MAX_RANK.
+qlora_status group_parts(const qlora_nf4_weight* w, int g, const int64_t* parts, int r, qlora::LoraParts* out) {
+  if (w == nullptr || parts == nullptr) return QLORA_ERR_NULL;
+  if (g < 1 || g > QLORA_MAX_PARTS || r < 1) return QLORA_ERR_SHAPE;
+  if (g * r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
+  int64_t end = 0;
+  out->g = g;
+  out->rpart = r;
+  for (int l = 0; l < g; ++l) {
+    if (parts[l] <= 0 || parts[l] % 256 != 0) return QLORA_ERR_SHAPE;
+    end += parts[l];
+    if (end > w->n) return QLORA_ERR_SHAPE;
+    out->end[l] = static_cast<int>(end);
+  }
+  if (end != w->n) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                              const uint16_t* b, int r, float alpha, uint16_t* y, float* h_out, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t m,
+                              const uint16_t* a, const uint16_t* b, int r, float alpha, const float* h_saved,
+                              uint16_t* dx, float* da, float* db, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_linear_fwd_grouped(const qlora_nf4_weight* w, int g, const int64_t* parts, const uint16_t* x,
+                                      int64_t m, const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                      uint16_t* y, float* h_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  qlora::LoraParts lp;
+  const qlora_status st = group_parts(w, g, parts, r, &lp);
+  if (st != QLORA_OK) return st;
+  return linear_fwd_impl(w, &lp, x, m, a, b, g * r, r, alpha, y, h_out, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd_grouped(const qlora_nf4_weight* w, int g, const int64_t* parts, const uint16_t* x,
+                                      const uint16_t* dy, int64_t m, const uint16_t* a, const uint16_t* b, int r,
+                                      float alpha, const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  qlora::LoraParts lp;
+  const qlora_status st = group_parts(w, g, parts, r, &lp);
+  if (st != QLORA_OK) return st;
+  if (r % 16 != 0) return QLORA_ERR_UNSUPPORTED;
+  return linear_bwd_impl(w, &lp, x, dy, m, a, b, g * r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -77,7 +77,7 @@ template <bool kTransW, bool kDQ>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,
                                                        int64_t P, int64_t Qn, const uint16_t* __restrict__ ep_a,
                                                        const uint16_t* __restrict__ ep_b, int64_t ep_ld, int ep_lim,
-                                                       int rpad, uint16_t* __restrict__ out, Levels L) {
+                                                       int rpad, LoraParts lp, uint16_t* __restrict__ out, Levels L) {
   __shared__ __attribute__((aligned(16))) uint16_t As[kStages * kAStage];
   __shared__ __attribute__((aligned(16))) uint16_t Bs[kStages * kBStage];
 
@@ -298,6 +298,16 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   }
 
   // LoRA term: rpad more contraction slots, operands straight from global memory.
+  // Grouped forward: the output columns are lp.g parts (tiles never straddle
+  // two) and part l only sees slots l rpart .. (l+1) rpart - 1, which carry its
+  // own H; row p of ep_b holds that part's B row.
+  int slot_shift = 0;
+  if (!kTransW) {
+    int part = 0;
+#pragma unroll
+    for (int l = 0; l < 3; ++l) part += (l + 1 < lp.g && p0 >= lp.end[l]) ? 1 : 0;
+    slot_shift = part * lp.rpart;
+  }
   for (int ks = 0; ks < rpad / 32; ++ks) {
     u32x4 xa[8], xb[4];
 #pragma unroll
@@ -308,7 +318,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int64_t p = p0 + wp * 64 + 16 * nt + i;
-      xb[nt] = (p < P) ? ld8_bf16_guarded(ep_b + p * ep_ld, 32 * ks + 8 * g, ep_lim, (ep_ld % 8) == 0)
+      xb[nt] = (p < P) ? ld8_bf16_window(ep_b + p * ep_ld, 32 * ks + 8 * g - slot_shift, ep_lim, (ep_ld % 8) == 0)
                        : u32x4{0, 0, 0, 0};
     }
     mma(xa, xb);
@@ -345,10 +355,10 @@ unsigned tiles(int64_t m, int64_t p) { return static_cast<unsigned>(((m + kBM - 
 }  // namespace
 
 hipError_t launch_gemm_fwd(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* hs, const uint16_t* b,
-                           int r, int rpad, uint16_t* y, hipStream_t st) {
+                           int r, int rpad, const LoraParts& parts, uint16_t* y, hipStream_t st) {
   auto kern = w.dq ? nf4_gemm_kernel<false, true> : nf4_gemm_kernel<false, false>;
   hipLaunchKernelGGL(kern, dim3(tiles(m, w.n)), dim3(512), 0, st, w, x, m, w.n, w.k, hs, b, static_cast<int64_t>(r), r,
-                     rpad, y, nf4_table());
+                     rpad, parts, y, nf4_table());
   return hipGetLastError();
 }
 
@@ -356,7 +366,7 @@ hipError_t launch_gemm_dx(const PackedW& w, const uint16_t* dy, int64_t m, const
                           int rpad, uint16_t* dx, hipStream_t st) {
   auto kern = w.dq ? nf4_gemm_kernel<true, true> : nf4_gemm_kernel<true, false>;
   hipLaunchKernelGGL(kern, dim3(tiles(m, w.k)), dim3(512), 0, st, w, dy, m, w.k, w.n, dhs, at,
-                     static_cast<int64_t>(rpad), rpad, rpad, dx, nf4_table());
+                     static_cast<int64_t>(rpad), rpad, rpad, LoraParts{}, dx, nf4_table());
   return hipGetLastError();
 }
 

@@ -68,10 +68,20 @@ bool gemv_fuses_h(int64_t k, int r);
 hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
                        int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st);
 
-// Fused dequant-GEMM, forward: y = x W16^T + hs B^T where hs is bf16 m x rpad
-// (already scaled by s), b is n x r bf16.
+// A weight made of g row blocks (grouped linears sharing their input): part
+// l covers output rows end[l-1] .. end[l]-1 (end[-1] = 0) and owns adapter
+// slots l rpart .. (l+1) rpart - 1. g = 1 (the default): one part.
+struct LoraParts {
+  int g = 1;
+  int rpart = 0;
+  int end[4] = {0, 0, 0, 0};
+};
+
+// Fused dequant-GEMM, forward: y = x W16^T + the LoRA term where hs is bf16
+// m x rpad (already scaled by s) and b is n x r bf16 (r = slots per part);
+// output column p of part l adds sum_j hs[.][l r + j] b[p][j].
 hipError_t launch_gemm_fwd(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* hs,
-                           const uint16_t* b, int r, int rpad, uint16_t* y, hipStream_t st);
+                           const uint16_t* b, int r, int rpad, const LoraParts& parts, uint16_t* y, hipStream_t st);
 
 // Fused dequant-GEMM, backward data: dx = dy W16 + dhs At where dhs is bf16
 // m x rpad and at is bf16 k x rpad (A transposed, zero padded).
@@ -79,8 +89,10 @@ hipError_t launch_gemm_dx(const PackedW& w, const uint16_t* dy, int64_t m, const
                           const uint16_t* at, int rpad, uint16_t* dx, hipStream_t st);
 
 // Transposes with zero padding: bt (rpad x n) from b (n x r); at (k x rpad) from a (r x k).
+// Grouped weights (parts != null, r = g rpart): b is n x rpart (the parts' B
+// stacked) and bt is block diagonal: slot j of part l is zero outside part l's columns.
 hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n, int64_t k, int r, int rpad,
-                                 uint16_t* at, uint16_t* bt, hipStream_t st);
+                                 uint16_t* at, uint16_t* bt, hipStream_t st, const LoraParts* parts = nullptr);
 
 // out(j, c) = scale * sum_m U[m][j] * V[m][c], U float32 m x r, V bf16 m x cn.
 // Deterministic: `splits` partial sums over m-ranges into part (splits x r x cn),
@@ -96,10 +108,13 @@ int rank_reduce_splits(int64_t m, int64_t n, int64_t k, int r);
 // (r % 16 == 0): da (r x k) = dh^T x and db (n x r) = scale * dy^T h, with
 // dh, h float32 m x r and x, dy bf16. part holds splits x r x (k + n)
 // float32 partial sums (splits = rank_grad_splits), reduced in a fixed order.
+// Grouped weights (parts != null): dh and h are m x r0 with r0 = g rpart,
+// da is r0 x k and db is n x rpart, row p of db (part l) from h columns
+// l rpart .. (l+1) rpart - 1; part holds splits x (r0 k + rpart n) float32.
 bool rank_grads_fused(int r);
-int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r);
+int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r0, int r1);
 hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, const float* h, const uint16_t* dy,
-                             int64_t n, int64_t m, int r, float scale, int splits, float* part, float* da, float* db,
-                             hipStream_t st);
+                             int64_t n, int64_t m, int r0, const LoraParts* parts, float scale, int splits, float* part,
+                             float* da, float* db, hipStream_t st);
 
 }  // namespace qlora

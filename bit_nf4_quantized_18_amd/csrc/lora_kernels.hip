@@ -222,7 +222,7 @@ __global__ void skinny_final_kernel(const float* __restrict__ part, int64_t M, i
 
 // at (k x rpad) = A^T zero-padded; bt (rpad x n) = B^T zero-padded.
 __global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int64_t n,
-                                      int64_t k, int r, int rpad, uint16_t* __restrict__ at,
+                                      int64_t k, int r, int rpad, LoraParts lp, uint16_t* __restrict__ at,
                                       uint16_t* __restrict__ bt) {
   int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t na = k * rpad;
@@ -234,9 +234,15 @@ __global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint
   }
   idx -= na;
   if (idx < static_cast<int64_t>(rpad) * n) {
+    // grouped weights: row j of B^T is slot j, owned by part j / rpart, and
+    // is zero outside that part's columns (b holds the parts' B stacked,
+    // rpart columns each)
     const int j = static_cast<int>(idx / n);
     const int64_t nn = idx % n;
-    bt[idx] = (j < r) ? b[nn * r + j] : uint16_t(0);
+    const int part = j / lp.rpart;
+    const int64_t lo = part == 0 ? 0 : lp.end[part - 1 < 3 ? part - 1 : 3];
+    const int64_t hi = part < lp.g ? lp.end[part] : 0;
+    bt[idx] = (j < r && nn >= lo && nn < hi) ? b[nn * lp.rpart + (j - part * lp.rpart)] : uint16_t(0);
   }
 }
 
@@ -354,11 +360,14 @@ __global__ void rank_final_kernel(const float* __restrict__ part, int64_t cn, in
 // order through LDS at the end. Rows past the split or past M and columns
 // past cn read as zeros (buffer ranges); columns past cn are never stored.
 struct RankGradProblem {
-  const float* U;     // m x r float32
+  const float* U;     // m x ldu float32
   const uint16_t* V;  // m x cn bf16
   int64_t cn;
   float* part;        // splits x r x cn float32
   int blocks;         // column blocks of 256
+  int r;              // ranks of this problem (a multiple of 16)
+  int ldu;            // row stride of U
+  LoraParts lp;       // grouped dB: the column block of part l reads U columns l rpart ..
 };
 
 constexpr int kRgCols = 256, kRgRows = 32, kRgStages = 4;
@@ -371,22 +380,28 @@ __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
 }
 
 __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGradProblem p0, RankGradProblem p1,
-                                                                        int64_t M, int r, int splits, int64_t per) {
+                                                                        int64_t M, int splits, int64_t per) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kRgStages * kRgV];
   __shared__ __attribute__((aligned(16))) float Us[kRgStages * kRgU];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rt = r / 16;
   // workgroup -> (problem, column block, rank tile, split)
   int id = blockIdx.x;
-  const int n0 = p0.blocks * rt * splits;
+  const int n0 = p0.blocks * (p0.r / 16) * splits;
   const bool second = id >= n0;
   if (second) id -= n0;
   const RankGradProblem& pb = second ? p1 : p0;
+  const int r = pb.r, ldu = pb.ldu;
+  const int rt = r / 16;
   const int s = id % splits;
   const int j0 = ((id / splits) % rt) * 16;
   const int cb = id / (splits * rt);
   const int64_t c0 = static_cast<int64_t>(cb) * kRgCols;
+  // grouped: the U columns of this column block's part (blocks never straddle parts)
+  int part = 0;
+#pragma unroll
+  for (int l = 0; l < 3; ++l) part += (l + 1 < pb.lp.g && c0 >= pb.lp.end[l]) ? 1 : 0;
+  const int uj0 = part * pb.lp.rpart + j0;
   const int64_t cn = pb.cn;
   const int64_t mb = s * per;
   const int64_t me = (mb + per < M) ? mb + per : M;
@@ -397,14 +412,14 @@ __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGrad
     // V instruction u: rows 2u, 2u+1 (lane / 32), 16 bytes at column 8 (lane % 32);
     // U instruction q: rows 16q + lane / 4, floats j0 + 4 (lane % 4) .. +3.
     const int v_voff = static_cast<int>(((lane >> 5) * cn + 8 * (lane & 31)) * 2);
-    const int u_voff = static_cast<int>(((lane >> 2) * r + j0 + 4 * (lane & 3)) * 4);
+    const int u_voff = static_cast<int>(((lane >> 2) * ldu + uj0 + 4 * (lane & 3)) * 4);
     auto copy_chunk = [&](int c) {
       const int64_t m0 = mb + static_cast<int64_t>(c) * kRgRows;
       const int64_t rows = (m0 < me) ? (me - m0 < kRgRows ? me - m0 : kRgRows) : 0;
       const int64_t mr = (m0 < M) ? m0 : M;
       // rows [m0, m0 + rows) from column c0; the last row ends at cn
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(pb.V + mr * cn + c0, rows > 0 ? (rows * cn - c0) * 2 : 0);
-      const __amdgpu_buffer_rsrc_t ur = make_rsrc(pb.U + mr * r, rows > 0 ? (M - mr) * r * 4 : 0);
+      const __amdgpu_buffer_rsrc_t ur = make_rsrc(pb.U + mr * ldu, rows > 0 ? (M - mr) * ldu * 4 : 0);
       uint16_t* vs = Vs + (c % kRgStages) * kRgV;
       float* us = Us + (c % kRgStages) * kRgU;
       // (whole offsets in the vector operand: the scalar offset is not range checked)
@@ -414,7 +429,7 @@ __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGrad
                                                  v_voff + static_cast<int>(u * 4 * cn), 0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (lds_void*)(us + q * 256), 16, u_voff + q * 64 * r, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (lds_void*)(us + q * 256), 16, u_voff + q * 64 * ldu, 0, 0, 0);
     };
     constexpr int kCopies = 18;  // per chunk
     copy_chunk(0);
@@ -483,13 +498,13 @@ __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGrad
   }
 }
 
-// da[j][c] = sum_s part0[s][j][c] (r x k); db[c][j] = scale * sum_s part1[s][j][c]
-// (n x r), each summed in split order.
+// da[j][c] = sum_s part0[s][j][c] (r0 x k); db[c][j] = scale * sum_s part1[s][j][c]
+// (n x r1), each summed in split order.
 __global__ void rank_grad_final_kernel(const float* __restrict__ part0, const float* __restrict__ part1, int64_t k,
-                                       int64_t n, int r, int splits, float scale, float* __restrict__ da,
+                                       int64_t n, int r0, int r, int splits, float scale, float* __restrict__ da,
                                        float* __restrict__ db) {
   int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t na = static_cast<int64_t>(r) * k;
+  const int64_t na = static_cast<int64_t>(r0) * k;
   if (idx < na) {
     float sum = 0.0f;
     for (int s = 0; s < splits; ++s) sum += part0[static_cast<int64_t>(s) * na + idx];
@@ -599,10 +614,14 @@ hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_
 }
 
 hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n, int64_t k, int r, int rpad,
-                                 uint16_t* at, uint16_t* bt, hipStream_t st) {
+                                 uint16_t* at, uint16_t* bt, hipStream_t st, const LoraParts* parts) {
   const int64_t total = (k + n) * rpad;
+  LoraParts lp;
+  lp.g = 1;
+  lp.rpart = r;
+  lp.end[0] = static_cast<int>(n);
   hipLaunchKernelGGL(lora_transpose_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, a, b,
-                     n, k, r, rpad, at, bt);
+                     n, k, r, rpad, parts != nullptr ? *parts : lp, at, bt);
   return hipGetLastError();
 }
 
@@ -623,10 +642,10 @@ hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int6
 
 bool rank_grads_fused(int r) { return r > 0 && r % 16 == 0; }
 
-int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r) {
+int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r0, int r1) {
   // about one workgroup per CU over both problems, at least one 32-row chunk per split
-  if (!rank_grads_fused(r)) return rank_reduce_splits(m, n, k, r);
-  const int64_t per_split = ((k + kRgCols - 1) / kRgCols + (n + kRgCols - 1) / kRgCols) * (r / 16);
+  if (!rank_grads_fused(r0) || !rank_grads_fused(r1)) return rank_reduce_splits(m, n, k, r0);
+  const int64_t per_split = ((k + kRgCols - 1) / kRgCols) * (r0 / 16) + ((n + kRgCols - 1) / kRgCols) * (r1 / 16);
   int64_t s = 256 / per_split;  // at most one workgroup per CU: no second round
   const int64_t by_rows = (m + kRgRows - 1) / kRgRows;
   if (s > by_rows) s = by_rows;
@@ -636,17 +655,24 @@ int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r) {
 }
 
 hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, const float* h, const uint16_t* dy,
-                             int64_t n, int64_t m, int r, float scale, int splits, float* part, float* da, float* db,
-                             hipStream_t st) {
+                             int64_t n, int64_t m, int r0, const LoraParts* parts, float scale, int splits, float* part,
+                             float* da, float* db, hipStream_t st) {
   // rows per split: a multiple of the 32-row chunk
   const int64_t per = ((m + splits - 1) / splits + kRgRows - 1) / kRgRows * kRgRows;
-  RankGradProblem p0{dh, x, k, part, static_cast<int>((k + kRgCols - 1) / kRgCols)};
-  RankGradProblem p1{h, dy, n, part + static_cast<int64_t>(splits) * r * k, static_cast<int>((n + kRgCols - 1) / kRgCols)};
-  const int64_t wgs = static_cast<int64_t>(p0.blocks + p1.blocks) * (r / 16) * splits;
-  hipLaunchKernelGGL(rank_grad_kernel, dim3(static_cast<unsigned>(wgs)), dim3((kRgWaves + 1) * 64), 0, st, p0, p1, m, r, splits, per);
-  const int64_t total = static_cast<int64_t>(r) * (k + n);
+  LoraParts one;
+  one.g = 1;
+  one.rpart = 0;
+  one.end[0] = static_cast<int>(n);
+  const int r1 = parts != nullptr ? parts->rpart : r0;
+  RankGradProblem p0{dh, x, k, part, static_cast<int>((k + kRgCols - 1) / kRgCols), r0, r0, one};
+  RankGradProblem p1{h, dy, n, part + static_cast<int64_t>(splits) * r0 * k, static_cast<int>((n + kRgCols - 1) / kRgCols),
+                     r1, r0, parts != nullptr ? *parts : one};
+  const int64_t wgs = (static_cast<int64_t>(p0.blocks) * (r0 / 16) + static_cast<int64_t>(p1.blocks) * (r1 / 16)) * splits;
+  hipLaunchKernelGGL(rank_grad_kernel, dim3(static_cast<unsigned>(wgs)), dim3((kRgWaves + 1) * 64), 0, st, p0, p1, m,
+                     splits, per);
+  const int64_t total = static_cast<int64_t>(r0) * k + static_cast<int64_t>(r1) * n;
   hipLaunchKernelGGL(rank_grad_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
-                     p0.part, p1.part, k, n, r, splits, scale, da, db);
+                     p0.part, p1.part, k, n, r0, r1, splits, scale, da, db);
   return hipGetLastError();
 }
 

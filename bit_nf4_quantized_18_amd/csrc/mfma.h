@@ -35,6 +35,19 @@ __device__ __forceinline__ u32x4 ld8_bf16_guarded(const uint16_t* row_ptr, int j
   return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// 8 bf16 from row_ptr[j0 .. j0+8) where only indices in [0, limit) are read
+// (the others are zeros); j0 may be negative. A 16-byte load when the run is
+// whole and 16-byte aligned.
+__device__ __forceinline__ u32x4 ld8_bf16_window(const uint16_t* row_ptr, int j0, int limit, bool row_aligned) {
+  if (j0 >= 0 && j0 + 8 <= limit && row_aligned && (j0 & 7) == 0) return ld16(row_ptr + j0);
+  uint32_t w[4] = {0, 0, 0, 0};
+  for (int e = 0; e < 8; ++e) {
+    const int j = j0 + e;
+    if (j >= 0 && j < limit) w[e >> 1] |= static_cast<uint32_t>(row_ptr[j]) << (16 * (e & 1));
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);

@@ -83,6 +83,7 @@ typedef enum { QLORA_BF16 = 0, QLORA_F32 = 1 } qlora_dtype;
 #define QLORA_BLOCK 64     /* weights per absmax block              */
 #define QLORA_DQ_GROUP 256 /* blocks per double-quantization group  */
 #define QLORA_MAX_RANK 128 /* largest LoRA rank r the kernels take  */
+#define QLORA_MAX_PARTS 4  /* most linears in one grouped call      */
 
 /* A packed NF4 weight W (n x k, row-major, numel = n * k). Device pointers.
  *   codes        : ceil(numel / 2) bytes, packing as above.
@@ -163,6 +164,46 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
 /* Bytes of device workspace that qlora_linear_fwd and qlora_linear_bwd need
  * for these sizes (the larger of the two); 0 if none. Host only, no GPU use. */
 size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+
+/* Grouped linears that read the same input: the adapted projections of one
+ * block ("LoRA y QLoRA en Profundidad", "Modulos Objetivo": q/k/v of the
+ * attention, gate/up of the MLP), run as one call over their stacked weights.
+ *   w     : the g weights W_1..W_g stacked by rows (n = sum of parts) and
+ *           quantized as one matrix. With k % 64 == 0 and every part a
+ *           multiple of 256 rows, no block or double-quantization group spans
+ *           two parts, so the codes, scale codes and group scales are those
+ *           of the parts quantized separately, laid end to end.
+ *   g     : number of parts, 1 .. QLORA_MAX_PARTS.
+ *   parts : host array of the g row counts (each a positive multiple of 256,
+ *           summing to w->n).
+ *   a     : bf16 (g r) x k, the parts' A matrices stacked (part l: rows l r ..).
+ *   b     : bf16 n x r, the parts' B matrices stacked (part l: its rows of W).
+ *   r     : rank of every part (1 <= r, g r <= QLORA_MAX_RANK); s = fl32(alpha / r).
+ * Forward: y (bf16 m x n) holds, in the columns of part l,
+ *   X W_l^T + s (X A_l^T) B_l^T;
+ * h_out (float32 m x (g r), may be NULL) = [X A_1^T | ... | X A_g^T].
+ * Backward for dL/dY = dy (bf16 m x n, part l in its columns):
+ *   dx (bf16 m x k, may be NULL) = sum over l of dY_l W_l + dH_l A_l,
+ *   da (float32 (g r) x k) = the dA_l stacked, db (float32 n x r) = the dB_l
+ *   stacked, with dH_l = s dY_l B_l, dA_l = dH_l^T X, dB_l = s dY_l^T H_l;
+ *   h_saved (float32 m x (g r), from h_out) may be NULL. The backward needs
+ *   r % 16 == 0 (QLORA_ERR_UNSUPPORTED otherwise).
+ * Both take the fused dequant-GEMM for every m; ws must hold
+ * qlora_linear_grouped_workspace_bytes(m, n, k, g, r) bytes.
+ * Errors as for the single-linear calls; SHAPE also for bad parts. */
+qlora_status qlora_linear_fwd_grouped(const qlora_nf4_weight* w, int g, const int64_t* parts,
+                                      const uint16_t* x, int64_t m, const uint16_t* a,
+                                      const uint16_t* b, int r, float alpha, uint16_t* y,
+                                      float* h_out, void* ws, size_t ws_bytes, hipStream_t stream);
+qlora_status qlora_linear_bwd_grouped(const qlora_nf4_weight* w, int g, const int64_t* parts,
+                                      const uint16_t* x, const uint16_t* dy, int64_t m,
+                                      const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                      const float* h_saved, uint16_t* dx, float* da, float* db,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for the grouped calls (n = sum of parts); 0 for invalid
+ * sizes. Host only, no GPU use. */
+size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int g, int r);
 
 /* Static, NUL-terminated description of a status. Host only. */
 const char* qlora_status_string(qlora_status status);
