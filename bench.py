@@ -113,23 +113,62 @@ def main():
             qn.linear_bwd(L["q"], L["x"], L["dy"], L["a"], L["b"], ALPHA, h=L["h"], dx=L["dx"], da=L["da"],
                           db=L["db"], ws=L["ws"])
 
+    # Grouped step: the linears that read the same input in the model run as
+    # one call over their stacked weight (q/k/v on one X, gate/up on one X).
+    byname = {L["lay"].name: L for L in layers}
+    groups = []
+    for names in (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",)):
+        Ls = [byname[nm] for nm in names]
+        if len(Ls) == 1:
+            groups.append(dict(single=Ls[0]))
+            continue
+        k = Ls[0]["lay"].k
+        parts_n = [L["lay"].n for L in Ls]
+        ntot = sum(parts_n)
+        w = torch.cat([torch.from_numpy(synth.weight(wl, L["lay"])) for L in Ls], dim=0).to(dev)
+        qg = qn.quantize(w)
+        del w
+        nbytes = qn.grouped_workspace_bytes(M, ntot, k, len(Ls), R)
+        groups.append(dict(
+            parts=parts_n, q=qg, x=Ls[0]["x"], a=torch.cat([L["a"] for L in Ls]), b=torch.cat([L["b"] for L in Ls]),
+            dy=torch.cat([L["dy"] for L in Ls], dim=1),
+            y=torch.empty((M, ntot), dtype=torch.bfloat16, device=dev),
+            h=torch.empty((M, len(Ls) * R), dtype=torch.float32, device=dev),
+            dx=torch.empty((M, k), dtype=torch.bfloat16, device=dev),
+            da=torch.empty((len(Ls) * R, k), dtype=torch.float32, device=dev),
+            db=torch.empty((ntot, R), dtype=torch.float32, device=dev),
+            ws=torch.empty(nbytes, dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+
+    def train_step_grouped():
+        for G in groups:
+            if "single" in G:
+                L = G["single"]
+                qn.linear_fwd(L["q"], L["x"], L["a"], L["b"], ALPHA, out=L["y"], h_out=L["h"], ws=L["ws"])
+                qn.linear_bwd(L["q"], L["x"], L["dy"], L["a"], L["b"], ALPHA, h=L["h"], dx=L["dx"], da=L["da"],
+                              db=L["db"], ws=L["ws"])
+                continue
+            qn.linear_fwd_grouped(G["q"], G["parts"], G["x"], G["a"], G["b"], ALPHA, out=G["y"], h_out=G["h"],
+                                  ws=G["ws"])
+            qn.linear_bwd_grouped(G["q"], G["parts"], G["x"], G["dy"], G["a"], G["b"], ALPHA, h=G["h"], dx=G["dx"],
+                                  da=G["da"], db=G["db"], ws=G["ws"])
+
     step_fwd = sum(fwd_flops(M, L["lay"].n, L["lay"].k, R) for L in layers)
     step_bwd = sum(bwd_flops(M, L["lay"].n, L["lay"].k, R) for L in layers)
     step_flops = step_fwd + step_bwd
 
     # ------------------------------------------------------- training step
-    value = ms_step = None
-    if want("train"):
-        log("[bench] training step: capture")
-        train_step()  # eager warm-up (also loads every kernel)
+    def time_step(fn, label):
+        log(f"[bench] {label}: capture")
+        fn()  # eager warm-up (also loads every kernel)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            train_step()
+            fn()
         for _ in range(args.warmup):
             g.replay()
         torch.cuda.synchronize()
-        log(f"[bench] training step: timing {args.steps} steps")
+        log(f"[bench] {label}: timing {args.steps} steps")
         t0 = time.perf_counter()
         e0, e1 = ev(), ev()
         e0.record()
@@ -138,12 +177,18 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms_step = e0.elapsed_time(e1) / args.steps
-        value = step_flops / (ms_step * 1e-3) / 1e12
-        parts["train_step"] = {"ms_per_step": ms_step, "tflops": value, "gflop_per_step": step_flops / 1e9,
-                               "frac_bf16_peak": value / BF16_PEAK_TFLOPS, "wall_s": wall}
-        log(f"[bench] training step {ms_step:.3f} ms  {value:.1f} TFLOP/s")
+        ms = e0.elapsed_time(e1) / args.steps
+        tf = step_flops / (ms * 1e-3) / 1e12
+        log(f"[bench] {label} {ms:.3f} ms  {tf:.1f} TFLOP/s")
         del g
+        return {"ms_per_step": ms, "tflops": tf, "gflop_per_step": step_flops / 1e9,
+                "frac_bf16_peak": tf / BF16_PEAK_TFLOPS, "wall_s": wall}
+
+    value = ms_step = None
+    if want("train"):
+        parts["train_step_per_linear"] = time_step(train_step, "training step, one call per linear")
+        parts["train_step"] = time_step(train_step_grouped, "training step (q/k/v and gate/up grouped)")
+        ms_step, value = parts["train_step"]["ms_per_step"], parts["train_step"]["tflops"]
 
     # ------------------------------------------- fused dequant-GEMM kernels
     roofline = None
@@ -320,7 +365,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "llama7b_layer_set_fwd_bwd", "layers": "q/k/v/o 4096x4096, gate/up 11008x4096, "
                    "down 4096x11008", "tokens": M, "lora_r": R, "lora_alpha": ALPHA, "nf4_block": 64,
-                   "double_quant_block": 256, "global_batch": 4, "seq_len": 512, "parallelism": "none (1 GPU)"},
+                   "double_quant_block": 256, "global_batch": 4, "seq_len": 512, "parallelism": "none (1 GPU)",
+                   "launches": "q/k/v one grouped call on a shared input, gate/up likewise; o and down single"},
         "roofline": roofline, "cpu_baseline": cpu, "parts": parts,
     }
     print(json.dumps(line), flush=True)
