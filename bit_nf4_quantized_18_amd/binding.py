@@ -24,7 +24,11 @@ STATUS = {0: "QLORA_OK", -1: "QLORA_ERR_NULL", -2: "QLORA_ERR_SHAPE", -3: "QLORA
 # Every symbol include/qlora_nf4.h declares.
 EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
            "qlora_linear_workspace_bytes", "qlora_linear_fwd_grouped", "qlora_linear_bwd_grouped",
-           "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels")
+           "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels",
+           "qlora_quantize_codebook", "qlora_codebook_levels")
+
+CODEBOOK_NF4 = 0   # normal-quantile levels
+CODEBOOK_INT4 = 1  # 16 evenly spaced levels on [-1, 1]
 
 
 class QloraError(RuntimeError):
@@ -36,7 +40,7 @@ class QloraError(RuntimeError):
 class NF4WeightC(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int64), ("k", ctypes.c_int64), ("codes", ctypes.c_void_p),
                 ("scale_codes", ctypes.c_void_p), ("group_scale", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
-                ("double_quant", ctypes.c_int32)]
+                ("double_quant", ctypes.c_int32), ("codebook", ctypes.c_int32)]
 
 
 _LIB = None
@@ -73,6 +77,10 @@ def load():
     lib.qlora_status_string.restype = ctypes.c_char_p
     lib.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
     lib.qlora_nf4_levels.restype = i32
+    lib.qlora_quantize_codebook.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp]
+    lib.qlora_quantize_codebook.restype = i32
+    lib.qlora_codebook_levels.argtypes = [i32, ctypes.POINTER(ctypes.c_float)]
+    lib.qlora_codebook_levels.restype = i32
     _LIB = lib
     return lib
 
@@ -81,12 +89,15 @@ def status_string(status: int) -> str:
     return load().qlora_status_string(status).decode()
 
 
-def levels():
-    """The 16 float32 levels the kernels use (host call)."""
+def levels(codebook: int = CODEBOOK_NF4):
+    """The 16 float32 levels the kernels use for `codebook` (host call)."""
     buf = (ctypes.c_float * 16)()
-    n = load().qlora_nf4_levels(buf)
+    if codebook == CODEBOOK_NF4:
+        n = load().qlora_nf4_levels(buf)
+    else:
+        n = load().qlora_codebook_levels(int(codebook), buf)
     if n != 16:
-        raise QloraError(n, "qlora_nf4_levels")
+        raise QloraError(n, "qlora_codebook_levels")
     return list(buf)
 
 
@@ -119,12 +130,14 @@ class PackedNF4:
     scale_codes: "object" = None    # uint8 [nblocks]        (double quant)
     group_scale: "object" = None    # float32 [ngroups]      (double quant)
     absmax: "object" = None         # float32 [nblocks]      (exact a_b; required without double quant)
+    codebook: int = CODEBOOK_NF4    # level table the codes index
 
     def c_struct(self) -> NF4WeightC:
         return NF4WeightC(self.n, self.k, self.codes.data_ptr(),
                           None if self.scale_codes is None else self.scale_codes.data_ptr(),
                           None if self.group_scale is None else self.group_scale.data_ptr(),
-                          None if self.absmax is None else self.absmax.data_ptr(), int(self.double_quant))
+                          None if self.absmax is None else self.absmax.data_ptr(), int(self.double_quant),
+                          int(self.codebook))
 
 
 def _empty(n, dtype, device):
@@ -134,9 +147,10 @@ def _empty(n, dtype, device):
     return torch.empty(max(n, 1), dtype=dtype, device=device)
 
 
-def quantize(w, double_quant: bool = True, keep_absmax: bool = False) -> PackedNF4:
+def quantize(w, double_quant: bool = True, keep_absmax: bool = False, codebook: int = CODEBOOK_NF4) -> PackedNF4:
     """Quantize a float32 CUDA tensor (any shape; flattened row-major).
-    A 2-D tensor gives n, k = its shape; other shapes give n = 1."""
+    A 2-D tensor gives n, k = its shape; other shapes give n = 1.
+    codebook: CODEBOOK_NF4 (qlora_nf4_quantize) or CODEBOOK_INT4."""
     import torch
 
     if w.dtype != torch.float32 or not w.is_cuda:
@@ -151,11 +165,16 @@ def quantize(w, double_quant: bool = True, keep_absmax: bool = False) -> PackedN
     sc = _empty(nb, torch.uint8, dev) if double_quant else None
     gs = _empty(ng, torch.float32, dev) if double_quant else None
     am = _empty(nb, torch.float32, dev) if (keep_absmax or not double_quant) else None
-    st = load().qlora_nf4_quantize(_ptr(w), numel, int(double_quant), _ptr(codes), _ptr(sc), _ptr(gs), _ptr(am),
-                                   _stream())
-    _check(st, "qlora_nf4_quantize")
+    if codebook == CODEBOOK_NF4:
+        st = load().qlora_nf4_quantize(_ptr(w), numel, int(double_quant), _ptr(codes), _ptr(sc), _ptr(gs),
+                                       _ptr(am), _stream())
+        _check(st, "qlora_nf4_quantize")
+    else:
+        st = load().qlora_quantize_codebook(_ptr(w), numel, int(double_quant), int(codebook), _ptr(codes),
+                                            _ptr(sc), _ptr(gs), _ptr(am), _stream())
+        _check(st, "qlora_quantize_codebook")
     return PackedNF4(n, k, codes[: (numel + 1) // 2], double_quant, None if sc is None else sc[:nb],
-                     None if gs is None else gs[:ng], None if am is None else am[:nb])
+                     None if gs is None else gs[:ng], None if am is None else am[:nb], int(codebook))
 
 
 def dequantize(q: PackedNF4, dtype=None):

@@ -78,6 +78,7 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r, int rpart) {
 qlora_status check_weight(const qlora_nf4_weight* w, bool linear) {
   if (w == nullptr || w->codes == nullptr) return QLORA_ERR_NULL;
   if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (w->codebook != QLORA_CODEBOOK_NF4 && w->codebook != QLORA_CODEBOOK_INT4) return QLORA_ERR_UNSUPPORTED;
   if (w->double_quant) {
     if (w->scale_codes == nullptr || w->group_scale == nullptr) return QLORA_ERR_NULL;
     if (!aligned16(w->scale_codes) || !aligned16(w->group_scale)) return QLORA_ERR_ALIGN;
@@ -105,6 +106,7 @@ PackedW view(const qlora_nf4_weight* w) {
   p.n = w->n;
   p.k = w->k;
   p.dq = w->double_quant;
+  p.codebook = w->codebook;
   return p;
 }
 
@@ -157,9 +159,10 @@ size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int
   return static_cast<size_t>(f > b ? f : b);
 }
 
-qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant, uint8_t* codes,
+qlora_status qlora_quantize_codebook(const float* w, int64_t numel, int double_quant, int codebook, uint8_t* codes,
                                 uint8_t* scale_codes, float* group_scale, float* absmax, hipStream_t stream) {
   if (double_quant != 0 && double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_INT4) return QLORA_ERR_UNSUPPORTED;
   if (w == nullptr || codes == nullptr) return QLORA_ERR_NULL;
   if (double_quant && (scale_codes == nullptr || group_scale == nullptr)) return QLORA_ERR_NULL;
   if (!double_quant && absmax == nullptr) return QLORA_ERR_NULL;
@@ -167,8 +170,14 @@ qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant,
   if (!aligned16(w) || !aligned16(codes)) return QLORA_ERR_ALIGN;
   if (double_quant && (!aligned16(scale_codes) || !aligned16(group_scale))) return QLORA_ERR_ALIGN;
   if (absmax != nullptr && !aligned16(absmax)) return QLORA_ERR_ALIGN;
-  return hip_status(qlora::launch_quantize(w, numel, double_quant, codes, double_quant ? scale_codes : nullptr,
+  return hip_status(qlora::launch_quantize(w, numel, double_quant, codebook, codes, double_quant ? scale_codes : nullptr,
                                            double_quant ? group_scale : nullptr, absmax, stream));
+}
+
+qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant, uint8_t* codes,
+                                uint8_t* scale_codes, float* group_scale, float* absmax, hipStream_t stream) {
+  return qlora_quantize_codebook(w, numel, double_quant, QLORA_CODEBOOK_NF4, codes, scale_codes, group_scale, absmax,
+                                 stream);
 }
 
 qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dtype, void* out,

@@ -56,7 +56,27 @@ Levels build_levels() {
   return L;
 }
 
+// numpy's float64 linspace(-1, 1, 16): k * (2 / 15) - 1, the last value
+// exactly 1, each rounded once to float32.
+Levels build_int4() {
+  Levels L;
+  const double step = 2.0 / 15.0;
+  for (int c = 0; c < 15; ++c) L.v[c] = static_cast<float>(static_cast<double>(c) * step + -1.0);
+  L.v[15] = 1.0f;
+  return L;
+}
+
 }  // namespace
+
+const Levels& codebook_table(int codebook) {
+  if (codebook == QLORA_CODEBOOK_INT4) {
+    static std::once_flag once;
+    static Levels table;
+    std::call_once(once, [] { table = build_int4(); });
+    return table;
+  }
+  return nf4_table();
+}
 
 const Levels& nf4_table() {
   static std::once_flag once;
@@ -70,6 +90,14 @@ const Levels& nf4_table() {
 extern "C" int qlora_nf4_levels(float out16[16]) {
   if (out16 == nullptr) return QLORA_ERR_NULL;
   const qlora::Levels& L = qlora::nf4_table();
+  for (int c = 0; c < 16; ++c) out16[c] = L.v[c];
+  return 16;
+}
+
+extern "C" int qlora_codebook_levels(int codebook, float out16[16]) {
+  if (out16 == nullptr) return QLORA_ERR_NULL;
+  if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_INT4) return QLORA_ERR_UNSUPPORTED;
+  const qlora::Levels& L = qlora::codebook_table(codebook);
   for (int c = 0; c < 16; ++c) out16[c] = L.v[c];
   return 16;
 }

@@ -358,7 +358,7 @@ hipError_t launch_gemm_fwd(const PackedW& w, const uint16_t* x, int64_t m, const
                            int r, int rpad, const LoraParts& parts, uint16_t* y, hipStream_t st) {
   auto kern = w.dq ? nf4_gemm_kernel<false, true> : nf4_gemm_kernel<false, false>;
   hipLaunchKernelGGL(kern, dim3(tiles(m, w.n)), dim3(512), 0, st, w, x, m, w.n, w.k, hs, b, static_cast<int64_t>(r), r,
-                     rpad, parts, y, nf4_table());
+                     rpad, parts, y, codebook_table(w.codebook));
   return hipGetLastError();
 }
 
@@ -366,7 +366,7 @@ hipError_t launch_gemm_dx(const PackedW& w, const uint16_t* dy, int64_t m, const
                           int rpad, uint16_t* dx, hipStream_t st) {
   auto kern = w.dq ? nf4_gemm_kernel<true, true> : nf4_gemm_kernel<true, false>;
   hipLaunchKernelGGL(kern, dim3(tiles(m, w.k)), dim3(512), 0, st, w, dy, m, w.k, w.n, dhs, at,
-                     static_cast<int64_t>(rpad), rpad, rpad, LoraParts{}, dx, nf4_table());
+                     static_cast<int64_t>(rpad), rpad, rpad, LoraParts{}, dx, codebook_table(w.codebook));
   return hipGetLastError();
 }
 

@@ -451,13 +451,13 @@ hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uin
     auto kern = w.dq ? (fuse ? gemv_persistent_kernel<true, true> : gemv_persistent_kernel<true, false>)
                      : (fuse ? gemv_persistent_kernel<false, true> : gemv_persistent_kernel<false, false>);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a, hpart, hsplits, b,
-                       r, s, y, h_out, nf4_table());
+                       r, s, y, h_out, codebook_table(w.codebook));
     return hipGetLastError();
   }
   auto kern = w.dq ? (fuse ? gemv_kernel<kWaves, true, true> : gemv_kernel<kWaves, true, false>)
                    : (fuse ? gemv_kernel<kWaves, false, true> : gemv_kernel<kWaves, false, false>);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nrg)), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a,
-                     hpart, hsplits, b, r, s, y, h_out, nf4_table());
+                     hpart, hsplits, b, r, s, y, h_out, codebook_table(w.codebook));
   return hipGetLastError();
 }
 

@@ -21,11 +21,14 @@ struct Levels {
 // Host-side level table, built once (thread-safe) from the standard-normal
 // quantile function.
 const Levels& nf4_table();
+// The table of a codebook: QLORA_CODEBOOK_NF4 or QLORA_CODEBOOK_INT4 (16
+// evenly spaced levels on [-1, 1]); any other value gives the NF4 table.
+const Levels& codebook_table(int codebook);
 
 // ---------------------------------------------------------------------------
 // Launchers (each enqueues on `s` and returns hipGetLastError()).
 // ---------------------------------------------------------------------------
-hipError_t launch_quantize(const float* w, int64_t numel, int dq, uint8_t* codes, uint8_t* scale_codes,
+hipError_t launch_quantize(const float* w, int64_t numel, int dq, int codebook, uint8_t* codes, uint8_t* scale_codes,
                            float* group_scale, float* absmax, hipStream_t s);
 
 // Packed weight view used by all kernels that read NF4 weights.
@@ -36,6 +39,7 @@ struct PackedW {
   const float* absmax;         // !dq
   int64_t n, k;
   int dq;
+  int codebook;  // QLORA_CODEBOOK_*
 };
 
 hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream_t s);

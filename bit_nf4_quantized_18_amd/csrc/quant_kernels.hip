@@ -20,7 +20,8 @@ constexpr int kGroup = 256;
 // Nearest level of x in [-1, 1]: bracket L[k] <= x < L[k+1] by a 4-step
 // binary search over the ascending table (held in LDS, with lv[16] = +inf),
 // then the closer of the two fp32 distances; an exact tie keeps k (the lower
-// index). Levels further away cannot tie: the gaps exceed 0.079.
+// index). Levels further away cannot tie: adjacent gaps exceed 0.079 in the
+// NF4 table and are 2/15 in the evenly spaced one.
 __device__ __forceinline__ uint32_t nearest_nf4(float x, const float* lv) {
   uint32_t k = 0;
 #pragma unroll
@@ -244,12 +245,12 @@ __global__ void fill_zero_kernel(float* p, int64_t count) {
 
 }  // namespace
 
-hipError_t launch_quantize(const float* w, int64_t numel, int dq, uint8_t* codes, uint8_t* scale_codes,
+hipError_t launch_quantize(const float* w, int64_t numel, int dq, int codebook, uint8_t* codes, uint8_t* scale_codes,
                            float* group_scale, float* absmax, hipStream_t s) {
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(nf4_quantize_kernel, dim3(static_cast<unsigned>(ngroups)), dim3(256), 0, s, w, numel, dq,
-                     codes, scale_codes, group_scale, absmax, nf4_table());
+                     codes, scale_codes, group_scale, absmax, codebook_table(codebook));
   return hipGetLastError();
 }
 
@@ -259,7 +260,7 @@ hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream
   const unsigned grid = static_cast<unsigned>((nwords + 1023) / 1024);
   auto kern = out_f32 ? (w.dq ? nf4_dequantize_kernel<true, true> : nf4_dequantize_kernel<true, false>)
                       : (w.dq ? nf4_dequantize_kernel<false, true> : nf4_dequantize_kernel<false, false>);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, w, out, nf4_table());
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, w, out, codebook_table(w.codebook));
   return hipGetLastError();
 }
 

@@ -19,7 +19,10 @@
  *
  * Numeric conventions (the readings taken where the pages are silent):
  *   - levels: 16 float32 values, ascending, level 7 is +0.0, levels 0 and 15
- *     are -1 and +1 (see qlora_nf4_levels);
+ *     are -1 and +1 (see qlora_nf4_levels). The same page's NF4-vs-INT4
+ *     example also names the evenly spaced 4-bit code; a weight may use it
+ *     instead (codebook QLORA_CODEBOOK_INT4: level k = fl32(-1 + 2k/15), no
+ *     exact zero level), with every other convention unchanged;
  *   - block b covers elements [64 b, 64 b + 64) of the row-major flattening
  *     (the last block may be partial); group g covers blocks [256 g, 256 g + 256);
  *   - a_b = max |w| over block b; x = w / a_b (correctly rounded float32);
@@ -85,11 +88,16 @@ typedef enum { QLORA_BF16 = 0, QLORA_F32 = 1 } qlora_dtype;
 #define QLORA_MAX_RANK 128 /* largest LoRA rank r the kernels take  */
 #define QLORA_MAX_PARTS 4  /* most linears in one grouped call      */
 
+#define QLORA_CODEBOOK_NF4 0  /* normal-quantile levels (the default)  */
+#define QLORA_CODEBOOK_INT4 1 /* 16 evenly spaced levels on [-1, 1]    */
+
 /* A packed NF4 weight W (n x k, row-major, numel = n * k). Device pointers.
  *   codes        : ceil(numel / 2) bytes, packing as above.
  *   scale_codes  : double_quant = 1: ceil(numel / 64) uint8 codes c2_b.
  *   group_scale  : double_quant = 1: ceil(ceil(numel / 64) / 256) float M_g.
  *   absmax       : double_quant = 0: ceil(numel / 64) float a_b.
+ *   codebook     : QLORA_CODEBOOK_NF4 or QLORA_CODEBOOK_INT4, the level table
+ *                  the codes index (a zero-initialised struct selects NF4).
  * Pointers not used by the selected mode may be NULL. */
 typedef struct {
   int64_t n, k;
@@ -98,6 +106,7 @@ typedef struct {
   const float* group_scale;
   const float* absmax;
   int32_t double_quant;
+  int32_t codebook;
 } qlora_nf4_weight;
 
 /* Quantize `numel` float32 weights `w` (any numel >= 1; partial last block and
@@ -115,6 +124,18 @@ typedef struct {
 qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant, uint8_t* codes,
                                 uint8_t* scale_codes, float* group_scale, float* absmax,
                                 hipStream_t stream);
+
+/* qlora_nf4_quantize with the level table chosen by `codebook`
+ * (QLORA_CODEBOOK_NF4 gives exactly qlora_nf4_quantize; QLORA_CODEBOOK_INT4
+ * the evenly spaced levels of the NF4-vs-INT4 example in Ultralytics glossary
+ * "QLoRA", "Come funziona QLoRA"). The nearest-level rule, ties, packing,
+ * blocks and double quantization are the same; an all-zero block gets code 7
+ * in either table. A weight quantized this way is used with its
+ * qlora_nf4_weight.codebook set to the same value.
+ * Errors: as qlora_nf4_quantize, and UNSUPPORTED for an unknown codebook. */
+qlora_status qlora_quantize_codebook(const float* w, int64_t numel, int double_quant, int codebook,
+                                     uint8_t* codes, uint8_t* scale_codes, float* group_scale,
+                                     float* absmax, hipStream_t stream);
 
 /* Dequantize a packed weight to bf16 (w16) or float32 (w32), n*k elements,
  * row-major, into `out`. Ultralytics glossary "QLoRA", "Come funziona QLoRA"
@@ -213,6 +234,12 @@ const char* qlora_status_string(qlora_status status);
  * offset 0.9677083 (Ultralytics glossary "QLoRA", the NF4-vs-INT4 example).
  * Returns 16, or QLORA_ERR_NULL. Host only, no GPU use. */
 int qlora_nf4_levels(float out16[16]);
+
+/* Copy the 16 float32 levels of `codebook` into out16 (host memory):
+ * QLORA_CODEBOOK_NF4 as qlora_nf4_levels, QLORA_CODEBOOK_INT4 level k =
+ * fl32(-1 + 2k/15) (correctly rounded; the last is exactly +1).
+ * Returns 16, QLORA_ERR_NULL or QLORA_ERR_UNSUPPORTED. Host only. */
+int qlora_codebook_levels(int codebook, float out16[16]);
 
 #ifdef __cplusplus
 }

@@ -78,7 +78,10 @@ def nf4_levels(inv_cdf=None) -> np.ndarray:
 
 
 def int4_levels() -> np.ndarray:
-    """16 evenly spaced levels on [-1, 1] -- [U]'s comparison baseline."""
+    """16 evenly spaced levels on [-1, 1] -- [U]'s comparison baseline.
+    Level k is -1 + 2k/15 rounded once to float32 (numpy forms the float64
+    value and rounds it; a float32-stepped linspace may differ in the last
+    bits)."""
     return np.linspace(-1.0, 1.0, 16, dtype=np.float32)
 
 

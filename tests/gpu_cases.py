@@ -29,10 +29,16 @@ def f64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def oracle_weight(w: np.ndarray, dq: bool = True):
+def oracle_levels(codebook: int = 0) -> np.ndarray:
+    """The oracle's table for a codebook id (0: NF4, 1: evenly spaced INT4)."""
+    return O.int4_levels() if codebook == 1 else O.nf4_levels()
+
+
+def oracle_weight(w: np.ndarray, dq: bool = True, codebook: int = 0):
     """Oracle quantization of an n x k fp32 weight and its bf16 dequantized values."""
-    q = O.quantize(w.reshape(-1), dq)
-    _, bits = O.dequantize(q)
+    lv = oracle_levels(codebook)
+    q = O.quantize(w.reshape(-1), dq, lv)
+    _, bits = O.dequantize(q, lv)
     return q, O.bf16_bits_to_f32(bits).reshape(w.shape)
 
 

@@ -37,6 +37,21 @@ def test_levels_bit_equal_to_oracle():
 def test_levels_null_pointer():
     lib = binding.load()
     assert lib.qlora_nf4_levels(None) == -1
+    assert lib.qlora_codebook_levels(binding.CODEBOOK_INT4, None) == -1
+
+
+def test_int4_levels_bit_equal_to_oracle():
+    got = np.array(binding.levels(binding.CODEBOOK_INT4), dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), O.int4_levels().view(np.uint32))
+    nf4 = np.array(binding.levels(binding.CODEBOOK_NF4), dtype=np.float32)
+    assert np.array_equal(nf4.view(np.uint32), O.nf4_levels().view(np.uint32))
+
+
+def test_unknown_codebook_levels():
+    buf = (ctypes.c_float * 16)()
+    lib = binding.load()
+    assert lib.qlora_codebook_levels(2, buf) == -4
+    assert lib.qlora_codebook_levels(-1, buf) == -4
 
 
 def test_status_strings():
@@ -59,8 +74,8 @@ def test_workspace_sizes():
 P = 1 << 20
 
 
-def wstruct(n=64, k=64, dq=1, codes=P, sc=P, gs=P, am=None):
-    return binding.NF4WeightC(n, k, codes, sc, gs, am, dq)
+def wstruct(n=64, k=64, dq=1, codes=P, sc=P, gs=P, am=None, codebook=0):
+    return binding.NF4WeightC(n, k, codes, sc, gs, am, dq, codebook)
 
 
 def test_quantize_argument_errors():
@@ -74,6 +89,13 @@ def test_quantize_argument_errors():
     assert q(P, -5, 1, P, P, P, None, None) == -2
     assert q(P + 4, 100, 1, P, P, P, None, None) == -3
     assert q(P, 100, 1, P + 8, P, P, None, None) == -3
+    qc = lib.qlora_quantize_codebook
+    assert qc(P, 100, 1, 2, P, P, P, None, None) == -4
+    assert qc(P, 100, 1, -1, P, P, P, None, None) == -4
+    assert qc(P, 100, 2, 1, P, P, P, None, None) == -4
+    assert qc(None, 100, 1, 1, P, P, P, None, None) == -1
+    assert qc(P, 0, 1, 1, P, P, P, None, None) == -2
+    assert qc(P, 100, 1, 1, P + 8, P, P, None, None) == -3
 
 
 def test_dequantize_argument_errors():
@@ -90,6 +112,8 @@ def test_dequantize_argument_errors():
     assert d(ctypes.byref(w), 0, P, None) == -2
     w = wstruct(dq=3)
     assert d(ctypes.byref(w), 0, P, None) == -4
+    w = wstruct(codebook=2)
+    assert d(ctypes.byref(w), 0, P, None) == -4
 
 
 def test_linear_argument_errors():
@@ -100,6 +124,7 @@ def test_linear_argument_errors():
     assert f(ctypes.byref(wstruct(n=64, k=100)), P, 4, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
     assert f(ctypes.byref(wstruct(n=60, k=128)), P, 4, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
     assert f(ctypes.byref(ok), P, 32, P, P, 200, 16.0, P, None, P, ws_need, None) == -4
+    assert f(ctypes.byref(wstruct(n=64, k=128, codebook=7)), P, 32, P, P, 8, 16.0, P, None, P, ws_need, None) == -4
     assert f(ctypes.byref(ok), P, 32, P, P, -1, 16.0, P, None, P, ws_need, None) == -2
     assert f(ctypes.byref(ok), P, -3, P, P, 8, 16.0, P, None, P, ws_need, None) == -2
     assert f(ctypes.byref(ok), None, 32, P, P, 8, 16.0, P, None, P, ws_need, None) == -1

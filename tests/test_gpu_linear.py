@@ -33,13 +33,13 @@ FWD_BWD_CASES = [
 ]
 
 
-def _run_case(gpu_lib, name, m, n, k, r, alpha, dq, check_bwd=True):
+def _run_case(gpu_lib, name, m, n, k, r, alpha, dq, check_bwd=True, codebook=0):
     import torch
 
     w, x, a, b, dy = layer_inputs(n, k, m, r, name)
-    q_ref, w16 = oracle_weight(w, dq)
-    say(f"[linear] case={name} m={m} n={n} k={k} r={r} dq={dq}")
-    q = gpu_lib.quantize(torch.from_numpy(w).cuda(), double_quant=dq)
+    q_ref, w16 = oracle_weight(w, dq, codebook)
+    say(f"[linear] case={name} m={m} n={n} k={k} r={r} dq={dq} codebook={codebook}")
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda(), double_quant=dq, codebook=codebook)
     xc, dyc = x.cuda(), dy.cuda()
     ac = a.cuda() if r else None
     bc = b.cuda() if r else None
@@ -76,6 +76,21 @@ def _run_case(gpu_lib, name, m, n, k, r, alpha, dq, check_bwd=True):
 @pytest.mark.parametrize("case", FWD_BWD_CASES, ids=[c[0] for c in FWD_BWD_CASES])
 def test_linear_parity(gpu_lib, case):
     _run_case(gpu_lib, *case)
+
+
+# Weights on the evenly spaced INT4 table: every path (GEMM, GEMV with H
+# inside, GEMV with H from the skinny kernel, no double quantization).
+INT4_CASES = [
+    ("int4_ragged_m300_n272_k320_r8", 300, 272, 320, 8, 16.0, True),
+    ("int4_decode_m1_r8", 1, 256, 256, 8, 16.0, True),
+    ("int4_decode_rank24_m8", 8, 128, 256, 24, 48.0, True),
+    ("int4_no_dq_m96", 96, 384, 448, 16, 32.0, False),
+]
+
+
+@pytest.mark.parametrize("case", INT4_CASES, ids=[c[0] for c in INT4_CASES])
+def test_linear_parity_int4(gpu_lib, case):
+    _run_case(gpu_lib, *case, codebook=1)
 
 
 @pytest.mark.parametrize("m", [1, 4, 16])

@@ -101,6 +101,54 @@ def test_quantize_dequantize_bit_exact(gpu_lib, name, dq):
     assert np.array_equal(d32.reshape(-1).cpu().numpy().view(np.uint32), w32_ref.view(np.uint32))
 
 
+INT4_CASES = ["single_256x256", "attn_4096x4096_outliers", "ragged_1d", "numel_3", "numel_65", "denormals", "zeros"]
+
+
+def _int4_ties_case():
+    """Values within a few ulp of every midpoint of the evenly spaced table."""
+    L = O.int4_levels()
+    a = np.float32(0.0371)
+    xs = []
+    for k in range(15):
+        v = np.float32((np.float64(L[k]) + np.float64(L[k + 1])) / 2)
+        for _ in range(4):
+            v = np.nextafter(v, np.float32(-2))
+        for _ in range(9):
+            xs.append(v)
+            v = np.nextafter(v, np.float32(2))
+    w = np.clip((np.array(xs, np.float64) * np.float64(a)).astype(np.float32), -a, a)
+    w = np.concatenate([w, np.zeros((-w.size) % 63, np.float32)]).reshape(-1, 63)
+    return np.concatenate([np.full((w.shape[0], 1), a, np.float32), w], axis=1).reshape(-1)
+
+
+@pytest.mark.parametrize("dq", [True, False])
+@pytest.mark.parametrize("name", INT4_CASES + ["int4_ties"])
+def test_int4_codebook_bit_exact(gpu_lib, name, dq):
+    """The evenly spaced codebook: same kernels with the other level table,
+    codes and dequantized values bit-equal to the oracle with that table."""
+    import torch
+
+    w = _int4_ties_case() if name == "int4_ties" else CASES[name]()
+    L = O.int4_levels()
+    say(f"[quantize int4] case={name} dq={dq} numel={w.size}")
+    ref = O.quantize(w.reshape(-1), dq, L)
+    q = gpu_lib.quantize(torch.from_numpy(np.ascontiguousarray(w)).cuda(), double_quant=dq, keep_absmax=True,
+                         codebook=gpu_lib.CODEBOOK_INT4)
+    torch.cuda.synchronize()
+    assert q.codebook == gpu_lib.CODEBOOK_INT4
+    assert np.array_equal(_u8(q.codes), ref["codes"])
+    assert np.array_equal(_f32bits(q.absmax), ref["absmax"].view(np.uint32))
+    if dq:
+        assert np.array_equal(_u8(q.scale_codes), ref["scale_codes"])
+        q.absmax = None
+    w32_ref, bits_ref = O.dequantize(ref, L)
+    d16 = gpu_lib.dequantize(q, torch.bfloat16)
+    d32 = gpu_lib.dequantize(q, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(d16.reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16), bits_ref)
+    assert np.array_equal(d32.reshape(-1).cpu().numpy().view(np.uint32), w32_ref.view(np.uint32))
+
+
 def test_dequantize_2d_non_multiple_of_64(gpu_lib):
     """Dequantize takes any n x k; blocks still follow the flattened order."""
     import torch

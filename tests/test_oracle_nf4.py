@@ -169,6 +169,36 @@ def test_encode_matches_exact_rational_argmin():
         assert codes[i] == exact_nearest(x, L), i
 
 
+def test_int4_levels_are_correctly_rounded_even_spacing():
+    """The evenly spaced table of the NF4-vs-INT4 example: level k is
+    -1 + 2k/15 rounded once to float32 (exact rationals), symmetric about 0,
+    with exact endpoints and no zero level."""
+    L = O.int4_levels()
+    assert L.dtype == np.float32 and L.size == 16
+    for k in range(16):
+        assert Fraction(float(L[k])) == round_fp32(Fraction(-1) + Fraction(2 * k, 15)), k
+        assert L[k] == -L[15 - k]
+    assert L[0] == -1.0 and L[15] == 1.0 and not np.any(L == 0)
+
+
+def test_int4_encode_matches_exact_rational_argmin():
+    """The encoder with the evenly spaced table, against exact rationals, on
+    values near every decision midpoint; x = 0 sits exactly between levels 7
+    and 8 and takes the low one."""
+    L = O.int4_levels()
+    rng = np.random.Generator(np.random.PCG64(17))
+    xs = np.concatenate([_near_midpoint_values(L, rng), np.zeros(1, np.float32)])
+    codes = O.encode_nearest(xs, L)
+    for i, x in enumerate(xs):
+        assert codes[i] == exact_nearest(Fraction(float(x)), L), i
+    assert codes[-1] == 7
+    # an all-zero block: code 7 everywhere, and L_7 * 0 decodes to -0.0
+    q = O.quantize(np.zeros(64, np.float32), True, L)
+    assert np.all(O.unpack_nibbles(q["codes"], 64) == 7)
+    w32, bits = O.dequantize(q, L)
+    assert np.all(w32 == 0) and np.all(np.signbit(w32)) and np.all(bits == 0x8000)
+
+
 def test_division_not_reciprocal_product():
     """Pick w where fl(w/a) and fl(w*fl(1/a)) differ and the difference moves
     the code; the oracle must follow the correctly rounded quotient."""
