@@ -57,7 +57,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run (train,gemm,copy,decode,dequant,quant,cpu)")
+    ap.add_argument("--only", default="", help="comma list of parts to run (train,gemm,copy,decode,dequant,quant,merge,cpu)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -352,6 +352,49 @@ def main():
             del ws_pool, w
             torch.cuda.empty_cache()
         parts["quantize_dq"] = qres
+
+    # ------------------------------------------- merge / unmerge / re-quantize
+    if want("merge"):
+        mres = []
+        for (n, k) in shapes:
+            lay = synth.DECODE_7B.layers[0 if n == 4096 else 1]
+            q = qn.quantize(torch.from_numpy(synth.weight(synth.DECODE_7B, lay)).to(dev))
+            a = torch.from_numpy(synth.lora_a(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
+            b = (torch.from_numpy(synth.lora_b(synth.DECODE_7B, lay)) + 0.01).to(torch.bfloat16).to(dev)
+            o16 = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+            o32 = torch.empty((n, k), dtype=torch.float32, device=dev)
+            packed = n * k * (0.5 + 1 / 64 + 1 / 4096)
+            calls = {
+                "merge_bf16": (lambda: qn.merge(q, a, b, 32.0, torch.bfloat16, out=o16), packed + 2 * n * k),
+                "merge_f32": (lambda: qn.merge(q, a, b, 32.0, torch.float32, out=o32), packed + 4 * n * k),
+                "unmerge_bf16_in_place": (lambda: qn.unmerge(o16, a, b, 32.0, out=o16), 4 * n * k),
+                "requantize_dq": (lambda: qn.requantize(q, a, b, 32.0), 2 * packed + 8 * n * k),
+            }
+            for name, (fn, byt) in calls.items():
+                fn()
+                torch.cuda.synchronize()
+                reps = 20
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=stream):
+                    for _ in range(reps):
+                        fn()
+                g.replay()
+                torch.cuda.synchronize()
+                e0, e1 = ev(), ev()
+                e0.record()
+                for _ in range(3):
+                    g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / (3 * reps)
+                gbs = byt / (us * 1e-6) / 1e9
+                mres.append({"op": name, "n": n, "k": k, "r": 16, "us_per_call": us, "bytes": byt, "GBps": gbs,
+                             "frac_hbm_peak": gbs / HBM_PEAK_GBS})
+                log(f"[bench] {name} {n}x{k} r=16: {us:.2f} us  {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+                del g
+            del q, o16, o32
+            torch.cuda.empty_cache()
+        parts["merge"] = mres
 
     # -------------------------------------------------------- CPU baseline
     cpu = None

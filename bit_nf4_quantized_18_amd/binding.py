@@ -25,7 +25,8 @@ STATUS = {0: "QLORA_OK", -1: "QLORA_ERR_NULL", -2: "QLORA_ERR_SHAPE", -3: "QLORA
 EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "qlora_linear_bwd",
            "qlora_linear_workspace_bytes", "qlora_linear_fwd_grouped", "qlora_linear_bwd_grouped",
            "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels",
-           "qlora_quantize_codebook", "qlora_codebook_levels")
+           "qlora_quantize_codebook", "qlora_codebook_levels", "qlora_merge", "qlora_unmerge",
+           "qlora_requantize")
 
 CODEBOOK_NF4 = 0   # normal-quantile levels
 CODEBOOK_INT4 = 1  # 16 evenly spaced levels on [-1, 1]
@@ -81,6 +82,12 @@ def load():
     lib.qlora_quantize_codebook.restype = i32
     lib.qlora_codebook_levels.argtypes = [i32, ctypes.POINTER(ctypes.c_float)]
     lib.qlora_codebook_levels.restype = i32
+    lib.qlora_merge.argtypes = [wp, vp, vp, i32, f32, i32, vp, vp]
+    lib.qlora_merge.restype = i32
+    lib.qlora_unmerge.argtypes = [vp, i32, i64, i64, vp, vp, i32, f32, vp, vp]
+    lib.qlora_unmerge.restype = i32
+    lib.qlora_requantize.argtypes = [wp, vp, vp, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp]
+    lib.qlora_requantize.restype = i32
     _LIB = lib
     return lib
 
@@ -186,6 +193,65 @@ def dequantize(q: PackedNF4, dtype=None):
     ws = q.c_struct()
     _check(load().qlora_nf4_dequantize(ctypes.byref(ws), code, _ptr(out), _stream()), "qlora_nf4_dequantize")
     return out
+
+
+def _adapter(a, b):
+    if a is None:
+        return 0, None, None
+    return a.shape[0], _ptr(a.contiguous()), _ptr(b.contiguous())
+
+
+def merge(q: PackedNF4, a, b, alpha: float, dtype=None, out=None):
+    """W16 + fl32(alpha/r) B A with the float32 order of qlora_merge.
+    a: bf16 (r, k), b: bf16 (n, r), or both None. Returns (n, k) of dtype."""
+    import torch
+
+    dtype = torch.bfloat16 if dtype is None else dtype
+    code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32}[dtype]
+    out = torch.empty((q.n, q.k), dtype=dtype, device=q.codes.device) if out is None else out
+    r, ap, bp = _adapter(a, b)
+    ws = q.c_struct()
+    _check(load().qlora_merge(ctypes.byref(ws), ap, bp, r, float(alpha), code, _ptr(out), _stream()), "qlora_merge")
+    return out
+
+
+def unmerge(merged, a, b, alpha: float, out=None):
+    """merged - fl32(alpha/r) B A (qlora_unmerge); merged: bf16 or float32
+    (n, k). ``out`` may be ``merged`` (in place)."""
+    import torch
+
+    code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32}[merged.dtype]
+    merged = merged.contiguous()
+    out = torch.empty_like(merged) if out is None else out
+    r, ap, bp = _adapter(a, b)
+    _check(load().qlora_unmerge(_ptr(merged), code, merged.shape[0], merged.shape[1], ap, bp, r, float(alpha),
+                                _ptr(out), _stream()), "qlora_unmerge")
+    return out
+
+
+def requantize(q: PackedNF4, a, b, alpha: float, double_quant: bool = True, codebook: int = CODEBOOK_NF4,
+               keep_absmax: bool = False):
+    """The merged weight quantized again (qlora_requantize). Returns
+    (PackedNF4 of the merged weight, merged float32 (n, k))."""
+    import torch
+
+    dev = q.codes.device
+    numel = q.n * q.k
+    nb = -(-numel // BLOCK)
+    ng = -(-nb // DQ_GROUP)
+    merged = torch.empty((q.n, q.k), dtype=torch.float32, device=dev)
+    codes = _empty((numel + 1) // 2, torch.uint8, dev)
+    sc = _empty(nb, torch.uint8, dev) if double_quant else None
+    gs = _empty(ng, torch.float32, dev) if double_quant else None
+    am = _empty(nb, torch.float32, dev) if (keep_absmax or not double_quant) else None
+    r, ap, bp = _adapter(a, b)
+    ws = q.c_struct()
+    _check(load().qlora_requantize(ctypes.byref(ws), ap, bp, r, float(alpha), int(double_quant), int(codebook),
+                                   _ptr(merged), _ptr(codes), _ptr(sc), _ptr(gs), _ptr(am), _stream()),
+           "qlora_requantize")
+    packed = PackedNF4(q.n, q.k, codes[: (numel + 1) // 2], double_quant, None if sc is None else sc[:nb],
+                       None if gs is None else gs[:ng], None if am is None else am[:nb], int(codebook))
+    return packed, merged
 
 
 def _workspace(m, n, k, r, device):

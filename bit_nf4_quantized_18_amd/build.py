@@ -21,14 +21,16 @@ HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
 # Packed-fp32 instructions are kept out of every device build; the quantizer
-# unit is also built without floating-point contraction because its outputs
-# (codes, scale codes, dequantized values) are bit-exact.
+# and merge units are also built without floating-point contraction because
+# their outputs (codes, scale codes, dequantized and merged values) are
+# bit-exact.
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc", "-munsafe-fp-atomics"]
 SOURCES = {
     "codebook.cpp": ["-ffp-contract=off"],
     "api.cpp": [],
     "quant_kernels.hip": DEVICE + ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt"],
+    "merge_kernels.hip": DEVICE + ["-ffp-contract=off"],
     "lora_kernels.hip": DEVICE,
     "gemv_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
     "gemm_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],

@@ -381,4 +381,62 @@ qlora_status qlora_linear_bwd_grouped(const qlora_nf4_weight* w, int g, const in
   return linear_bwd_impl(w, &lp, x, dy, m, a, b, g * r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream);
 }
 
+
+// Adapter arguments of the merge calls: r in 0..QLORA_MAX_RANK; for r > 0,
+// a (r x k) and b (n x r) are required and 16-byte aligned.
+static qlora_status check_adapter(const uint16_t* a, const uint16_t* b, int r) {
+  if (r < 0) return QLORA_ERR_SHAPE;
+  if (r > QLORA_MAX_RANK) return QLORA_ERR_UNSUPPORTED;
+  if (r > 0 && (a == nullptr || b == nullptr)) return QLORA_ERR_NULL;
+  if (r > 0 && (!aligned16(a) || !aligned16(b))) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+qlora_status qlora_merge(const qlora_nf4_weight* w, const uint16_t* a, const uint16_t* b, int r, float alpha,
+                         qlora_dtype out_dtype, void* out, hipStream_t stream) {
+  qlora_status st = check_weight(w, false);
+  if (st != QLORA_OK) return st;
+  if (w->k % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if (out_dtype != QLORA_BF16 && out_dtype != QLORA_F32) return QLORA_ERR_UNSUPPORTED;
+  if ((st = check_adapter(a, b, r)) != QLORA_OK) return st;
+  if (out == nullptr) return QLORA_ERR_NULL;
+  if (!aligned16(out)) return QLORA_ERR_ALIGN;
+  const float s = (r == 0) ? 0.0f : alpha / static_cast<float>(r);
+  return hip_status(qlora::launch_merge(view(w), a, b, r, s, out_dtype == QLORA_F32, out, stream));
+}
+
+qlora_status qlora_unmerge(const void* merged, qlora_dtype dtype, int64_t n, int64_t k, const uint16_t* a,
+                           const uint16_t* b, int r, float alpha, void* out, hipStream_t stream) {
+  if (dtype != QLORA_BF16 && dtype != QLORA_F32) return QLORA_ERR_UNSUPPORTED;
+  if (n < 1 || k < 1 || k % 8 != 0 || n > (INT64_C(1) << 40) / k) return QLORA_ERR_SHAPE;
+  qlora_status st = check_adapter(a, b, r);
+  if (st != QLORA_OK) return st;
+  if (merged == nullptr || out == nullptr) return QLORA_ERR_NULL;
+  if (!aligned16(merged) || !aligned16(out)) return QLORA_ERR_ALIGN;
+  const float s = (r == 0) ? 0.0f : alpha / static_cast<float>(r);
+  return hip_status(qlora::launch_unmerge(merged, dtype == QLORA_F32, n, k, a, b, r, s, out, stream));
+}
+
+qlora_status qlora_requantize(const qlora_nf4_weight* w, const uint16_t* a, const uint16_t* b, int r, float alpha,
+                              int double_quant, int codebook, float* merged, uint8_t* codes, uint8_t* scale_codes,
+                              float* group_scale, float* absmax, hipStream_t stream) {
+  qlora_status st = check_weight(w, false);
+  if (st != QLORA_OK) return st;
+  if (w->k % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
+  if ((st = check_adapter(a, b, r)) != QLORA_OK) return st;
+  if (double_quant != 0 && double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_INT4) return QLORA_ERR_UNSUPPORTED;
+  if (merged == nullptr || codes == nullptr) return QLORA_ERR_NULL;
+  if (double_quant && (scale_codes == nullptr || group_scale == nullptr)) return QLORA_ERR_NULL;
+  if (!double_quant && absmax == nullptr) return QLORA_ERR_NULL;
+  if (!aligned16(merged) || !aligned16(codes)) return QLORA_ERR_ALIGN;
+  if (double_quant && (!aligned16(scale_codes) || !aligned16(group_scale))) return QLORA_ERR_ALIGN;
+  if (absmax != nullptr && !aligned16(absmax)) return QLORA_ERR_ALIGN;
+  const float s = (r == 0) ? 0.0f : alpha / static_cast<float>(r);
+  QLORA_TRY(qlora::launch_merge(view(w), a, b, r, s, 1, merged, stream));
+  return hip_status(qlora::launch_quantize(merged, w->n * w->k, double_quant, codebook, codes,
+                                           double_quant ? scale_codes : nullptr, double_quant ? group_scale : nullptr,
+                                           absmax, stream));
+}
+
 }  // extern "C"

@@ -106,6 +106,16 @@ hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int6
 
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
+// Merge: out (w.n x w.k, float32 if out_f32 else bf16) = w16 + t with
+// t = fl32(s d), d the float32 sum over ascending j of b[p][j] a[j][q]
+// (a r x k, b n x r bf16). Unmerge: out = merged - t for a dense merged
+// weight (float32 if src_f32, else bf16; out of the same type, may alias).
+// k % 64 == 0 for merge, k % 8 == 0 for unmerge; r = 0 gives t = 0.
+hipError_t launch_merge(const PackedW& w, const uint16_t* a, const uint16_t* b, int r, float s, int out_f32,
+                        void* out, hipStream_t st);
+hipError_t launch_unmerge(const void* merged, int src_f32, int64_t n, int64_t k, const uint16_t* a,
+                          const uint16_t* b, int r, float s, void* out, hipStream_t st);
+
 int rank_reduce_splits(int64_t m, int64_t n, int64_t k, int r);
 
 // Both adapter gradients in two launches when rank_grads_fused(r)

@@ -226,6 +226,50 @@ qlora_status qlora_linear_bwd_grouped(const qlora_nf4_weight* w, int g, const in
  * sizes. Host only, no GPU use. */
 size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int g, int r);
 
+/* Merge a trained adapter into the weight: out (n x k, row-major) =
+ * fl32(W16 + t), where W16 is the bf16 dequantized weight (as
+ * qlora_nf4_dequantize), t = fl32(s d), s = fl32(alpha / r), and d is the
+ * float32 sum of b[p][j] a[j][q] over j = 0 .. r-1 in that order (each step
+ * one float32 addition; bf16 products are exact). "LoRA y QLoRA en
+ * Profundidad", "La Idea Central" (W + (alpha/r) B A for inference);
+ * Ultralytics glossary "QLoRA", "Compromessi" (merging starts from the
+ * weight dequantized to 16 bit).
+ *   w         : packed weight, k % 64 == 0 (any codebook, DQ on or off).
+ *   a, b      : bf16 A (r x k) and B (n x r); may be NULL when r = 0.
+ *   r         : 0 .. QLORA_MAX_RANK; r = 0 gives out = W16.
+ *   out_dtype : QLORA_F32 writes the float32 value, QLORA_BF16 its
+ *               round-to-nearest-even bf16 (the 16-bit model).
+ *   out       : n x k, caller-allocated.
+ * Bit-exact with the CPU oracle. Errors: NULL / ALIGN / SHAPE (k % 64 != 0,
+ * r < 0) / UNSUPPORTED (r > QLORA_MAX_RANK, dtype, codebook, flag) / HIP. */
+qlora_status qlora_merge(const qlora_nf4_weight* w, const uint16_t* a, const uint16_t* b, int r,
+                         float alpha, qlora_dtype out_dtype, void* out, hipStream_t stream);
+
+/* Take an adapter back out of a merged weight (adapters are stored and
+ * swapped per task: Ultralytics glossary "QLoRA", "Compromessi"):
+ * out = fl32(W' - t) with t as in qlora_merge.
+ *   merged : W', n x k, bf16 (dtype QLORA_BF16) or float32 (QLORA_F32).
+ *   out    : n x k of the same dtype (bf16: round-to-nearest-even); may be
+ *            `merged` itself (in place).
+ *   n >= 1, k % 8 == 0. a, b, r, alpha as in qlora_merge.
+ * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED / HIP. */
+qlora_status qlora_unmerge(const void* merged, qlora_dtype dtype, int64_t n, int64_t k,
+                           const uint16_t* a, const uint16_t* b, int r, float alpha, void* out,
+                           hipStream_t stream);
+
+/* Re-quantize a merged model for distribution (Ultralytics glossary
+ * "QLoRA", "QLoRA e metodi correlati": the merged 16-bit weights are
+ * quantized again). Two launches on `stream`: `merged` (n x k float32,
+ * caller-allocated) receives qlora_merge's float32 output, then the packed
+ * outputs receive qlora_quantize_codebook(merged, n k, double_quant,
+ * codebook, ...), with the same buffer sizes and NULL rules. The new weight
+ * may use another codebook or DQ mode than `w`.
+ * Errors: as qlora_merge and qlora_quantize_codebook. */
+qlora_status qlora_requantize(const qlora_nf4_weight* w, const uint16_t* a, const uint16_t* b, int r,
+                              float alpha, int double_quant, int codebook, float* merged,
+                              uint8_t* codes, uint8_t* scale_codes, float* group_scale,
+                              float* absmax, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status. Host only. */
 const char* qlora_status_string(qlora_status status);
 

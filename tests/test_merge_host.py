@@ -1,0 +1,53 @@
+"""Host-side argument checks of the merge entry points: every call below
+fails validation before anything is launched (the pointers are placeholders
+and are never dereferenced)."""
+import ctypes
+
+from bit_nf4_quantized_18_amd import binding
+
+P = 1 << 20
+
+
+def wstruct(n=64, k=128, dq=1, codebook=0):
+    return binding.NF4WeightC(n, k, P, P, P, None, dq, codebook)
+
+
+def test_merge_argument_errors():
+    f = binding.load().qlora_merge
+    w = ctypes.byref(wstruct())
+    assert f(w, P, P, 8, 16.0, 7, P, None) == -4           # dtype
+    assert f(w, P, P, 200, 16.0, 0, P, None) == -4         # rank above the maximum
+    assert f(w, P, P, -1, 16.0, 0, P, None) == -2
+    assert f(w, None, P, 8, 16.0, 0, P, None) == -1
+    assert f(w, P, None, 8, 16.0, 0, P, None) == -1
+    assert f(w, P + 2, P, 8, 16.0, 0, P, None) == -3
+    assert f(w, P, P, 8, 16.0, 0, None, None) == -1
+    assert f(w, P, P, 8, 16.0, 0, P + 4, None) == -3
+    assert f(ctypes.byref(wstruct(k=100)), P, P, 8, 16.0, 0, P, None) == -2  # k % 64
+    assert f(ctypes.byref(wstruct(codebook=3)), P, P, 8, 16.0, 0, P, None) == -4
+    assert f(ctypes.byref(wstruct(dq=2)), P, P, 8, 16.0, 0, P, None) == -4
+    assert f(None, P, P, 8, 16.0, 0, P, None) == -1
+
+
+def test_unmerge_argument_errors():
+    f = binding.load().qlora_unmerge
+    assert f(P, 5, 64, 128, P, P, 8, 16.0, P, None) == -4
+    assert f(P, 0, 0, 128, P, P, 8, 16.0, P, None) == -2
+    assert f(P, 0, 64, 100, P, P, 8, 16.0, P, None) == -2  # k % 8
+    assert f(P, 0, 64, 128, P, P, 129, 16.0, P, None) == -4
+    assert f(None, 0, 64, 128, P, P, 8, 16.0, P, None) == -1
+    assert f(P, 0, 64, 128, P, P, 8, 16.0, None, None) == -1
+    assert f(P, 1, 64, 128, P, P, 8, 16.0, P + 8, None) == -3
+    assert f(P, 1, 64, 128, None, P, 8, 16.0, P, None) == -1
+
+
+def test_requantize_argument_errors():
+    f = binding.load().qlora_requantize
+    w = ctypes.byref(wstruct())
+    assert f(w, P, P, 8, 16.0, 2, 0, P, P, P, P, None, None) == -4   # dq flag
+    assert f(w, P, P, 8, 16.0, 1, 4, P, P, P, P, None, None) == -4   # codebook
+    assert f(w, P, P, 8, 16.0, 1, 0, None, P, P, P, None, None) == -1
+    assert f(w, P, P, 8, 16.0, 1, 0, P, P, None, P, None, None) == -1
+    assert f(w, P, P, 8, 16.0, 0, 0, P, P, None, None, None, None) == -1  # no absmax without DQ
+    assert f(w, P, P, 8, 16.0, 1, 0, P + 4, P, P, P, None, None) == -3
+    assert f(ctypes.byref(wstruct(k=96)), P, P, 8, 16.0, 1, 0, P, P, P, P, None, None) == -2
