@@ -57,7 +57,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run (train,gemm,copy,decode,dequant,quant,merge,cpu)")
+    ap.add_argument("--only", default="", help="comma list of parts to run (train,dropout,gemm,copy,decode,dequant,quant,merge,cpu)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -189,6 +189,28 @@ def main():
         parts["train_step_per_linear"] = time_step(train_step, "training step, one call per linear")
         parts["train_step"] = time_step(train_step_grouped, "training step (q/k/v and gate/up grouped)")
         ms_step, value = parts["train_step"]["ms_per_step"], parts["train_step"]["tflops"]
+
+    # Training step with adapter dropout (p = 0.05, one keep mask per linear):
+    # the same algorithmic flops plus the masked copy of X and the masked dX
+    # update; every linear as its own call.
+    if want("dropout"):
+        p_drop = 0.05
+        for L in layers:
+            lay = L["lay"]
+            L["keep"] = torch.from_numpy(synth.keep_mask((M, lay.k), p_drop, wl.name, lay.name, "keep")).to(dev)
+            L["wsd"] = torch.empty(qn.dropout_workspace_bytes(M, lay.n, lay.k, R), dtype=torch.uint8, device=dev)
+
+        def train_step_dropout():
+            for L in layers:
+                qn.linear_fwd_dropout(L["q"], L["x"], L["a"], L["b"], ALPHA, L["keep"], p_drop, out=L["y"],
+                                      h_out=L["h"], ws=L["wsd"])
+                qn.linear_bwd_dropout(L["q"], L["x"], L["dy"], L["a"], L["b"], ALPHA, L["keep"], p_drop, h=L["h"],
+                                      dx=L["dx"], da=L["da"], db=L["db"], ws=L["wsd"])
+
+        parts["train_step_dropout"] = time_step(train_step_dropout, "training step with adapter dropout p=0.05")
+        parts["train_step_dropout"]["p"] = p_drop
+        for L in layers:
+            del L["keep"], L["wsd"]
 
     # ------------------------------------------- fused dequant-GEMM kernels
     roofline = None

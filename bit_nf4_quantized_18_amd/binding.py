@@ -26,7 +26,8 @@ EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "ql
            "qlora_linear_workspace_bytes", "qlora_linear_fwd_grouped", "qlora_linear_bwd_grouped",
            "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels",
            "qlora_quantize_codebook", "qlora_codebook_levels", "qlora_merge", "qlora_unmerge",
-           "qlora_requantize")
+           "qlora_requantize", "qlora_linear_dropout_workspace_bytes", "qlora_linear_fwd_dropout",
+           "qlora_linear_bwd_dropout")
 
 CODEBOOK_NF4 = 0   # normal-quantile levels
 CODEBOOK_INT4 = 1  # 16 evenly spaced levels on [-1, 1]
@@ -88,6 +89,12 @@ def load():
     lib.qlora_unmerge.restype = i32
     lib.qlora_requantize.argtypes = [wp, vp, vp, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp]
     lib.qlora_requantize.restype = i32
+    lib.qlora_linear_dropout_workspace_bytes.argtypes = [i64, i64, i64, i32]
+    lib.qlora_linear_dropout_workspace_bytes.restype = sz
+    lib.qlora_linear_fwd_dropout.argtypes = [wp, vp, i64, vp, vp, i32, f32, vp, f32, vp, vp, vp, sz, vp]
+    lib.qlora_linear_fwd_dropout.restype = i32
+    lib.qlora_linear_bwd_dropout.argtypes = [wp, vp, vp, i64, vp, vp, i32, f32, vp, f32, vp, vp, vp, vp, vp, sz, vp]
+    lib.qlora_linear_bwd_dropout.restype = i32
     _LIB = lib
     return lib
 
@@ -307,6 +314,55 @@ def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, 
     st = load().qlora_linear_bwd(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(h),
                                  _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes, _stream())
     _check(st, "qlora_linear_bwd")
+    return dx, da, db
+
+
+def dropout_workspace_bytes(m: int, n: int, k: int, r: int) -> int:
+    return int(load().qlora_linear_dropout_workspace_bytes(m, n, k, r))
+
+
+def _drop_ws(ws, m, n, k, r, dev):
+    import torch
+
+    if ws is not None:
+        return ws, ws.numel()
+    nbytes = dropout_workspace_bytes(m, n, k, r)
+    return (torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None), nbytes
+
+
+def linear_fwd_dropout(q: PackedNF4, x, a, b, alpha: float, keep, p: float, want_h: bool = True, out=None,
+                       h_out=None, ws=None):
+    """qlora_linear_fwd_dropout. keep: uint8 (m, k) on the GPU, non-zero =
+    kept; p: drop probability. Returns (y, h) with h from the dropped input."""
+    import torch
+
+    m, r, dev = x.shape[0], a.shape[0], x.device
+    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=dev)
+    h = h_out if h_out is not None else (torch.empty((m, r), dtype=torch.float32, device=dev) if want_h else None)
+    ws, nbytes = _drop_ws(ws, m, q.n, q.k, r, dev)
+    wc = q.c_struct()
+    st = load().qlora_linear_fwd_dropout(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
+                                         _ptr(keep), float(p), _ptr(y), _ptr(h), _ptr(ws), nbytes, _stream())
+    _check(st, "qlora_linear_fwd_dropout")
+    return y, h
+
+
+def linear_bwd_dropout(q: PackedNF4, x, dy, a, b, alpha: float, keep, p: float, h=None, need_dx: bool = True,
+                       dx=None, da=None, db=None, ws=None):
+    """qlora_linear_bwd_dropout with the forward's mask. Returns (dx, dA, dB)."""
+    import torch
+
+    m, r, dev = dy.shape[0], a.shape[0], dy.device
+    if dx is None and need_dx:
+        dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev)
+    da = torch.empty((r, q.k), dtype=torch.float32, device=dev) if da is None else da
+    db = torch.empty((q.n, r), dtype=torch.float32, device=dev) if db is None else db
+    ws, nbytes = _drop_ws(ws, m, q.n, q.k, r, dev)
+    wc = q.c_struct()
+    st = load().qlora_linear_bwd_dropout(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha),
+                                         _ptr(keep), float(p), _ptr(h), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
+                                         nbytes, _stream())
+    _check(st, "qlora_linear_bwd_dropout")
     return dx, da, db
 
 

@@ -32,6 +32,7 @@ SOURCES = {
     "quant_kernels.hip": DEVICE + ["-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt"],
     "merge_kernels.hip": DEVICE + ["-ffp-contract=off"],
     "lora_kernels.hip": DEVICE,
+    "dropout_kernels.hip": DEVICE,
     "gemv_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
     "gemm_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
 }

@@ -75,6 +75,21 @@ BwdLayout bwd_layout(int64_t m, int64_t n, int64_t k, int r, int rpart) {
   return L;
 }
 
+// Dropout calls: the masked copy of X first, then the forward's (GEMM path)
+// or the backward's buffers.
+int64_t drop_xm_bytes(int64_t m, int64_t k) { return round_up(m * k * 2, kAlign); }
+int64_t drop_total(int64_t m, int64_t n, int64_t k, int r) {
+  const int64_t f = fwd_layout(m, n, k, r, true).total;
+  const int64_t b = bwd_layout(m, n, k, r, r).total;
+  return drop_xm_bytes(m, k) + (f > b ? f : b);
+}
+
+// Adapter dropout: keep mask (m x k bytes, non-zero = kept) and 1 / (1 - p).
+struct DropArg {
+  const uint8_t* keep;
+  float inv_keep;
+};
+
 qlora_status check_weight(const qlora_nf4_weight* w, bool linear) {
   if (w == nullptr || w->codes == nullptr) return QLORA_ERR_NULL;
   if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_UNSUPPORTED;
@@ -198,7 +213,8 @@ namespace {
 // part) with r adapter slots in total, rpart per part, s = alpha / rpart.
 qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x, int64_t m,
                              const uint16_t* a, const uint16_t* b, int r, int rpart, float alpha, uint16_t* y,
-                             float* h_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                             float* h_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                             const DropArg* drop = nullptr) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
@@ -213,18 +229,29 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
   if (h_out != nullptr && !aligned16(h_out)) return QLORA_ERR_ALIGN;
   const int64_t n = w->n, k = w->k;
   const bool grouped = grp != nullptr;
-  const size_t need = grouped ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
-                              : qlora_linear_workspace_bytes(m, n, k, r);
+  if (drop != nullptr && r == 0) drop = nullptr;  // no adapter, nothing to drop
+  const size_t need = drop != nullptr ? static_cast<size_t>(drop_total(m, n, k, r))
+                      : grouped       ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
+                                      : qlora_linear_workspace_bytes(m, n, k, r);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
 
-  const FwdLayout L = fwd_layout(m, n, k, r, grouped);
+  // with dropout: the GEMM path for every m, after the masked copy of X
+  const bool gemm_path = grouped || drop != nullptr;
+  const FwdLayout L = fwd_layout(m, n, k, r, gemm_path);
   char* base = static_cast<char*>(ws);
+  const uint16_t* xa = x;  // the adapter's input
+  if (drop != nullptr) {
+    uint16_t* xm = reinterpret_cast<uint16_t*>(base);
+    QLORA_TRY(qlora::launch_mask_input(x, drop->keep, m * k, xm, stream));
+    xa = xm;
+    base += drop_xm_bytes(m, k);
+  }
   const float s = (rpart == 0) ? 0.0f : alpha / static_cast<float>(rpart);
   const int rp = rank_pad(r);
   const PackedW pw = view(w);
 
-  if (m <= kGemvMaxM && !grouped) {
+  if (m <= kGemvMaxM && !gemm_path) {
     // One launch when the GEMV computes H itself; otherwise H as per-split
     // partial sums in the workspace, which the GEMV sums.
     float* hpart = nullptr;
@@ -238,9 +265,11 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     float* h32 = (r == 0) ? nullptr : (h_out != nullptr ? h_out : reinterpret_cast<float*>(base + L.h32));
     uint16_t* hs = (r == 0) ? nullptr : reinterpret_cast<uint16_t*>(base + L.hs);
     // H of every part at once: the parts' A matrices are stacked (r x k)
+    // H = D(X) A^T = (X * keep) A^T / (1 - p) under dropout
+    const float hscale = drop != nullptr ? drop->inv_keep : 1.0f;
     if (r > 0)
-      QLORA_TRY(qlora::launch_skinny_prefill(x, a, m, k, r, rp, 1.0f, s, reinterpret_cast<float*>(base + L.part), h32,
-                                             hs, stream));
+      QLORA_TRY(qlora::launch_skinny_prefill(xa, a, m, k, r, rp, hscale, s, reinterpret_cast<float*>(base + L.part),
+                                             h32, hs, stream));
     qlora::LoraParts one;
     one.g = 1;
     one.rpart = rpart;
@@ -253,7 +282,7 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
 qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x,
                              const uint16_t* dy, int64_t m, const uint16_t* a, const uint16_t* b, int r, int rpart,
                              float alpha, const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
-                             size_t ws_bytes, hipStream_t stream) {
+                             size_t ws_bytes, hipStream_t stream, const DropArg* drop = nullptr) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
@@ -278,13 +307,22 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
   if (dx == nullptr && r == 0) return QLORA_OK;  // nothing requested
   if (!aligned16(dy) || (x != nullptr && !aligned16(x)) || (dx != nullptr && !aligned16(dx))) return QLORA_ERR_ALIGN;
   if (h_saved != nullptr && !aligned16(h_saved)) return QLORA_ERR_ALIGN;
-  const size_t need = grouped ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
-                              : qlora_linear_workspace_bytes(m, n, k, r);
+  if (drop != nullptr && r == 0) drop = nullptr;  // no adapter, nothing to drop
+  const size_t need = drop != nullptr ? static_cast<size_t>(drop_total(m, n, k, r))
+                      : grouped       ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
+                                      : qlora_linear_workspace_bytes(m, n, k, r);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
 
   const BwdLayout L = bwd_layout(m, n, k, r, rpart);
   char* base = static_cast<char*>(ws);
+  const uint16_t* xa = x;  // the adapter's input
+  if (drop != nullptr) {
+    uint16_t* xm = reinterpret_cast<uint16_t*>(base);
+    QLORA_TRY(qlora::launch_mask_input(x, drop->keep, m * k, xm, stream));
+    xa = xm;
+    base += drop_xm_bytes(m, k);
+  }
   const float s = (rpart == 0) ? 0.0f : alpha / static_cast<float>(rpart);
   const int rp = rank_pad(r);
   const PackedW pw = view(w);
@@ -299,30 +337,45 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     float* part = reinterpret_cast<float*>(base + L.part);
     float* spart = reinterpret_cast<float*>(base + L.spart);
     const float* h = h_saved;
+    const float inv_keep = drop != nullptr ? drop->inv_keep : 1.0f;
     if (h == nullptr) {
       float* h32 = reinterpret_cast<float*>(base + L.h32);
-      QLORA_TRY(qlora::launch_skinny_prefill(x, a, m, k, r, rp, 1.0f, 1.0f, spart, h32, nullptr, stream));
+      QLORA_TRY(qlora::launch_skinny_prefill(xa, a, m, k, r, rp, inv_keep, 1.0f, spart, h32, nullptr, stream));
       h = h32;
     }
     // A^T, and B^T (block diagonal for grouped weights: part l's slots see
     // only its own output columns)
     QLORA_TRY(qlora::launch_lora_transpose(a, b, n, k, r, rp, at, bt, stream, grp));
-    // dH = s dY B  (contraction over n, with B^T as the r x n operand)
-    QLORA_TRY(qlora::launch_skinny_prefill(dy, bt, m, n, r, rp, s, 1.0f, spart, dh32, dhs, stream));
+    // dH = s dY B  (contraction over n, with B^T as the r x n operand).
+    // Under dropout dh32 holds dH / (1 - p), the factor both dA and the
+    // masked dX update need; the frozen-weight GEMM then runs without
+    // adapter slots.
+    if (drop != nullptr) dhs = nullptr;
+    QLORA_TRY(qlora::launch_skinny_prefill(dy, bt, m, n, r, rp, drop != nullptr ? s * inv_keep : s, 1.0f, spart, dh32,
+                                           dhs, stream));
     if (qlora::rank_grads_fused(r) && qlora::rank_grads_fused(rpart)) {
       // dA = dH^T X (r x k) and dB = s dY^T H (n x rpart) in one pass each
-      QLORA_TRY(qlora::launch_rank_grads(dh32, x, k, h, dy, n, m, r, grp, s,
+      QLORA_TRY(qlora::launch_rank_grads(dh32, xa, k, h, dy, n, m, r, grp, s,
                                          qlora::rank_grad_splits(m, n, k, r, rpart), part, da, db, stream));
     } else {
       if (grouped) return QLORA_ERR_UNSUPPORTED;  // checked by the caller
       const int splits = qlora::rank_reduce_splits(m, n, k, r);
       // dA = dH^T X  (r x k)
-      QLORA_TRY(qlora::launch_rank_reduce(dh32, x, m, k, r, 1.0f, splits, part, da, 0, stream));
+      QLORA_TRY(qlora::launch_rank_reduce(dh32, xa, m, k, r, 1.0f, splits, part, da, 0, stream));
       // dB = s dY^T H  (n x r)
       QLORA_TRY(qlora::launch_rank_reduce(h, dy, m, n, r, s, splits, part, db, 1, stream));
     }
   }
-  if (dx != nullptr) QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream));
+  if (dx != nullptr) {
+    if (drop != nullptr) {
+      // dX = dY W16, then + (dH A) / (1 - p) where the input was kept
+      QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, nullptr, nullptr, 0, dx, stream));
+      QLORA_TRY(qlora::launch_masked_lora_add(dx, drop->keep, reinterpret_cast<const float*>(base + L.dh32), a, m, k,
+                                              r, stream));
+    } else {
+      QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream));
+    }
+  }
   return QLORA_OK;
 }
 
@@ -437,6 +490,44 @@ qlora_status qlora_requantize(const qlora_nf4_weight* w, const uint16_t* a, cons
   return hip_status(qlora::launch_quantize(merged, w->n * w->k, double_quant, codebook, codes,
                                            double_quant ? scale_codes : nullptr, double_quant ? group_scale : nullptr,
                                            absmax, stream));
+}
+
+// Dropout probability p in [0, 1) (NaN fails the test) and the keep mask.
+static qlora_status make_drop(const uint8_t* keep, float p, DropArg* out) {
+  if (!(p >= 0.0f && p < 1.0f)) return QLORA_ERR_UNSUPPORTED;
+  if (keep == nullptr) return QLORA_ERR_NULL;
+  if (!aligned16(keep)) return QLORA_ERR_ALIGN;
+  out->keep = keep;
+  out->inv_keep = static_cast<float>(1.0 / (1.0 - static_cast<double>(p)));
+  return QLORA_OK;
+}
+
+size_t qlora_linear_dropout_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
+  if (m <= 0 || n <= 0 || k <= 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (r == 0) return qlora_linear_workspace_bytes(m, n, k, r);
+  return static_cast<size_t>(drop_total(m, n, k, r));
+}
+
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                                      const uint16_t* b, int r, float alpha, const uint8_t* keep, float p,
+                                      uint16_t* y, float* h_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (m == 0) return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, ws, ws_bytes, stream);
+  DropArg d{};
+  const qlora_status st = make_drop(keep, p, &d);
+  if (st != QLORA_OK) return st;
+  return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, ws, ws_bytes, stream, &d);
+}
+
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t m,
+                                      const uint16_t* a, const uint16_t* b, int r, float alpha, const uint8_t* keep,
+                                      float p, const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  if (m == 0)
+    return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream);
+  DropArg d{};
+  const qlora_status st = make_drop(keep, p, &d);
+  if (st != QLORA_OK) return st;
+  return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream, &d);
 }
 
 }  // extern "C"

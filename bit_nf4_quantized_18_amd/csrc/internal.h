@@ -113,6 +113,13 @@ hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 // k % 64 == 0 for merge, k % 8 == 0 for unmerge; r = 0 gives t = 0.
 hipError_t launch_merge(const PackedW& w, const uint16_t* a, const uint16_t* b, int r, float s, int out_f32,
                         void* out, hipStream_t st);
+// Adapter dropout: xm = x where keep != 0, else +0 (count = m k, a multiple
+// of 8); dx += keep ? dh a : 0 per element, dh float32 m x r, a bf16 r x k,
+// k % 64 == 0, dx rounded to bf16 once.
+hipError_t launch_mask_input(const uint16_t* x, const uint8_t* keep, int64_t count, uint16_t* xm, hipStream_t st);
+hipError_t launch_masked_lora_add(uint16_t* dx, const uint8_t* keep, const float* dh, const uint16_t* a, int64_t m,
+                                  int64_t k, int r, hipStream_t st);
+
 hipError_t launch_unmerge(const void* merged, int src_f32, int64_t n, int64_t k, const uint16_t* a,
                           const uint16_t* b, int r, float s, void* out, hipStream_t st);
 

@@ -182,6 +182,34 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
                               const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
                               size_t ws_bytes, hipStream_t stream);
 
+/* Forward and backward with dropout on the adapter path ("LoRA y QLoRA en
+ * Profundidad", "Dropout (lora_dropout)": the LoRA layers randomly zero
+ * elements during training). The adapter's input is dropped, the frozen
+ * path is not:
+ *   D(X) = X * keep / (1 - p),   H = D(X) A^T,   Y = X W16^T + s H B^T;
+ *   dH = s dY B,   dX = dY W16 + (dH A) * keep / (1 - p),
+ *   dA = dH^T D(X),   dB = s dY^T H.
+ *   keep : m x k bytes, row-major, 16-byte aligned; non-zero = element kept.
+ *          The caller draws it (Bernoulli(1 - p) per element) and passes
+ *          the same mask to both calls of a step.
+ *   p    : drop probability, 0 <= p < 1 (the factor is fl32(1 / (1 - p))).
+ *   h_out / h_saved : H from the dropped input, as above.
+ *   ws   : at least qlora_linear_dropout_workspace_bytes(m, n, k, r).
+ * Every other argument, layout and limit is as in qlora_linear_fwd /
+ * qlora_linear_bwd; every m takes the matmul path. r = 0 is the plain call.
+ * Errors: as those calls, plus NULL (keep), ALIGN (keep) and UNSUPPORTED
+ * (p outside [0, 1)). */
+size_t qlora_linear_dropout_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, int64_t m,
+                                      const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                      const uint8_t* keep, float p, uint16_t* y, float* h_out,
+                                      void* ws, size_t ws_bytes, hipStream_t stream);
+qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t* x,
+                                      const uint16_t* dy, int64_t m, const uint16_t* a,
+                                      const uint16_t* b, int r, float alpha, const uint8_t* keep,
+                                      float p, const float* h_saved, uint16_t* dx, float* da,
+                                      float* db, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of device workspace that qlora_linear_fwd and qlora_linear_bwd need
  * for these sizes (the larger of the two); 0 if none. Host only, no GPU use. */
 size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);

@@ -18,7 +18,9 @@ Distributions follow the workloads the pages describe:
   * LoRA A Gaussian and B at zero at init ("LoRA y QLoRA en Profundidad",
     section "Inicializacion"); for parity we draw B small but non-zero so the
     adapter path is exercised, and test B = 0 separately;
-  * a heavy-tailed Student-t(4) variant for the 65B-shaped set.
+  * a heavy-tailed Student-t(4) variant for the 65B-shaped set;
+  * Bernoulli keep masks for adapter dropout ("LoRA y QLoRA en Profundidad",
+    section "Dropout (lora_dropout)").
 """
 from __future__ import annotations
 
@@ -55,6 +57,12 @@ def with_outliers(w: np.ndarray, frac: float, mul: float, *parts) -> np.ndarray:
 
 def student_t(shape, df, scale, *parts) -> np.ndarray:
     return (rng(*parts).standard_t(df, size=shape) * scale).astype(np.float32)
+
+
+def keep_mask(shape, p: float, *parts) -> np.ndarray:
+    """Dropout keep mask: uint8, 1 with probability 1 - p, else 0 (one
+    uniform draw per element; the pages' dropout rates are 0.05 and 0.1)."""
+    return (rng(*parts).random(shape) >= p).astype(np.uint8)
 
 
 # ----------------------------------------------------------------------------

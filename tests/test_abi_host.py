@@ -145,3 +145,22 @@ def test_linear_argument_errors():
     assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, None, P, P, P, P, 16, None) == -5
     assert b(ctypes.byref(ok), P, None, 32, P, P, 8, 16.0, None, P, P, P, P, ws_need, None) == -1
     assert b(ctypes.byref(ok), P, P, 32, P, P, 300, 16.0, None, P, P, P, P, ws_need, None) == -4
+
+
+def test_dropout_argument_errors():
+    lib = binding.load()
+    f, b = lib.qlora_linear_fwd_dropout, lib.qlora_linear_bwd_dropout
+    ok = wstruct(n=64, k=128)
+    need = binding.dropout_workspace_bytes(32, 64, 128, 8)
+    assert need > binding.workspace_bytes(32, 64, 128, 8)  # room for the masked copy of X
+    assert binding.dropout_workspace_bytes(32, 64, 128, 200) == 0
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, 1.0, P, None, P, need, None) == -4    # p = 1
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, -0.1, P, None, P, need, None) == -4   # p < 0
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, float("nan"), P, None, P, need, None) == -4
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, None, 0.1, P, None, P, need, None) == -1  # keep
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P + 8, 0.1, P, None, P, need, None) == -3
+    assert f(ctypes.byref(ok), P, 32, P, P, 8, 16.0, P, 0.1, P, None, P, need - 1, None) == -5
+    assert f(ctypes.byref(ok), P, 0, None, None, 8, 16.0, None, 0.1, None, None, None, 0, None) == 0
+    assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, P, 1.5, None, P, P, P, P, need, None) == -4
+    assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, None, 0.1, None, P, P, P, P, need, None) == -1
+    assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, P, 0.1, None, P, P, P, P, need - 16, None) == -5
