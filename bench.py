@@ -190,18 +190,22 @@ def main():
         parts["train_step"] = time_step(train_step_grouped, "training step (q/k/v and gate/up grouped)")
         ms_step, value = parts["train_step"]["ms_per_step"], parts["train_step"]["tflops"]
 
-    # Training step with adapter dropout (p = 0.05, one keep mask per linear):
-    # the same algorithmic flops plus the masked copy of X and the masked dX
-    # update; every linear as its own call.
+    # Training step with adapter dropout (p = 0.05, one keep mask per linear
+    # drawn on the device each step): the same algorithmic flops plus the mask,
+    # the masked copy of X and the masked dX update; every linear its own call.
     if want("dropout"):
         p_drop = 0.05
+        mask_off = 0
         for L in layers:
             lay = L["lay"]
-            L["keep"] = torch.from_numpy(synth.keep_mask((M, lay.k), p_drop, wl.name, lay.name, "keep")).to(dev)
+            L["keep"] = torch.empty((M, lay.k), dtype=torch.uint8, device=dev)
+            L["mask_off"] = mask_off  # disjoint windows of one Philox stream
+            mask_off += M * lay.k
             L["wsd"] = torch.empty(qn.dropout_workspace_bytes(M, lay.n, lay.k, R), dtype=torch.uint8, device=dev)
 
         def train_step_dropout():
             for L in layers:
+                qn.dropout_mask(2024, L["mask_off"], (M, L["lay"].k), p_drop, out=L["keep"])
                 qn.linear_fwd_dropout(L["q"], L["x"], L["a"], L["b"], ALPHA, L["keep"], p_drop, out=L["y"],
                                       h_out=L["h"], ws=L["wsd"])
                 qn.linear_bwd_dropout(L["q"], L["x"], L["dy"], L["a"], L["b"], ALPHA, L["keep"], p_drop, h=L["h"],

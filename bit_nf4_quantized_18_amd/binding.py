@@ -27,7 +27,7 @@ EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "ql
            "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels",
            "qlora_quantize_codebook", "qlora_codebook_levels", "qlora_merge", "qlora_unmerge",
            "qlora_requantize", "qlora_linear_dropout_workspace_bytes", "qlora_linear_fwd_dropout",
-           "qlora_linear_bwd_dropout")
+           "qlora_linear_bwd_dropout", "qlora_dropout_mask")
 
 CODEBOOK_NF4 = 0   # normal-quantile levels
 CODEBOOK_INT4 = 1  # 16 evenly spaced levels on [-1, 1]
@@ -95,6 +95,8 @@ def load():
     lib.qlora_linear_fwd_dropout.restype = i32
     lib.qlora_linear_bwd_dropout.argtypes = [wp, vp, vp, i64, vp, vp, i32, f32, vp, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.qlora_linear_bwd_dropout.restype = i32
+    lib.qlora_dropout_mask.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i64, f32, vp, vp]
+    lib.qlora_dropout_mask.restype = i32
     _LIB = lib
     return lib
 
@@ -328,6 +330,17 @@ def _drop_ws(ws, m, n, k, r, dev):
         return ws, ws.numel()
     nbytes = dropout_workspace_bytes(m, n, k, r)
     return (torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None), nbytes
+
+
+def dropout_mask(seed: int, offset: int, shape, p: float, out=None):
+    """Keep mask (uint8, 1 = kept) drawn on the GPU by qlora_dropout_mask:
+    elements offset .. offset + numel - 1 of the stream of `seed`."""
+    import torch
+
+    out = torch.empty(shape, dtype=torch.uint8, device="cuda") if out is None else out
+    _check(load().qlora_dropout_mask(int(seed), int(offset), out.numel(), float(p), _ptr(out), _stream()),
+           "qlora_dropout_mask")
+    return out
 
 
 def linear_fwd_dropout(q: PackedNF4, x, a, b, alpha: float, keep, p: float, want_h: bool = True, out=None,

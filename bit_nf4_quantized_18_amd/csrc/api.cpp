@@ -530,4 +530,13 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t*
   return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream, &d);
 }
 
+qlora_status qlora_dropout_mask(uint64_t seed, uint64_t offset, int64_t count, float p, uint8_t* keep,
+                                hipStream_t stream) {
+  if (!(p >= 0.0f && p < 1.0f)) return QLORA_ERR_UNSUPPORTED;
+  if (count < 1 || count > (INT64_C(1) << 40) || offset % 16 != 0) return QLORA_ERR_SHAPE;
+  if (keep == nullptr) return QLORA_ERR_NULL;
+  if (!aligned16(keep)) return QLORA_ERR_ALIGN;
+  return hip_status(qlora::launch_dropout_mask(seed, offset / 16, count, p * 65536.0f, keep, stream));
+}
+
 }  // extern "C"

@@ -8,7 +8,11 @@
 //
 // Two elementwise kernels, both bound by HBM: the masked copy of X (the
 // 1 / (1 - p) factor goes into the projection's scale, so the copy is exact)
-// and the masked rank-r update of dX after the frozen-weight GEMM.
+// and the masked rank-r update of dX after the frozen-weight GEMM. A third
+// draws keep masks with the counter-based generator Philox4x64-10 (J. K.
+// Salmon, M. A. Moraes, R. O. Dror and D. E. Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC 2011), so a mask can be made on the device and
+// reproduced anywhere from (seed, offset).
 #include "internal.h"
 #include "nf4_lut.h"
 
@@ -17,6 +21,57 @@ namespace {
 
 constexpr int kRows = 16;   // rows per workgroup of the dX update: 4 per wave
 constexpr int kCols = 512;  // columns per workgroup: 8 per lane
+
+// Ten Philox rounds on the counter c under the key (k0, k1): each round takes
+// the two 64 x 64 -> 128-bit products of the paper's multipliers with c0 and
+// c2, mixes their high halves with c1, c3 and the key, and advances the key
+// by the paper's two Weyl constants. Integer arithmetic only.
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    const uint64_t hi0 = __umul64hi(kM0, c[0]), lo0 = kM0 * c[0];
+    const uint64_t hi1 = __umul64hi(kM1, c[2]), lo1 = kM1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += kW0;
+    k1 += kW1;
+  }
+}
+
+// keep[16 t + j] for thread t: block block0 + t under the key (seed, 0);
+// chunk j is bits 16 (j % 4) .. of word j / 4, dropped when float(chunk) <
+// thr = 65536 p. One 16-byte store per block (byte stores for the tail).
+__global__ __launch_bounds__(256) void dropout_mask_kernel(uint64_t seed, uint64_t block0, int64_t count, float thr,
+                                                           uint8_t* __restrict__ keep) {
+  const int64_t nblocks = (count + 15) / 16;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; t < nblocks; t += stride) {
+    uint64_t c[4] = {block0 + static_cast<uint64_t>(t), 0, 0, 0};
+    philox4x64_10(c, seed, 0);
+    uint32_t out[4];
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float u = static_cast<float>(static_cast<uint32_t>((c[wd] >> (16 * q)) & 0xFFFFu));
+        v |= (u < thr ? 0u : 1u) << (8 * q);
+      }
+      out[wd] = v;
+    }
+    const int64_t e0 = 16 * t;
+    if (e0 + 16 <= count) {
+      *reinterpret_cast<u32x4*>(keep + e0) = u32x4{out[0], out[1], out[2], out[3]};
+    } else {
+      for (int j = 0; e0 + j < count; ++j) keep[e0 + j] = static_cast<uint8_t>(out[j >> 2] >> (8 * (j & 3)));
+    }
+  }
+}
 
 // 0xFFFF for each of the two bf16 halves whose keep byte is non-zero.
 __device__ __forceinline__ uint32_t keep_halves(uint32_t word, int pair) {
@@ -111,6 +166,16 @@ hipError_t launch_mask_input(const uint16_t* x, const uint8_t* keep, int64_t cou
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(mask_input_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, x, keep, count8, xm);
+  return hipGetLastError();
+}
+
+hipError_t launch_dropout_mask(uint64_t seed, uint64_t block0, int64_t count, float thr, uint8_t* keep,
+                               hipStream_t st) {
+  int64_t blocks = ((count + 15) / 16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(dropout_mask_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, seed, block0, count,
+                     thr, keep);
   return hipGetLastError();
 }
 

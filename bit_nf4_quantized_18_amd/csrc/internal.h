@@ -117,6 +117,10 @@ hipError_t launch_merge(const PackedW& w, const uint16_t* a, const uint16_t* b, 
 // of 8); dx += keep ? dh a : 0 per element, dh float32 m x r, a bf16 r x k,
 // k % 64 == 0, dx rounded to bf16 once.
 hipError_t launch_mask_input(const uint16_t* x, const uint8_t* keep, int64_t count, uint16_t* xm, hipStream_t st);
+// keep[i] for i < count from Philox4x64-10 block block0 + i / 16 under the
+// key (seed, 0): 16-bit chunk i % 16, dropped when float(chunk) < thr.
+hipError_t launch_dropout_mask(uint64_t seed, uint64_t block0, int64_t count, float thr, uint8_t* keep,
+                               hipStream_t st);
 hipError_t launch_masked_lora_add(uint16_t* dx, const uint8_t* keep, const float* dh, const uint16_t* a, int64_t m,
                                   int64_t k, int r, hipStream_t st);
 

@@ -200,6 +200,22 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
  * Errors: as those calls, plus NULL (keep), ALIGN (keep) and UNSUPPORTED
  * (p outside [0, 1)). */
 size_t qlora_linear_dropout_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
+
+/* Draw a keep mask on the device with a counter-based generator, Philox4x64
+ * with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC 2011), so that the mask for the dropout calls above
+ * is reproducible from (seed, offset) alone.
+ *   Element i (0 <= i < count) is element g = offset + i of one stream. Block
+ *   b = g / 16 gives the four 64-bit words Philox4x64-10(counter (b, 0, 0, 0),
+ *   key (seed, 0)); chunk j = g % 16 is bits 16 (j % 4) .. 16 (j % 4) + 15 of
+ *   word j / 4, and keep[i] = 0 when float(chunk) < 65536 p, else 1. The
+ *   drop probability is ceil(65536 p) / 65536.
+ *   offset % 16 == 0 (distinct layers and steps take disjoint windows);
+ *   1 <= count <= 2^40; 0 <= p < 1; keep: count bytes, device, 16-byte
+ *   aligned. Bit-exact with the CPU oracle.
+ * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED (p) / HIP. */
+qlora_status qlora_dropout_mask(uint64_t seed, uint64_t offset, int64_t count, float p, uint8_t* keep,
+                                hipStream_t stream);
 qlora_status qlora_linear_fwd_dropout(const qlora_nf4_weight* w, const uint16_t* x, int64_t m,
                                       const uint16_t* a, const uint16_t* b, int r, float alpha,
                                       const uint8_t* keep, float p, uint16_t* y, float* h_out,

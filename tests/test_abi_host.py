@@ -164,3 +164,13 @@ def test_dropout_argument_errors():
     assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, P, 1.5, None, P, P, P, P, need, None) == -4
     assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, None, 0.1, None, P, P, P, P, need, None) == -1
     assert b(ctypes.byref(ok), P, P, 32, P, P, 8, 16.0, P, 0.1, None, P, P, P, P, need - 16, None) == -5
+
+
+def test_dropout_mask_argument_errors():
+    f = binding.load().qlora_dropout_mask
+    assert f(1, 0, 100, 1.0, P, None) == -4
+    assert f(1, 0, 100, -0.5, P, None) == -4
+    assert f(1, 8, 100, 0.1, P, None) == -2      # offset not a multiple of 16
+    assert f(1, 0, 0, 0.1, P, None) == -2
+    assert f(1, 0, 100, 0.1, None, None) == -1
+    assert f(1, 0, 100, 0.1, P + 4, None) == -3

@@ -98,3 +98,44 @@ def test_drop_all_leaves_frozen_path(gpu_lib):
     torch.cuda.synchronize()
     assert not torch.any(h) and not torch.any(da) and not torch.any(db)
     assert torch.equal(y, y0) and torch.equal(dx, dx0)
+
+
+@pytest.mark.parametrize("seed,offset,count,p", [
+    (0, 0, 2048 * 4096, 0.05),          # one 7B activation tile's mask
+    (12345, 16 * 7, 1000 + 37, 0.1),    # ragged tail
+    (2**64 - 1, 2**40, 16, 0.5),
+    (7, 0, 5, 0.999),
+    (7, 32, 4096, 0.0),
+])
+def test_dropout_mask_bit_exact(gpu_lib, seed, offset, count, p):
+    """Keep masks drawn on the GPU equal the oracle's Philox4x64-10 masks."""
+    import torch
+
+    from oracle import philox as OP
+
+    say(f"[dropout mask] seed={seed} offset={offset} count={count} p={p}")
+    got = gpu_lib.dropout_mask(seed, offset, (count,), p)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), OP.keep_mask(seed, offset, count, p))
+
+
+def test_dropout_step_with_generated_mask(gpu_lib):
+    """A layer step whose mask is drawn on the device: parity with the oracle
+    given the oracle's mask for the same (seed, offset)."""
+    import torch
+
+    from oracle import philox as OP
+
+    m, n, k, r, alpha, p = 300, 256, 320, 16, 32.0, 0.1
+    q, w16, x, a, b, dy, _ = _inputs(gpu_lib, "gen_mask", m, n, k, r, p)
+    say("[dropout] step with a device-drawn mask")
+    kc = gpu_lib.dropout_mask(42, 16 * 1000, (m, k), p)
+    keep = OP.keep_mask(42, 16 * 1000, m * k, p).reshape(m, k)
+    xc, dyc, ac, bc = x.cuda(), dy.cuda(), a.cuda(), b.cuda()
+    y, h = gpu_lib.linear_fwd_dropout(q, xc, ac, bc, alpha, kc, p)
+    dx, da, db = gpu_lib.linear_bwd_dropout(q, xc, dyc, ac, bc, alpha, kc, p, h=h)
+    torch.cuda.synchronize()
+    assert np.array_equal(kc.cpu().numpy(), keep)
+    y_ref, _ = OD.linear_fwd_dropout(f64(x), w16, f64(a), f64(b), alpha, r, keep, p)
+    dx_ref, da_ref, db_ref = OD.linear_bwd_dropout(f64(x), w16, f64(a), f64(b), f64(dy), alpha, r, keep, p)
+    assert max(rel(f64(y), y_ref), rel(f64(dx), dx_ref), rel(f64(da), da_ref), rel(f64(db), db_ref)) <= TOL
