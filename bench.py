@@ -57,7 +57,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run (train,dropout,gemm,copy,decode,dequant,quant,merge,cpu)")
+    ap.add_argument("--only", default="", help="comma list of parts to run (train,f16,dropout,gemm,library,copy,decode,dequant,quant,merge,cpu)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -190,6 +190,26 @@ def main():
         parts["train_step"] = time_step(train_step_grouped, "training step (q/k/v and gate/up grouped)")
         ms_step, value = parts["train_step"]["ms_per_step"], parts["train_step"]["tflops"]
 
+    # The same per-linear step with IEEE half as the compute type (fp16 X, A,
+    # B, dY; the weight unpacked to half inside the matmuls).
+    if want("f16"):
+        for L in layers:
+            for key in ("x", "a", "b", "dy"):
+                L[key + "16"] = L[key].float().to(torch.float16)
+            L["y16"] = torch.empty_like(L["y"], dtype=torch.float16)
+            L["dx16"] = torch.empty_like(L["dx"], dtype=torch.float16)
+
+        def train_step_f16():
+            for L in layers:
+                qn.linear_fwd(L["q"], L["x16"], L["a16"], L["b16"], ALPHA, out=L["y16"], h_out=L["h"], ws=L["ws"])
+                qn.linear_bwd(L["q"], L["x16"], L["dy16"], L["a16"], L["b16"], ALPHA, h=L["h"], dx=L["dx16"],
+                              da=L["da"], db=L["db"], ws=L["ws"])
+
+        parts["train_step_f16"] = time_step(train_step_f16, "training step, fp16 compute, one call per linear")
+        for L in layers:
+            for key in ("x16", "a16", "b16", "dy16", "y16", "dx16"):
+                del L[key]
+
     # Training step with adapter dropout (p = 0.05, one keep mask per linear
     # drawn on the device each step): the same algorithmic flops plus the mask,
     # the masked copy of X and the masked dX update; every linear its own call.
@@ -255,6 +275,36 @@ def main():
                     "kernel": res["fwd"]["kernel"],
                     "per_launch_gflop": step_fwd_base(layers, M) / len(layers) / 1e9,
                     "avg_launch_ms": res["fwd"]["avg_launch_ms"]}
+
+    # Context, not the product: the vendor library's dense bf16 GEMM
+    # (torch.matmul -> hipBLASLt) on the same shapes with a bf16 weight that
+    # is already dequantized (no NF4 unpack), timed the same way.
+    if want("library"):
+        lib_res = []
+        for L in layers:
+            lay = L["lay"]
+            wd = qn.dequantize(L["q"], torch.bfloat16)
+            for kind, fn in (("fwd", lambda: L["x"] @ wd.t()), ("dx", lambda: L["dy"] @ wd)):
+                fn()
+                torch.cuda.synchronize()
+                pairs = []
+                for _ in range(10):
+                    s0, s1 = ev(), ev()
+                    s0.record()
+                    fn()
+                    s1.record()
+                    pairs.append((s0, s1))
+                torch.cuda.synchronize()
+                ms = sum(a.elapsed_time(b) for a, b in pairs) / 10
+                lib_res.append({"layer": lay.name, "kind": kind, "n": lay.n, "k": lay.k, "ms": ms,
+                                "tflops": 2.0 * M * lay.n * lay.k / ms / 1e9})
+            del wd
+        for kind in ("fwd", "dx"):
+            rows = [e for e in lib_res if e["kind"] == kind]
+            tf = sum(2.0 * M * e["n"] * e["k"] for e in rows) / sum(e["ms"] for e in rows) / 1e9
+            log(f"[bench] library dense bf16 GEMM {kind} (hipBLASLt, weight pre-dequantized): {tf:.1f} TFLOP/s")
+        parts["library_dense_bf16_gemm"] = {"note": "torch.matmul on a pre-dequantized bf16 weight, same shapes",
+                                            "per_layer": lib_res}
 
     # ------------------------------------- plain copy (counter calibration)
     if want("copy"):

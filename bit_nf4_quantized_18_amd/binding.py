@@ -14,7 +14,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libqlora_nf4.so")
 
-QLORA_BF16, QLORA_F32 = 0, 1
+QLORA_BF16, QLORA_F32, QLORA_F16 = 0, 1, 2
 MAX_RANK = 128
 BLOCK, DQ_GROUP = 64, 256
 
@@ -27,7 +27,7 @@ EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "ql
            "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels",
            "qlora_quantize_codebook", "qlora_codebook_levels", "qlora_merge", "qlora_unmerge",
            "qlora_requantize", "qlora_linear_dropout_workspace_bytes", "qlora_linear_fwd_dropout",
-           "qlora_linear_bwd_dropout", "qlora_dropout_mask")
+           "qlora_linear_bwd_dropout", "qlora_dropout_mask", "qlora_linear_fwd_f16", "qlora_linear_bwd_f16")
 
 CODEBOOK_NF4 = 0   # normal-quantile levels
 CODEBOOK_INT4 = 1  # 16 evenly spaced levels on [-1, 1]
@@ -66,6 +66,10 @@ def load():
     lib.qlora_linear_fwd.restype = i32
     lib.qlora_linear_bwd.argtypes = [wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.qlora_linear_bwd.restype = i32
+    lib.qlora_linear_fwd_f16.argtypes = lib.qlora_linear_fwd.argtypes
+    lib.qlora_linear_fwd_f16.restype = i32
+    lib.qlora_linear_bwd_f16.argtypes = lib.qlora_linear_bwd.argtypes
+    lib.qlora_linear_bwd_f16.restype = i32
     lib.qlora_linear_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.qlora_linear_workspace_bytes.restype = sz
     p64 = ctypes.POINTER(ctypes.c_int64)
@@ -197,7 +201,7 @@ def dequantize(q: PackedNF4, dtype=None):
     import torch
 
     dtype = torch.bfloat16 if dtype is None else dtype
-    code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32}[dtype]
+    code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32, torch.float16: QLORA_F16}[dtype]
     out = torch.empty((q.n, q.k), dtype=dtype, device=q.codes.device)
     ws = q.c_struct()
     _check(load().qlora_nf4_dequantize(ctypes.byref(ws), code, _ptr(out), _stream()), "qlora_nf4_dequantize")
@@ -272,14 +276,16 @@ def _workspace(m, n, k, r, device):
 
 def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool = True, out=None, h_out=None,
                ws=None):
-    """Y = X W16^T + (alpha/r) (X A^T) B^T. x: bf16 (m, k). Returns (y, h).
+    """Y = X W16^T + (alpha/r) (X A^T) B^T. x: bf16 (m, k), or fp16 for the
+    fp16 compute entry point (A, B and Y then fp16 too). Returns (y, h).
     ``out``, ``h_out`` and ``ws`` (uint8 workspace) may be preallocated."""
     import torch
 
     m = x.shape[0]
     r = 0 if a is None else a.shape[0]
     dev = x.device
-    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=dev)
+    f16 = x.dtype == torch.float16  # fp16 compute: the _f16 entry point
+    y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=dev)
     h = h_out if h_out is not None else (
         torch.empty((m, r), dtype=torch.float32, device=dev) if (want_h and r > 0) else None)
     if ws is None:
@@ -287,23 +293,26 @@ def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool
     else:
         nbytes = ws.numel()
     wc = q.c_struct()
-    st = load().qlora_linear_fwd(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(y), _ptr(h),
-                                 _ptr(ws), nbytes, _stream())
-    _check(st, "qlora_linear_fwd")
+    fn = load().qlora_linear_fwd_f16 if f16 else load().qlora_linear_fwd
+    st = fn(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(y), _ptr(h), _ptr(ws), nbytes,
+            _stream())
+    _check(st, "qlora_linear_fwd_f16" if f16 else "qlora_linear_fwd")
     return y, h
 
 
 def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, need_dx: bool = True,
                dx=None, da=None, db=None, ws=None):
-    """Returns (dx bf16 (m,k) or None, dA float32 (r,k), dB float32 (n,r)).
-    Outputs and the workspace may be preallocated."""
+    """Returns (dx (m,k) of dy's 16-bit type or None, dA float32 (r,k), dB
+    float32 (n,r)). fp16 inputs take the fp16 entry point. Outputs and the
+    workspace may be preallocated."""
     import torch
 
     m = dy.shape[0]
     r = 0 if a is None else a.shape[0]
     dev = dy.device
+    f16 = dy.dtype == torch.float16
     if dx is None and need_dx:
-        dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((m, q.k), dtype=dy.dtype, device=dev)
     if r and da is None:
         da = torch.empty((r, q.k), dtype=torch.float32, device=dev)
     if r and db is None:
@@ -313,9 +322,10 @@ def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, 
     else:
         nbytes = ws.numel()
     wc = q.c_struct()
-    st = load().qlora_linear_bwd(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(h),
-                                 _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes, _stream())
-    _check(st, "qlora_linear_bwd")
+    fn = load().qlora_linear_bwd_f16 if f16 else load().qlora_linear_bwd
+    st = fn(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(h), _ptr(dx), _ptr(da),
+            _ptr(db), _ptr(ws), nbytes, _stream())
+    _check(st, "qlora_linear_bwd_f16" if f16 else "qlora_linear_bwd")
     return dx, da, db
 
 

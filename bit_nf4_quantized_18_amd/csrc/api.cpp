@@ -199,10 +199,11 @@ qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dty
                                   hipStream_t stream) {
   const qlora_status st = check_weight(w, false);
   if (st != QLORA_OK) return st;
-  if (out_dtype != QLORA_BF16 && out_dtype != QLORA_F32) return QLORA_ERR_UNSUPPORTED;
+  if (out_dtype != QLORA_BF16 && out_dtype != QLORA_F32 && out_dtype != QLORA_F16) return QLORA_ERR_UNSUPPORTED;
   if (out == nullptr) return QLORA_ERR_NULL;
   if (!aligned16(out)) return QLORA_ERR_ALIGN;
-  return hip_status(qlora::launch_dequantize(view(w), out_dtype == QLORA_F32, out, stream));
+  const int kind = out_dtype == QLORA_F32 ? 1 : (out_dtype == QLORA_F16 ? 2 : 0);
+  return hip_status(qlora::launch_dequantize(view(w), kind, out, stream));
 }
 
 }  // extern "C"
@@ -214,7 +215,7 @@ namespace {
 qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x, int64_t m,
                              const uint16_t* a, const uint16_t* b, int r, int rpart, float alpha, uint16_t* y,
                              float* h_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                             const DropArg* drop = nullptr) {
+                             const DropArg* drop = nullptr, bool f16 = false) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
@@ -258,9 +259,9 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     const int splits = qlora::skinny_splits(m, k);
     if (r > 0 && !qlora::gemv_fuses_h(k, r)) {
       hpart = reinterpret_cast<float*>(base + L.h32);
-      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, hpart, nullptr, splits, stream));
+      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, hpart, nullptr, splits, stream, f16));
     }
-    QLORA_TRY(qlora::launch_gemv(pw, x, m, a, hpart, splits, b, r, s, y, h_out, stream));
+    QLORA_TRY(qlora::launch_gemv(pw, x, m, a, hpart, splits, b, r, s, y, h_out, stream, f16));
   } else {
     float* h32 = (r == 0) ? nullptr : (h_out != nullptr ? h_out : reinterpret_cast<float*>(base + L.h32));
     uint16_t* hs = (r == 0) ? nullptr : reinterpret_cast<uint16_t*>(base + L.hs);
@@ -269,12 +270,12 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     const float hscale = drop != nullptr ? drop->inv_keep : 1.0f;
     if (r > 0)
       QLORA_TRY(qlora::launch_skinny_prefill(xa, a, m, k, r, rp, hscale, s, reinterpret_cast<float*>(base + L.part),
-                                             h32, hs, stream));
+                                             h32, hs, stream, f16));
     qlora::LoraParts one;
     one.g = 1;
     one.rpart = rpart;
     one.end[0] = static_cast<int>(n);
-    QLORA_TRY(qlora::launch_gemm_fwd(pw, x, m, hs, b, rpart, rp, grouped ? *grp : one, y, stream));
+    QLORA_TRY(qlora::launch_gemm_fwd(pw, x, m, hs, b, rpart, rp, grouped ? *grp : one, y, stream, f16));
   }
   return QLORA_OK;
 }
@@ -282,7 +283,8 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
 qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x,
                              const uint16_t* dy, int64_t m, const uint16_t* a, const uint16_t* b, int r, int rpart,
                              float alpha, const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
-                             size_t ws_bytes, hipStream_t stream, const DropArg* drop = nullptr) {
+                             size_t ws_bytes, hipStream_t stream, const DropArg* drop = nullptr,
+                             bool f16 = false) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
@@ -340,7 +342,7 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     const float inv_keep = drop != nullptr ? drop->inv_keep : 1.0f;
     if (h == nullptr) {
       float* h32 = reinterpret_cast<float*>(base + L.h32);
-      QLORA_TRY(qlora::launch_skinny_prefill(xa, a, m, k, r, rp, inv_keep, 1.0f, spart, h32, nullptr, stream));
+      QLORA_TRY(qlora::launch_skinny_prefill(xa, a, m, k, r, rp, inv_keep, 1.0f, spart, h32, nullptr, stream, f16));
       h = h32;
     }
     // A^T, and B^T (block diagonal for grouped weights: part l's slots see
@@ -352,18 +354,18 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     // adapter slots.
     if (drop != nullptr) dhs = nullptr;
     QLORA_TRY(qlora::launch_skinny_prefill(dy, bt, m, n, r, rp, drop != nullptr ? s * inv_keep : s, 1.0f, spart, dh32,
-                                           dhs, stream));
+                                           dhs, stream, f16));
     if (qlora::rank_grads_fused(r) && qlora::rank_grads_fused(rpart)) {
       // dA = dH^T X (r x k) and dB = s dY^T H (n x rpart) in one pass each
       QLORA_TRY(qlora::launch_rank_grads(dh32, xa, k, h, dy, n, m, r, grp, s,
-                                         qlora::rank_grad_splits(m, n, k, r, rpart), part, da, db, stream));
+                                         qlora::rank_grad_splits(m, n, k, r, rpart), part, da, db, stream, f16));
     } else {
       if (grouped) return QLORA_ERR_UNSUPPORTED;  // checked by the caller
       const int splits = qlora::rank_reduce_splits(m, n, k, r);
       // dA = dH^T X  (r x k)
-      QLORA_TRY(qlora::launch_rank_reduce(dh32, xa, m, k, r, 1.0f, splits, part, da, 0, stream));
+      QLORA_TRY(qlora::launch_rank_reduce(dh32, xa, m, k, r, 1.0f, splits, part, da, 0, stream, f16));
       // dB = s dY^T H  (n x r)
-      QLORA_TRY(qlora::launch_rank_reduce(h, dy, m, n, r, s, splits, part, db, 1, stream));
+      QLORA_TRY(qlora::launch_rank_reduce(h, dy, m, n, r, s, splits, part, db, 1, stream, f16));
     }
   }
   if (dx != nullptr) {
@@ -373,7 +375,7 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
       QLORA_TRY(qlora::launch_masked_lora_add(dx, drop->keep, reinterpret_cast<const float*>(base + L.dh32), a, m, k,
                                               r, stream));
     } else {
-      QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream));
+      QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream, f16));
     }
   }
   return QLORA_OK;
@@ -537,6 +539,19 @@ qlora_status qlora_dropout_mask(uint64_t seed, uint64_t offset, int64_t count, f
   if (keep == nullptr) return QLORA_ERR_NULL;
   if (!aligned16(keep)) return QLORA_ERR_ALIGN;
   return hip_status(qlora::launch_dropout_mask(seed, offset / 16, count, p * 65536.0f, keep, stream));
+}
+
+qlora_status qlora_linear_fwd_f16(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                                  const uint16_t* b, int r, float alpha, uint16_t* y, float* h_out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, ws, ws_bytes, stream, nullptr, true);
+}
+
+qlora_status qlora_linear_bwd_f16(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t m,
+                                  const uint16_t* a, const uint16_t* b, int r, float alpha, const float* h_saved,
+                                  uint16_t* dx, float* da, float* db, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream, nullptr,
+                         true);
 }
 
 }  // extern "C"

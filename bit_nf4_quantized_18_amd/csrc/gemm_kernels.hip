@@ -41,6 +41,8 @@
 // output columns of one token row and stores 8 contiguous bytes. Tiles are
 // ordered so that the workgroups on one XCD (ids congruent mod 8) share token
 // rows in that XCD's L2. The rank-r LoRA term is one more pass of MFMAs.
+// kF16 builds the same kernel for IEEE-half compute: half lookup tables, the
+// f16 MFMA and a half output; everything else is bit-pattern movement.
 #include "bufmem.h"
 #include "internal.h"
 #include "mfma.h"
@@ -73,7 +75,7 @@ __device__ __forceinline__ u32x2 ld_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-template <bool kTransW, bool kDQ>
+template <bool kTransW, bool kDQ, bool kF16>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,
                                                        int64_t P, int64_t Qn, const uint16_t* __restrict__ ep_a,
                                                        const uint16_t* __restrict__ ep_b, int64_t ep_ld, int ep_lim,
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     };
     auto store_w = [&](int kt, u32x4 c, uint32_t sc, float gs) {
       const float s = kDQ ? u8_unit(sc) * gs : gs;
-      const BlockLut lut = make_block_lut(L.v, wk_ok ? s : 0.0f);
+      const BlockLut lut = make_block_lut<kF16>(L.v, wk_ok ? s : 0.0f);
       uint16_t* bs = Bs + (kt % kStages) * kBStage;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = mfma_16x16x32(xb[nt], xa[mt], acc[nt][mt]);
+      for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = mma16<kF16>(xb[nt], xa[mt], acc[nt][mt]);
   };
 
   __syncthreads();
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     for (int nt = 0; nt < 4; ++nt) {
       const f32x4 c = acc[nt][mt];
       *reinterpret_cast<u32x2*>(ep + (16 * mt + i) * kEpRow + 16 * nt + 4 * g) =
-          u32x2{cvt_bf16x2(c[0], c[1]), cvt_bf16x2(c[2], c[3])};
+          u32x2{cvt_16x2<kF16>(c[0], c[1]), cvt_16x2<kF16>(c[2], c[3])};
     }
   const int rr = lane >> 3, cc = lane & 7;
   const int64_t pcol = p0 + wp * 64 + 8 * cc;
@@ -355,16 +357,18 @@ unsigned tiles(int64_t m, int64_t p) { return static_cast<unsigned>(((m + kBM - 
 }  // namespace
 
 hipError_t launch_gemm_fwd(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* hs, const uint16_t* b,
-                           int r, int rpad, const LoraParts& parts, uint16_t* y, hipStream_t st) {
-  auto kern = w.dq ? nf4_gemm_kernel<false, true> : nf4_gemm_kernel<false, false>;
+                           int r, int rpad, const LoraParts& parts, uint16_t* y, hipStream_t st, bool f16) {
+  auto kern = f16 ? (w.dq ? nf4_gemm_kernel<false, true, true> : nf4_gemm_kernel<false, false, true>)
+                  : (w.dq ? nf4_gemm_kernel<false, true, false> : nf4_gemm_kernel<false, false, false>);
   hipLaunchKernelGGL(kern, dim3(tiles(m, w.n)), dim3(512), 0, st, w, x, m, w.n, w.k, hs, b, static_cast<int64_t>(r), r,
                      rpad, parts, y, codebook_table(w.codebook));
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_dx(const PackedW& w, const uint16_t* dy, int64_t m, const uint16_t* dhs, const uint16_t* at,
-                          int rpad, uint16_t* dx, hipStream_t st) {
-  auto kern = w.dq ? nf4_gemm_kernel<true, true> : nf4_gemm_kernel<true, false>;
+                          int rpad, uint16_t* dx, hipStream_t st, bool f16) {
+  auto kern = f16 ? (w.dq ? nf4_gemm_kernel<true, true, true> : nf4_gemm_kernel<true, false, true>)
+                  : (w.dq ? nf4_gemm_kernel<true, true, false> : nf4_gemm_kernel<true, false, false>);
   hipLaunchKernelGGL(kern, dim3(tiles(m, w.k)), dim3(512), 0, st, w, dy, m, w.k, w.n, dhs, at,
                      static_cast<int64_t>(rpad), rpad, rpad, LoraParts{}, dx, codebook_table(w.codebook));
   return hipGetLastError();

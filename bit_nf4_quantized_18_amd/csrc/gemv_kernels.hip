@@ -51,7 +51,7 @@ __device__ __forceinline__ u32x4 decode_order(u32x4 v) {
   return u32x4{out[0], out[1], out[2], out[3]};
 }
 
-template <int WAVES, bool kDQ, bool kFuseH>
+template <int WAVES, bool kDQ, bool kFuseH, bool kF16>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
                                                           const uint16_t* __restrict__ a,
                                                           const float* __restrict__ hpart, int hsplits,
@@ -160,13 +160,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     if (base + wave * 4 < nbk) {
       const bool ok = (n < N) && (kb < nbk);
       const float sc = kDQ ? u8_unit(scode) * gsc : gsc;
-      const BlockLut lut = make_block_lut(L.v, ok ? sc : 0.0f);
+      const BlockLut lut = make_block_lut<kF16>(L.v, ok ? sc : 0.0f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
         uint32_t wv[4];
         lut8_decode_order(lut, cw, wv);
-        acc = mfma_16x16x32(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
+        acc = mma16<kF16>(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
       }
     }
     if (kFuseH) {
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
         for (int j = 0; j < 8; ++j) {
           const int p = 8 * G + j;
           const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
-          hacc = mfma_16x16x32(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
+          hacc = mma16<kF16>(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
         }
       }
     }
@@ -224,10 +224,10 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     float lo = 0.0f;
     const uint16_t* brow = b_lds + (l2 & 15) * r;
     const float* hrow = h_lds + mo * r;
-    for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], __uint_as_float(static_cast<uint32_t>(brow[j]) << 16), lo);
+    for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
     sum = fmaf(s, lo, sum);
   }
-  y[mo * N + no] = f32_to_bf16_rne(sum);
+  y[mo * N + no] = to16<kF16>(sum);
 }
 
 // Persistent form for k <= 4096 (one pass covers a row): a workgroup takes
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
 // are in flight while the current one is unpacked and multiplied. X is loaded
 // once (the same fragments serve every row group) and, with kFuseH, H is
 // computed once per workgroup, in its first row group, from A copied into LDS.
-template <bool kDQ, bool kFuseH>
+template <bool kDQ, bool kFuseH, bool kF16>
 __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
                                                                const uint16_t* __restrict__ a,
                                                                const float* __restrict__ hpart, int hsplits,
@@ -344,13 +344,13 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
       const int n = rg * 16 + i;
       const bool ok = (n < N) && kval;
       const float sc = kDQ ? u8_unit(Tc.scode) * Tc.gsc : Tc.gsc;
-      const BlockLut lut = make_block_lut(L.v, ok ? sc : 0.0f);
+      const BlockLut lut = make_block_lut<kF16>(L.v, ok ? sc : 0.0f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t cw = (j < 4) ? Tc.c0[j] : Tc.c1[j - 4];
         uint32_t wv[4];
         lut8_decode_order(lut, cw, wv);
-        acc = mfma_16x16x32(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
+        acc = mma16<kF16>(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
       }
     }
     const bool first = rg == rg0;
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
         for (int j = 0; j < 8; ++j) {
           const int p = 8 * G + j;
           const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
-          hacc = mfma_16x16x32(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
+          hacc = mma16<kF16>(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
         }
       }
     }
@@ -409,10 +409,10 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
         float lo = 0.0f;
         const uint16_t* brow = b_lds + (l2 & 15) * r;
         const float* hrow = h_lds + mo * r;
-        for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], __uint_as_float(static_cast<uint32_t>(brow[j]) << 16), lo);
+        for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
         sum = fmaf(s, lo, sum);
       }
-      y[mo * N + no] = f32_to_bf16_rne(sum);
+      y[mo * N + no] = to16<kF16>(sum);
     }
     acc = f32x4{0.f, 0.f, 0.f, 0.f};
   };
@@ -441,24 +441,36 @@ int device_cus() {
   return cus[dev];
 }
 
-hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
-                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
+namespace {
+
+template <bool kF16>
+hipError_t launch_gemv_t(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
+                         int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
   constexpr int kWaves = 16;
   const int64_t nrg = (w.n + 15) / 16;
   const bool fuse = gemv_fuses_h(w.k, r);
   if (w.k <= 4096) {
     const unsigned grid = static_cast<unsigned>(nrg < device_cus() ? nrg : device_cus());
-    auto kern = w.dq ? (fuse ? gemv_persistent_kernel<true, true> : gemv_persistent_kernel<true, false>)
-                     : (fuse ? gemv_persistent_kernel<false, true> : gemv_persistent_kernel<false, false>);
+    auto kern = w.dq ? (fuse ? gemv_persistent_kernel<true, true, kF16> : gemv_persistent_kernel<true, false, kF16>)
+                     : (fuse ? gemv_persistent_kernel<false, true, kF16> : gemv_persistent_kernel<false, false, kF16>);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a, hpart, hsplits, b,
                        r, s, y, h_out, codebook_table(w.codebook));
     return hipGetLastError();
   }
-  auto kern = w.dq ? (fuse ? gemv_kernel<kWaves, true, true> : gemv_kernel<kWaves, true, false>)
-                   : (fuse ? gemv_kernel<kWaves, false, true> : gemv_kernel<kWaves, false, false>);
+  auto kern = w.dq ? (fuse ? gemv_kernel<kWaves, true, true, kF16> : gemv_kernel<kWaves, true, false, kF16>)
+                   : (fuse ? gemv_kernel<kWaves, false, true, kF16> : gemv_kernel<kWaves, false, false, kF16>);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nrg)), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a,
                      hpart, hsplits, b, r, s, y, h_out, codebook_table(w.codebook));
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
+                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
+                       bool f16) {
+  return f16 ? launch_gemv_t<true>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st)
+             : launch_gemv_t<false>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st);
 }
 
 }  // namespace qlora

@@ -1,4 +1,7 @@
 // Internal declarations shared by the host library and the kernels.
+//
+// Every launcher that reads or writes 16-bit activations takes `f16`: false
+// for bfloat16 (the default), true for IEEE half; the data layout is the same.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,7 +45,8 @@ struct PackedW {
   int codebook;  // QLORA_CODEBOOK_*
 };
 
-hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream_t s);
+// out_kind: 0 bf16, 1 float32, 2 IEEE half.
+hipError_t launch_dequantize(const PackedW& w, int out_kind, void* out, hipStream_t s);
 
 // H-like skinny projection: out[m][j] = scale * sum_q P[m][q] * Q[j][q] for j < r,
 // P bf16 m x qn (row stride qn, qn % 8 == 0), Q bf16 r x qn. With one
@@ -51,7 +55,8 @@ hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream
 // bf16(scale2 * scale * sum). With several splits (m <= 16, see
 // skinny_splits, decode path only) it writes raw partial sums to out_f32 as splits x m x r.
 hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
-                         float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s);
+                         float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s,
+                         bool f16 = false);
 int skinny_splits(int64_t m, int64_t qn);
 
 // Prefill (m > 16) form of the same projection, split over the contraction
@@ -62,7 +67,7 @@ int skinny_splits(int64_t m, int64_t qn);
 int skinny_prefill_splits(int64_t m, int64_t qn, int r);
 hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
                                  float scale, float scale2, float* part, float* out_f32, uint16_t* out_bf16,
-                                 hipStream_t st);
+                                 hipStream_t st, bool f16 = false);
 
 // Decode GEMV, m <= 16: y = x W16^T + s * h B^T in one launch when
 // gemv_fuses_h(k, r) (H = x A^T computed in the kernel from a); otherwise
@@ -70,7 +75,8 @@ hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m
 // launch_skinny). r = 0: base only. h_out (m x r, may be null) receives H.
 bool gemv_fuses_h(int64_t k, int r);
 hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
-                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st);
+                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
+                       bool f16 = false);
 
 // A weight made of g row blocks (grouped linears sharing their input): part
 // l covers output rows end[l-1] .. end[l]-1 (end[-1] = 0) and owns adapter
@@ -85,12 +91,13 @@ struct LoraParts {
 // m x rpad (already scaled by s) and b is n x r bf16 (r = slots per part);
 // output column p of part l adds sum_j hs[.][l r + j] b[p][j].
 hipError_t launch_gemm_fwd(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* hs,
-                           const uint16_t* b, int r, int rpad, const LoraParts& parts, uint16_t* y, hipStream_t st);
+                           const uint16_t* b, int r, int rpad, const LoraParts& parts, uint16_t* y, hipStream_t st,
+                           bool f16 = false);
 
 // Fused dequant-GEMM, backward data: dx = dy W16 + dhs At where dhs is bf16
 // m x rpad and at is bf16 k x rpad (A transposed, zero padded).
 hipError_t launch_gemm_dx(const PackedW& w, const uint16_t* dy, int64_t m, const uint16_t* dhs,
-                          const uint16_t* at, int rpad, uint16_t* dx, hipStream_t st);
+                          const uint16_t* at, int rpad, uint16_t* dx, hipStream_t st, bool f16 = false);
 
 // Transposes with zero padding: bt (rpad x n) from b (n x r); at (k x rpad) from a (r x k).
 // Grouped weights (parts != null, r = g rpart): b is n x rpart (the parts' B
@@ -102,7 +109,7 @@ hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n
 // Deterministic: `splits` partial sums over m-ranges into part (splits x r x cn),
 // then a fixed-order reduce. c_major=0 writes out[j*cn + c], 1 writes out[c*r + j].
 hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int64_t cn, int r, float scale,
-                              int splits, float* part, float* out, int c_major, hipStream_t st);
+                              int splits, float* part, float* out, int c_major, hipStream_t st, bool f16 = false);
 
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st);
 
@@ -140,6 +147,6 @@ bool rank_grads_fused(int r);
 int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r0, int r1);
 hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, const float* h, const uint16_t* dy,
                              int64_t n, int64_t m, int r0, const LoraParts* parts, float scale, int splits, float* part,
-                             float* da, float* db, hipStream_t st);
+                             float* da, float* db, hipStream_t st, bool f16 = false);
 
 }  // namespace qlora

@@ -21,7 +21,7 @@ namespace {
 // output column tiles (0: only the reordered copy of P is produced). Narrow
 // ranks get more waves per row block, so that each wave makes only one or
 // two trips to memory.
-template <int RT, int WAVES>
+template <int RT, int WAVES, bool kF16>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
                                                      int64_t M, int64_t qn, int r, int rpad, float scale,
                                                      float scale2, float* __restrict__ out_f32,
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int j = 16 * t + i;
-        acc[t] = mfma_16x16x32(av, j < r ? b[u][t] : u32x4{0, 0, 0, 0}, acc[t]);
+        acc[t] = mma16<kF16>(av, j < r ? b[u][t] : u32x4{0, 0, 0, 0}, acc[t]);
       }
     }
   }
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
     } else {
       const float val = scale * sum;
       if (out_f32 != nullptr && j < r) out_f32[mo * r + j] = val;
-      if (out_bf16 != nullptr && j < rpad) out_bf16[mo * rpad + j] = f32_to_bf16_rne(scale2 * val);
+      if (out_bf16 != nullptr && j < rpad) out_bf16[mo * rpad + j] = to16<kF16>(scale2 * val);
     }
   }
 }
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
 constexpr int kPjRows = 64, kPjCols = 128, kPjStages = 4;
 constexpr int kPjP = kPjRows * kPjCols;  // bf16 elements per stage
 
-template <int RT>
+template <int RT, bool kF16>
 __global__ __launch_bounds__(384) void proj_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
                                                    int64_t M, int64_t qn, int r, int splits, int64_t per,
                                                    float* __restrict__ part) {
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(384) void proj_kernel(const uint16_t* __restrict__ 
       const int off = ((4 * kk + g) ^ i) * 8;  // rows 16 w + i and 16 t + i: the swizzle key is i
       const u32x4 pf = ld16(ps + off);
 #pragma unroll
-      for (int t = 0; t < RT; ++t) acc[t] = mfma_16x16x32(ld16(qs + t * 16 * kPjCols + off), pf, acc[t]);
+      for (int t = 0; t < RT; ++t) acc[t] = mma16<kF16>(ld16(qs + t * 16 * kPjCols + off), pf, acc[t]);
     }
     __syncthreads();  // the slot may be refilled
   }
@@ -205,6 +205,7 @@ __global__ __launch_bounds__(384) void proj_kernel(const uint16_t* __restrict__ 
 // Second half of the split prefill projection: out_f32 = scale * sum of the
 // split partials (summed in split order), out_bf16 = bf16(scale2 * that),
 // zero-padded from r to rpad columns.
+template <bool kF16>
 __global__ void skinny_final_kernel(const float* __restrict__ part, int64_t M, int r, int rpad, int splits,
                                     float scale, float scale2, float* __restrict__ out_f32,
                                     uint16_t* __restrict__ out_bf16) {
@@ -217,7 +218,7 @@ __global__ void skinny_final_kernel(const float* __restrict__ part, int64_t M, i
     for (int sp = 0; sp < splits; ++sp) sum += part[(static_cast<int64_t>(sp) * M + mo) * r + j];
   const float val = scale * sum;
   if (out_f32 != nullptr && j < r) out_f32[mo * r + j] = val;
-  if (out_bf16 != nullptr) out_bf16[idx] = f32_to_bf16_rne(scale2 * val);
+  if (out_bf16 != nullptr) out_bf16[idx] = to16<kF16>(scale2 * val);
 }
 
 // at (k x rpad) = A^T zero-padded; bt (rpad x n) = B^T zero-padded.
@@ -252,7 +253,7 @@ __global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint
 // all V loads issued first, and are summed in LDS in a fixed order. The
 // 16-rank slice of a U row is the same for every lane, so it is fetched with
 // scalar loads. kFull: r is a multiple of 16 (no rank tail).
-template <bool kFull>
+template <bool kFull, bool kF16>
 __global__ __launch_bounds__(1024) void rank_partial_kernel(const float* __restrict__ U, const uint16_t* __restrict__ V,
                                                             int64_t M, int64_t cn, int r, int splits,
                                                             float* __restrict__ part) {
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(1024) void rank_partial_kernel(const float* __restr
     for (int u = 0; u < kRows; ++u) {
       const int64_t m = m0 + kWaves * u;
       if (m >= me) break;  // uniform across the wave
-      const float v0 = __uint_as_float(v2[u] << 16), v1 = __uint_as_float(v2[u] & 0xFFFF0000u);
+      const float v0 = lo16<kF16>(v2[u]), v1 = hi16<kF16>(v2[u]);
       float uu[16];
       if (kFull) {
         const f32x4* up = reinterpret_cast<const f32x4*>(U + __builtin_amdgcn_readfirstlane(static_cast<int>(m)) *
@@ -379,6 +380,7 @@ __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+template <bool kF16>
 __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGradProblem p0, RankGradProblem p1,
                                                                         int64_t M, int splits, int64_t per) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[kRgStages * kRgV];
@@ -468,10 +470,10 @@ __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGrad
       const int row = 4 * (2 * e + half) + g;
       const float a = us[row * 16];
       const u32x2 xv = *reinterpret_cast<const u32x2*>(vs + row * kRgCols);
-      acc[0] = mfma_16x16x4_f32(a, __uint_as_float(xv[0] << 16), acc[0]);
-      acc[1] = mfma_16x16x4_f32(a, __uint_as_float(xv[0] & 0xFFFF0000u), acc[1]);
-      acc[2] = mfma_16x16x4_f32(a, __uint_as_float(xv[1] << 16), acc[2]);
-      acc[3] = mfma_16x16x4_f32(a, __uint_as_float(xv[1] & 0xFFFF0000u), acc[3]);
+      acc[0] = mfma_16x16x4_f32(a, lo16<kF16>(xv[0]), acc[0]);
+      acc[1] = mfma_16x16x4_f32(a, hi16<kF16>(xv[0]), acc[1]);
+      acc[2] = mfma_16x16x4_f32(a, lo16<kF16>(xv[1]), acc[2]);
+      acc[3] = mfma_16x16x4_f32(a, hi16<kF16>(xv[1]), acc[3]);
     }
     __syncthreads();  // the slot may be refilled
   }
@@ -522,10 +524,27 @@ __global__ void rank_grad_final_kernel(const float* __restrict__ part0, const fl
 
 template <int RT>
 void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r,
-                      int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits) {
+                      int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits, bool f16) {
   constexpr int kWaves = (RT <= 2) ? 16 : (RT <= 4 ? 8 : 4);
-  hipLaunchKernelGGL((skinny_kernel<RT, kWaves>), grid, dim3(kWaves * 64), 0, st, P, Q, m, qn, r, rpad, scale, scale2,
-                     out_f32, out_bf16, splits);
+  if (f16) {
+    hipLaunchKernelGGL((skinny_kernel<RT, kWaves, true>), grid, dim3(kWaves * 64), 0, st, P, Q, m, qn, r, rpad, scale,
+                       scale2, out_f32, out_bf16, splits);
+  } else {
+    hipLaunchKernelGGL((skinny_kernel<RT, kWaves, false>), grid, dim3(kWaves * 64), 0, st, P, Q, m, qn, r, rpad, scale,
+                       scale2, out_f32, out_bf16, splits);
+  }
+}
+
+template <bool kF16>
+void launch_proj(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r,
+                 int splits, int64_t per, float* part) {
+  if (r <= 16) {
+    hipLaunchKernelGGL((proj_kernel<1, kF16>), grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+  } else if (r <= 32) {
+    hipLaunchKernelGGL((proj_kernel<2, kF16>), grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+  } else {
+    hipLaunchKernelGGL((proj_kernel<4, kF16>), grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+  }
 }
 
 }  // namespace
@@ -570,26 +589,30 @@ int skinny_prefill_splits(int64_t m, int64_t qn, int r) {
 
 hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
                                  float scale, float scale2, float* part, float* out_f32, uint16_t* out_bf16,
-                                 hipStream_t st) {
+                                 hipStream_t st, bool f16) {
   const int splits = skinny_prefill_splits(m, qn, r);
   if (proj_fast(r)) {
     // columns per split: a multiple of the 128-column chunk
     const int64_t per = ((qn + splits - 1) / splits + kPjCols - 1) / kPjCols * kPjCols;
     const dim3 grid(static_cast<unsigned>((m + kPjRows - 1) / kPjRows), splits);
-    if (r <= 16) {
-      hipLaunchKernelGGL(proj_kernel<1>, grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
-    } else if (r <= 32) {
-      hipLaunchKernelGGL(proj_kernel<2>, grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+    if (f16) {
+      launch_proj<true>(grid, st, P, Q, m, qn, r, splits, per, part);
     } else {
-      hipLaunchKernelGGL(proj_kernel<4>, grid, dim3(384), 0, st, P, Q, m, qn, r, splits, per, part);
+      launch_proj<false>(grid, st, P, Q, m, qn, r, splits, per, part);
     }
   } else {
-    hipError_t e = launch_skinny(P, Q, m, qn, r, rpad, 1.0f, 1.0f, part, nullptr, splits, st);
+    hipError_t e = launch_skinny(P, Q, m, qn, r, rpad, 1.0f, 1.0f, part, nullptr, splits, st, f16);
     if (e != hipSuccess) return e;
   }
   const int64_t total = m * rpad;
-  hipLaunchKernelGGL(skinny_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, part, m,
-                     r, rpad, splits, scale, scale2, out_f32, out_bf16);
+  const dim3 fgrid(static_cast<unsigned>((total + 255) / 256));
+  if (f16) {
+    hipLaunchKernelGGL(skinny_final_kernel<true>, fgrid, dim3(256), 0, st, part, m, r, rpad, splits, scale, scale2,
+                       out_f32, out_bf16);
+  } else {
+    hipLaunchKernelGGL(skinny_final_kernel<false>, fgrid, dim3(256), 0, st, part, m, r, rpad, splits, scale, scale2,
+                       out_f32, out_bf16);
+  }
   return hipGetLastError();
 }
 
@@ -600,14 +623,14 @@ int skinny_splits(int64_t m, int64_t qn) {
 }
 
 hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad, float scale,
-                         float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s) {
+                         float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s, bool f16) {
   const dim3 grid(static_cast<unsigned>((m + 15) / 16), static_cast<unsigned>(splits));
   switch (rpad / 16) {
-    case 0: launch_skinny_rt<0>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
-    case 2: launch_skinny_rt<2>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
-    case 4: launch_skinny_rt<4>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
-    case 6: launch_skinny_rt<6>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
-    case 8: launch_skinny_rt<8>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits); break;
+    case 0: launch_skinny_rt<0>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits, f16); break;
+    case 2: launch_skinny_rt<2>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits, f16); break;
+    case 4: launch_skinny_rt<4>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits, f16); break;
+    case 6: launch_skinny_rt<6>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits, f16); break;
+    case 8: launch_skinny_rt<8>(grid, s, P, Q, m, qn, r, rpad, scale, scale2, out_f32, out_bf16, splits, f16); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -626,13 +649,21 @@ hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n
 }
 
 hipError_t launch_rank_reduce(const float* U, const uint16_t* V, int64_t m, int64_t cn, int r, float scale,
-                              int splits, float* part, float* out, int c_major, hipStream_t st) {
+                              int splits, float* part, float* out, int c_major, hipStream_t st, bool f16) {
   const dim3 grid(static_cast<unsigned>((cn + 127) / 128), static_cast<unsigned>((r + 15) / 16),
                   static_cast<unsigned>(splits));
   if (r % 16 == 0) {
-    hipLaunchKernelGGL(rank_partial_kernel<true>, grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+    if (f16) {
+      hipLaunchKernelGGL((rank_partial_kernel<true, true>), grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+    } else {
+      hipLaunchKernelGGL((rank_partial_kernel<true, false>), grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+    }
   } else {
-    hipLaunchKernelGGL(rank_partial_kernel<false>, grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+    if (f16) {
+      hipLaunchKernelGGL((rank_partial_kernel<false, true>), grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+    } else {
+      hipLaunchKernelGGL((rank_partial_kernel<false, false>), grid, dim3(1024), 0, st, U, V, m, cn, r, splits, part);
+    }
   }
   const int64_t total = static_cast<int64_t>(r) * cn;
   hipLaunchKernelGGL(rank_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, part, cn,
@@ -656,7 +687,7 @@ int rank_grad_splits(int64_t m, int64_t n, int64_t k, int r0, int r1) {
 
 hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, const float* h, const uint16_t* dy,
                              int64_t n, int64_t m, int r0, const LoraParts* parts, float scale, int splits, float* part,
-                             float* da, float* db, hipStream_t st) {
+                             float* da, float* db, hipStream_t st, bool f16) {
   // rows per split: a multiple of the 32-row chunk
   const int64_t per = ((m + splits - 1) / splits + kRgRows - 1) / kRgRows * kRgRows;
   LoraParts one;
@@ -668,8 +699,13 @@ hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, cons
   RankGradProblem p1{h, dy, n, part + static_cast<int64_t>(splits) * r0 * k, static_cast<int>((n + kRgCols - 1) / kRgCols),
                      r1, r0, parts != nullptr ? *parts : one};
   const int64_t wgs = (static_cast<int64_t>(p0.blocks) * (r0 / 16) + static_cast<int64_t>(p1.blocks) * (r1 / 16)) * splits;
-  hipLaunchKernelGGL(rank_grad_kernel, dim3(static_cast<unsigned>(wgs)), dim3((kRgWaves + 1) * 64), 0, st, p0, p1, m,
-                     splits, per);
+  if (f16) {
+    hipLaunchKernelGGL(rank_grad_kernel<true>, dim3(static_cast<unsigned>(wgs)), dim3((kRgWaves + 1) * 64), 0, st, p0,
+                       p1, m, splits, per);
+  } else {
+    hipLaunchKernelGGL(rank_grad_kernel<false>, dim3(static_cast<unsigned>(wgs)), dim3((kRgWaves + 1) * 64), 0, st, p0,
+                       p1, m, splits, per);
+  }
   const int64_t total = static_cast<int64_t>(r0) * k + static_cast<int64_t>(r1) * n;
   hipLaunchKernelGGL(rank_grad_final_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st,
                      p0.part, p1.part, k, n, r0, r1, splits, scale, da, db);

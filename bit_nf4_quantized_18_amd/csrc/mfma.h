@@ -21,6 +21,34 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  0, 0, 0);
 }
 
+// The same MFMA for either 16-bit compute type: bf16 (kF16 = false) or IEEE
+// half (v_mfma_f32_16x16x32_f16), operand layout unchanged.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+template <bool kF16>
+__device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+  if (kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  return mfma_16x16x32(a, b, c);
+}
+
+// Element 0 (low half) and 1 (high half) of a packed 16-bit pair as float32:
+// exact for both types.
+template <bool kF16>
+__device__ __forceinline__ float lo16(uint32_t v) {
+  if (kF16) return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v & 0xFFFFu)));
+  return __uint_as_float(v << 16);
+}
+template <bool kF16>
+__device__ __forceinline__ float hi16(uint32_t v) {
+  if (kF16) return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(v >> 16)));
+  return __uint_as_float(v & 0xFFFF0000u);
+}
+template <bool kF16>
+__device__ __forceinline__ float to_f32(uint16_t v) {
+  return lo16<kF16>(v);
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
@@ -51,6 +79,13 @@ __device__ __forceinline__ u32x4 ld8_bf16_window(const uint16_t* row_ptr, int j0
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// float32 -> the compute type, round to nearest even.
+template <bool kF16>
+__device__ __forceinline__ uint16_t to16(float f) {
+  if (kF16) return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+  return f32_to_bf16_rne(f);
 }
 
 }  // namespace qlora

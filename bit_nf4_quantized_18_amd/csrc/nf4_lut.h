@@ -81,6 +81,22 @@ __host__ __device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
 #endif
 }
 
+// The same pair conversion into either 16-bit compute type: bf16 (kF16 =
+// false) or IEEE half (v_cvt_pk_f16_f32, round to nearest even). The host
+// build models the bf16 form only.
+template <bool kF16>
+__host__ __device__ __forceinline__ uint32_t cvt_16x2(float lo, float hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (kF16) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const f2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+  }
+#endif
+  return cvt_bf16x2(lo, hi);
+}
+
 // fl32(k / 255) for an 8-bit scale code k, the double-quantization level
 // (Ultralytics glossary "QLoRA", "Come funziona QLoRA": the block scales are
 // themselves stored as 8-bit codes). One multiply by fl32(1/255) and one FMA
@@ -100,11 +116,14 @@ struct BlockLut {
   uint32_t th[4];  // high bytes of T[0..15]
 };
 
-// Build the tables for scale s. L holds the 16 float32 levels.
+// Build the tables for scale s. L holds the 16 float32 levels. kF16 selects
+// half-precision entries (fp16 compute) instead of bf16; the lookup below
+// only moves bytes, so it serves both.
+template <bool kF16 = false>
 __host__ __device__ __forceinline__ BlockLut make_block_lut(const float* L, float s) {
   uint32_t p[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) p[j] = cvt_bf16x2(L[2 * j] * s, L[2 * j + 1] * s);
+  for (int j = 0; j < 8; ++j) p[j] = cvt_16x2<kF16>(L[2 * j] * s, L[2 * j + 1] * s);
   BlockLut t;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {

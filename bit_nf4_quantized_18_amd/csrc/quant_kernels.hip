@@ -159,7 +159,9 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
 // Dequantize: each lane turns one 32-bit word of codes (8 weights) into 8
 // outputs per step; a wave covers 256 contiguous code bytes -> 1 KB of bf16
 // (or 2 KB of fp32) contiguous. Four steps per lane, all loads first.
-template <bool kF32, bool kDQ>
+// kOut: 0 = bf16, 1 = float32, 2 = IEEE half (both 16-bit forms round the
+// float32 value to nearest even).
+template <int kOut, bool kDQ>
 __global__ __launch_bounds__(256) void nf4_dequantize_kernel(PackedW w, void* __restrict__ out, Levels L) {
   __shared__ float lv[16];
   if (threadIdx.x < 16) lv[threadIdx.x] = L.v[threadIdx.x];
@@ -216,10 +218,14 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(PackedW w, void* __
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = lv[(cw[j] >> (4 * i)) & 0xF] * s;
     if (e0 + 8 <= numel) {
-      if (kF32) {
+      if (kOut == 1) {
         f32x4* o = reinterpret_cast<f32x4*>(static_cast<float*>(out) + e0);
         __builtin_nontemporal_store(f32x4{f[0], f[1], f[2], f[3]}, o);
         __builtin_nontemporal_store(f32x4{f[4], f[5], f[6], f[7]}, o + 1);
+      } else if (kOut == 2) {
+        const u32x4 o = {cvt_16x2<true>(f[0], f[1]), cvt_16x2<true>(f[2], f[3]), cvt_16x2<true>(f[4], f[5]),
+                         cvt_16x2<true>(f[6], f[7])};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e0));
       } else {
         const u32x4 o = {pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
                          pack_bf16x2(f[6], f[7])};
@@ -228,8 +234,10 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(PackedW w, void* __
     } else {
       for (int i = 0; i < 8; ++i) {
         if (e0 + i >= numel) break;
-        if (kF32) {
+        if (kOut == 1) {
           static_cast<float*>(out)[e0 + i] = f[i];
+        } else if (kOut == 2) {
+          static_cast<uint16_t*>(out)[e0 + i] = static_cast<uint16_t>(cvt_16x2<true>(f[i], 0.0f) & 0xFFFFu);
         } else {
           static_cast<uint16_t*>(out)[e0 + i] = static_cast<uint16_t>(bf16_rne_hi(f[i]) >> 16);
         }
@@ -254,12 +262,13 @@ hipError_t launch_quantize(const float* w, int64_t numel, int dq, int codebook, 
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const PackedW& w, int out_f32, void* out, hipStream_t s) {
+hipError_t launch_dequantize(const PackedW& w, int out_kind, void* out, hipStream_t s) {
   const int64_t numel = w.n * w.k;
   const int64_t nwords = (numel + 7) / 8;
   const unsigned grid = static_cast<unsigned>((nwords + 1023) / 1024);
-  auto kern = out_f32 ? (w.dq ? nf4_dequantize_kernel<true, true> : nf4_dequantize_kernel<true, false>)
-                      : (w.dq ? nf4_dequantize_kernel<false, true> : nf4_dequantize_kernel<false, false>);
+  auto kern = out_kind == 1   ? (w.dq ? nf4_dequantize_kernel<1, true> : nf4_dequantize_kernel<1, false>)
+              : out_kind == 2 ? (w.dq ? nf4_dequantize_kernel<2, true> : nf4_dequantize_kernel<2, false>)
+                              : (w.dq ? nf4_dequantize_kernel<0, true> : nf4_dequantize_kernel<0, false>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, w, out, codebook_table(w.codebook));
   return hipGetLastError();
 }

@@ -81,7 +81,7 @@ typedef enum {
   QLORA_ERR_HIP = -6          /* a kernel launch failed                         */
 } qlora_status;
 
-typedef enum { QLORA_BF16 = 0, QLORA_F32 = 1 } qlora_dtype;
+typedef enum { QLORA_BF16 = 0, QLORA_F32 = 1, QLORA_F16 = 2 } qlora_dtype;
 
 #define QLORA_BLOCK 64     /* weights per absmax block              */
 #define QLORA_DQ_GROUP 256 /* blocks per double-quantization group  */
@@ -138,7 +138,8 @@ qlora_status qlora_quantize_codebook(const float* w, int64_t numel, int double_q
                                      float* absmax, hipStream_t stream);
 
 /* Dequantize a packed weight to bf16 (w16) or float32 (w32), n*k elements,
- * row-major, into `out`. Ultralytics glossary "QLoRA", "Come funziona QLoRA"
+ * row-major, into `out`; QLORA_F16 gives the IEEE-half rounding (nearest
+ * even) of w32 instead, the weight of the fp16 compute calls. Ultralytics glossary "QLoRA", "Come funziona QLoRA"
  * (restore = level[code] * scale; dequantize to bfloat16 before the matmul).
  * Any n, k >= 1 (k need not be a multiple of 64 here).
  * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED (dtype) / HIP. */
@@ -181,6 +182,23 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, cons
                               int64_t m, const uint16_t* a, const uint16_t* b, int r, float alpha,
                               const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
                               size_t ws_bytes, hipStream_t stream);
+
+/* The same two calls with IEEE half as the 16-bit compute type ("Modulo 4:
+ * QLoRA", section "QLoRA combina tres componentes clave": the LoRA weights
+ * stay in full 16-bit precision, BF16 or FP16): X, A, B, dY, Y and dX are
+ * fp16 (uint16_t bit patterns), the weight is dequantized to fp16
+ * (round-to-nearest-even of w32) inside the matmuls, and the f16 matrix-core
+ * instructions accumulate in float32. H, dA and dB stay float32. Arguments,
+ * layouts, limits, workspace (qlora_linear_workspace_bytes) and errors are
+ * those of qlora_linear_fwd / qlora_linear_bwd. */
+qlora_status qlora_linear_fwd_f16(const qlora_nf4_weight* w, const uint16_t* x, int64_t m,
+                                  const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                  uint16_t* y, float* h_out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+qlora_status qlora_linear_bwd_f16(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                                  int64_t m, const uint16_t* a, const uint16_t* b, int r,
+                                  float alpha, const float* h_saved, uint16_t* dx, float* da,
+                                  float* db, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Forward and backward with dropout on the adapter path ("LoRA y QLoRA en
  * Profundidad", "Dropout (lora_dropout)": the LoRA layers randomly zero

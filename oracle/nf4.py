@@ -198,6 +198,13 @@ def quantize(w: np.ndarray, double_quant: bool = True, levels: np.ndarray | None
 # ---------------------------------------------------------------------------
 # Dequantization [U]
 # ---------------------------------------------------------------------------
+def f16_rne_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to IEEE half, nearest-even (subnormals kept), returned as
+    uint16 bit patterns: the weight of the fp16 compute variant."""
+    with np.errstate(over="ignore"):  # past 65504 rounds to infinity, as IEEE says
+        return np.asarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def bf16_rne_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16, nearest-even, returned as uint16 bit patterns
     (finite inputs only)."""

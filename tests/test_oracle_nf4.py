@@ -357,6 +357,22 @@ def test_dq_mse_increase_is_small():
 
 
 # --- bf16 rounding ----------------------------------------------------------
+def test_f16_rounding_matches_torch():
+    """The half rounding of the fp16 variant against torch's conversion, on
+    random values, ties, subnormals and values past the half range."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.Generator(np.random.PCG64(19))
+    x = np.concatenate([
+        (rng.standard_normal(20000) * 0.02).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-6).astype(np.float32),             # half subnormals
+        np.array([1 + 2 ** -11, 1 + 3 * 2 ** -11, 2 ** -24, 2 ** -25, 3 * 2 ** -26, 65504.0, 65520.0,
+                  -0.0, 0.0, 6.1e-5], dtype=np.float32),                  # ties, smallest subnormal, overflow edge
+    ])
+    got = O.f16_rne_bits(x)
+    ref = torch.from_numpy(x).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)
+
+
 def test_bf16_rounding_matches_torch():
     torch = pytest.importorskip("torch")
     rng = np.random.Generator(np.random.PCG64(2))
