@@ -36,6 +36,11 @@ Readings where the pages are silent (each also listed in the design doc):
   * the 8-bit scale code is the unsigned linear codebook U_k = k/255 on
     [0, 1] times the group absmax M_g, encoded by the same nearest-level rule
     (parity unpinned: the pages say only "8 bit in blocks of 256");
+  * an alternative, float-like 8-bit scale code (double_quant = 2): the
+    unsigned 4-bit-exponent / 4-bit-mantissa values E_c, c = 16 e + m,
+    E = m 2^-18 for e = 0 and (16 + m) 2^(e - 19) otherwise, so E_240 = 1 and
+    codes 241..255 (above 1) are never chosen; same nearest-level rule
+    (parity unpinned like the linear code: the pages fix only "8 bit");
   * the weights are encoded with their exact block absmax; the decoded scale
     s_b = fl32(U[c2_b] * M_g) is what dequantization uses;
   * dequantized value = fl32(L[code] * s_b), then round-to-nearest-even bf16.
@@ -83,6 +88,23 @@ def int4_levels() -> np.ndarray:
     value and rounds it; a float32-stepped linspace may differ in the last
     bits)."""
     return np.linspace(-1.0, 1.0, 16, dtype=np.float32)
+
+
+def e4m4_scale_levels() -> np.ndarray:
+    """E_c for c = 0..255: a float-like unsigned 8-bit code with 4 exponent
+    and 4 mantissa bits whose code 240 is exactly 1 (the group maximum).
+    Every value is a small integer times a power of two, so float32 holds it
+    exactly."""
+    c = np.arange(256)
+    e, m = c >> 4, c & 15
+    val = np.where(e == 0, m * 2.0 ** -18, (16 + m) * np.exp2(e - 19.0))
+    return val.astype(np.float32)
+
+
+def scale_levels(double_quant: int) -> np.ndarray:
+    """The 8-bit scale codebook of a double-quantization mode: 1 linear k/255,
+    2 the float-like E4M4 values."""
+    return e4m4_scale_levels() if int(double_quant) == 2 else u8_scale_levels()
 
 
 def u8_scale_levels() -> np.ndarray:
@@ -151,7 +173,7 @@ def unpack_nibbles(packed: np.ndarray, numel: int) -> np.ndarray:
     return out[:numel]
 
 
-def double_quantize(absmax: np.ndarray):
+def double_quantize(absmax: np.ndarray, scale_table: np.ndarray | None = None):
     """Second level [U], [M]: per group of 256 blocks, M_g = max a_b; each
     a_b / M_g is encoded to the nearest U_k. Returns (c2 uint8, M_g float32)."""
     absmax = np.asarray(absmax, dtype=np.float32)
@@ -164,19 +186,21 @@ def double_quantize(absmax: np.ndarray):
     x2 = np.zeros(nb, dtype=np.float32)
     nz = mg > 0
     x2[nz] = absmax[nz] / mg[nz]
-    c2 = encode_nearest(x2, u8_scale_levels())
+    c2 = encode_nearest(x2, u8_scale_levels() if scale_table is None else scale_table)
     return c2, group_max
 
 
-def decode_scales(c2: np.ndarray, group_max: np.ndarray) -> np.ndarray:
+def decode_scales(c2: np.ndarray, group_max: np.ndarray, scale_table: np.ndarray | None = None) -> np.ndarray:
     """s_b = fl32(U[c2_b] * M_g)."""
     c2 = np.asarray(c2, dtype=np.uint8)
     mg = np.repeat(np.asarray(group_max, dtype=np.float32), DQ_GROUP)[: c2.size]
-    return u8_scale_levels()[c2] * mg
+    return (u8_scale_levels() if scale_table is None else scale_table)[c2] * mg
 
 
-def quantize(w: np.ndarray, double_quant: bool = True, levels: np.ndarray | None = None) -> dict:
-    """Full quantizer. Weights first (with exact a_b), then the scales [M]."""
+def quantize(w: np.ndarray, double_quant: bool | int = True, levels: np.ndarray | None = None) -> dict:
+    """Full quantizer. Weights first (with exact a_b), then the scales [M].
+    double_quant: 0/False none, 1/True the linear 8-bit code, 2 the
+    float-like E4M4 code."""
     if levels is None:
         levels = nf4_levels()
     w = np.asarray(w, dtype=np.float32).reshape(-1)
@@ -185,11 +209,13 @@ def quantize(w: np.ndarray, double_quant: bool = True, levels: np.ndarray | None
     absmax = block_absmax(w)
     codes = encode_nearest(normalize(w, absmax), levels)
     out = {"numel": w.size, "codes": pack_nibbles(codes), "absmax": absmax, "double_quant": bool(double_quant)}
+    out["dq_mode"] = int(double_quant)
     if double_quant:
-        c2, mg = double_quantize(absmax)
+        table = scale_levels(double_quant)
+        c2, mg = double_quantize(absmax, table)
         out["scale_codes"] = c2
         out["group_scale"] = mg
-        out["scales"] = decode_scales(c2, mg)
+        out["scales"] = decode_scales(c2, mg, table)
     else:
         out["scales"] = absmax
     return out

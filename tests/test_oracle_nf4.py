@@ -346,6 +346,66 @@ def test_dq_codes_match_exact_rational_argmin():
         assert c2[b] == best
 
 
+def test_e4m4_scale_table():
+    """The float-like scale code: strictly increasing, 0 at code 0, exactly 1
+    at code 240 (codes above exceed 1), powers of two at each exponent step,
+    every value the exact dyadic rational of its definition, and a relative
+    spacing of at most 1/16 above the subnormal codes."""
+    E = O.e4m4_scale_levels()
+    assert E.dtype == np.float32 and E.size == 256
+    assert np.all(np.diff(E.astype(np.float64)) > 0)
+    assert E[0] == 0 and E[240] == 1.0 and np.all(E[241:] > 1)
+    for e in range(1, 16):
+        assert E[16 * e] == np.float32(2.0 ** (e - 15))
+    for c in range(256):
+        e, m = c >> 4, c & 15
+        want = Fraction(m, 2 ** 18) if e == 0 else Fraction(16 + m) * Fraction(2) ** (e - 19)
+        assert Fraction(float(E[c])) == want, c
+    rel = np.diff(E[16:241].astype(np.float64)) / E[16:240].astype(np.float64)
+    assert rel.max() <= 1 / 16 + 1e-12
+
+
+def test_e4m4_codes_match_exact_rational_argmin_and_bound():
+    """Double quantization with the float-like code: codes equal the exact
+    rational argmin (ties low), the decoded scale is within 1/32 relative of
+    a_b wherever a_b / M_g >= 2^-14, and the group maximum decodes exactly."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    a = (np.abs(rng.standard_normal(256 * 2)) * 0.03 + 1e-6).astype(np.float32)
+    a[:60] = (a.max() * np.float32(2.0) ** -rng.uniform(0, 16, 60)).astype(np.float32)  # many binades
+    E = O.e4m4_scale_levels()
+    c2, mg = O.double_quantize(a, E)
+    EF = [Fraction(float(v)) for v in E]
+    for b in range(a.size):
+        M = Fraction(float(mg[b // 256]))
+        x = round_fp32(Fraction(float(a[b])) / M)
+        best, bd = None, None
+        for k, u in enumerate(EF):
+            d = round_fp32(abs(x - u))
+            if bd is None or d < bd:
+                best, bd = k, d
+        assert c2[b] == best, b
+    s = O.decode_scales(c2, mg, E).astype(np.float64)
+    mgr = np.repeat(mg.astype(np.float64), 256)[: a.size]
+    big = a / mgr >= 2.0 ** -14
+    assert np.all(np.abs(s[big] - a[big]) <= a[big] / 32 * (1 + 1e-6))
+    assert np.all(c2[a == mgr] == 240)
+
+
+def test_e4m4_beats_linear_on_small_ratios():
+    """Where an outlier makes most blocks small next to the group maximum
+    (ratios below 1/16), the float-like code's worst relative scale error is
+    below the linear code's -- the reason for the variant."""
+    rng = np.random.Generator(np.random.PCG64(24))
+    w = (rng.standard_normal(64 * 256 * 4) * 0.02).astype(np.float32)
+    w[rng.choice(w.size, 4, replace=False)] = 2.0  # one huge outlier per group, ratios about 0.03
+    errs = {}
+    for mode in (1, 2):
+        q = O.quantize(w, mode)
+        a, s = q["absmax"].astype(np.float64), q["scales"].astype(np.float64)
+        errs[mode] = float(np.max(np.abs(s - a) / a))
+    assert errs[2] < errs[1]
+
+
 def test_dq_mse_increase_is_small():
     rng = np.random.Generator(np.random.PCG64(9))
     w = (rng.standard_normal(64 * 256 * 8) * 0.02).astype(np.float32)
