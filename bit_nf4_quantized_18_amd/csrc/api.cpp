@@ -92,7 +92,7 @@ struct DropArg {
 
 qlora_status check_weight(const qlora_nf4_weight* w, bool linear) {
   if (w == nullptr || w->codes == nullptr) return QLORA_ERR_NULL;
-  if (w->double_quant != 0 && w->double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (w->double_quant < 0 || w->double_quant > 2) return QLORA_ERR_UNSUPPORTED;
   if (w->codebook != QLORA_CODEBOOK_NF4 && w->codebook != QLORA_CODEBOOK_INT4) return QLORA_ERR_UNSUPPORTED;
   if (w->double_quant) {
     if (w->scale_codes == nullptr || w->group_scale == nullptr) return QLORA_ERR_NULL;
@@ -176,7 +176,7 @@ size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int
 
 qlora_status qlora_quantize_codebook(const float* w, int64_t numel, int double_quant, int codebook, uint8_t* codes,
                                 uint8_t* scale_codes, float* group_scale, float* absmax, hipStream_t stream) {
-  if (double_quant != 0 && double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (double_quant < 0 || double_quant > 2) return QLORA_ERR_UNSUPPORTED;
   if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_INT4) return QLORA_ERR_UNSUPPORTED;
   if (w == nullptr || codes == nullptr) return QLORA_ERR_NULL;
   if (double_quant && (scale_codes == nullptr || group_scale == nullptr)) return QLORA_ERR_NULL;
@@ -479,7 +479,7 @@ qlora_status qlora_requantize(const qlora_nf4_weight* w, const uint16_t* a, cons
   if (st != QLORA_OK) return st;
   if (w->k % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
   if ((st = check_adapter(a, b, r)) != QLORA_OK) return st;
-  if (double_quant != 0 && double_quant != 1) return QLORA_ERR_UNSUPPORTED;
+  if (double_quant < 0 || double_quant > 2) return QLORA_ERR_UNSUPPORTED;
   if (codebook != QLORA_CODEBOOK_NF4 && codebook != QLORA_CODEBOOK_INT4) return QLORA_ERR_UNSUPPORTED;
   if (merged == nullptr || codes == nullptr) return QLORA_ERR_NULL;
   if (double_quant && (scale_codes == nullptr || group_scale == nullptr)) return QLORA_ERR_NULL;

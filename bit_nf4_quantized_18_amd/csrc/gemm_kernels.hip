@@ -175,7 +175,7 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
       }
     };
     auto store_w = [&](int kt, u32x4 c, uint32_t sc, float gs) {
-      const float s = kDQ ? u8_unit(sc) * gs : gs;
+      const float s = kDQ ? dq_unit(sc, w.dq) * gs : gs;
       const BlockLut lut = make_block_lut<kF16>(L.v, wk_ok ? s : 0.0f);
       uint16_t* bs = Bs + (kt % kStages) * kBStage;
 #pragma unroll

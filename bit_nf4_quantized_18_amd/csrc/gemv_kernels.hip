@@ -159,7 +159,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     // wave-uniform: skip a pass slot no lane group of this wave uses
     if (base + wave * 4 < nbk) {
       const bool ok = (n < N) && (kb < nbk);
-      const float sc = kDQ ? u8_unit(scode) * gsc : gsc;
+      const float sc = kDQ ? dq_unit(scode, w.dq) * gsc : gsc;
       const BlockLut lut = make_block_lut<kF16>(L.v, ok ? sc : 0.0f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
     if (wave * 4 < nbk) {
       const int n = rg * 16 + i;
       const bool ok = (n < N) && kval;
-      const float sc = kDQ ? u8_unit(Tc.scode) * Tc.gsc : Tc.gsc;
+      const float sc = kDQ ? dq_unit(Tc.scode, w.dq) * Tc.gsc : Tc.gsc;
       const BlockLut lut = make_block_lut<kF16>(L.v, ok ? sc : 0.0f);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs g, Levels L) {
     if (kSrc == kPacked) {
       const uint32_t cw = *reinterpret_cast<const uint32_t*>(g.w.codes + e0 / 2);
       const int64_t blk = e0 / kBlock;
-      const float sc = g.w.dq ? u8_unit(g.w.scale_codes[blk]) * g.w.group_scale[blk / kGroup] : g.w.absmax[blk];
+      const float sc =
+          g.w.dq ? dq_unit(g.w.scale_codes[blk], g.w.dq) * g.w.group_scale[blk / kGroup] : g.w.absmax[blk];
 #pragma unroll
       for (int c = 0; c < 8; ++c) base[c] = bf16_hi(bf16_rne_hi(lv[(cw >> (4 * c)) & 0xF] * sc));
     } else if (kSrc == kDenseBf16) {

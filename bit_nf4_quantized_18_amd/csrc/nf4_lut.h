@@ -111,6 +111,28 @@ __host__ __device__ __forceinline__ float u8_unit(uint32_t k) {
   return fmaf(r, c, q0);
 }
 
+// E_c of the float-like 8-bit scale code (double_quant = 2): c = 16 e + m,
+// E = m 2^-18 for e = 0 and (16 + m) 2^(e - 19) = (1 + m/16) 2^(e - 15)
+// otherwise, built exactly from its float32 bits (exponent field e + 112,
+// top mantissa bits m). Code 240 is exactly 1.
+__host__ __device__ __forceinline__ float e4m4_unit(uint32_t c) {
+  const uint32_t e = c >> 4, m = c & 15u;
+  const uint32_t bits = ((e + 112u) << 23) | (m << 19);
+  float nrm;
+#if defined(__HIP_DEVICE_COMPILE__)
+  nrm = __uint_as_float(bits);
+#else
+  __builtin_memcpy(&nrm, &bits, 4);
+#endif
+  return e == 0 ? static_cast<float>(m) * 3.814697265625e-06f : nrm;  // 2^-18
+}
+
+// The scale unit of a double-quantization mode: 2 the float-like code,
+// otherwise (1) the linear k / 255.
+__host__ __device__ __forceinline__ float dq_unit(uint32_t c, int mode) {
+  return mode == 2 ? e4m4_unit(c) : u8_unit(c);
+}
+
 struct BlockLut {
   uint32_t tl[4];  // low bytes of T[0..15], 4 per dword
   uint32_t th[4];  // high bytes of T[0..15]

@@ -54,6 +54,25 @@ __device__ __forceinline__ uint32_t nearest_u8(float x2) {
   return best;
 }
 
+// Nearest E_c (the float-like code, nf4_lut.h) to x2 in [0, 1], lowest c on
+// ties. c0, the largest code with E_c0 <= x2, comes from x2's bits: below
+// 2^-14 it is floor(x2 2^18) (exact scaling), above it the exponent and the
+// top 4 mantissa bits; the nearest is c0 or c0 + 1 (farther codes are at
+// least one spacing away, about x2 / 16). x2 = 1 gives c0 = 240, E = 1.
+__device__ __forceinline__ uint32_t nearest_e4m4(float x2) {
+  uint32_t c0;
+  if (x2 < 6.103515625e-05f) {  // 2^-14
+    c0 = static_cast<uint32_t>(x2 * 262144.0f);
+  } else {
+    const uint32_t b = __float_as_uint(x2);
+    c0 = (((b >> 23) - 112u) << 4) | ((b >> 19) & 15u);
+  }
+  if (c0 >= 240u) return 240u;
+  const float d_lo = x2 - e4m4_unit(c0);
+  const float d_hi = e4m4_unit(c0 + 1) - x2;
+  return (d_hi < d_lo) ? c0 + 1 : c0;
+}
+
 // One workgroup (256 threads) per double-quantization group of 256 blocks.
 // Wave w owns blocks [64w, 64w + 64) of the group, 8 at a time: 8 lanes per
 // block, 8 consecutive elements per lane (two 16-byte loads), so a wave reads
@@ -150,7 +169,7 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
     if (absmax_out != nullptr) absmax_out[b] = a;
     if (dq) {
       const float x2 = (mg > 0.0f) ? a / mg : 0.0f;
-      scale_codes[b] = static_cast<uint8_t>(nearest_u8(x2));
+      scale_codes[b] = static_cast<uint8_t>(dq == 2 ? nearest_e4m4(x2) : nearest_u8(x2));
     }
   }
   if (dq && tid == 0) group_scale[g] = mg;
@@ -213,7 +232,7 @@ __global__ __launch_bounds__(256) void nf4_dequantize_kernel(PackedW w, void* __
     const int64_t q = base + j * 256;
     if (q >= nwords) continue;
     const int64_t e0 = q * 8;
-    const float s = kDQ ? u8_level(sc8[j]) * sc32[j] : sc32[j];
+    const float s = kDQ ? (w.dq == 2 ? e4m4_unit(sc8[j]) : u8_level(sc8[j])) * sc32[j] : sc32[j];
     float f[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) f[i] = lv[(cw[j] >> (4 * i)) & 0xF] * s;

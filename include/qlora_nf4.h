@@ -33,7 +33,12 @@
  *   - double quantization: M_g = max a_b over group g; c2_b = argmin_k
  *     fl32(|a_b / M_g - U_k|) with U_k = fl32(k / 255), lowest k on ties
  *     (c2_b = 0 when M_g = 0); decoded scale s_b = fl32(U[c2_b] * M_g);
- *     without double quantization s_b = a_b stored as float32;
+ *     without double quantization s_b = a_b stored as float32. double_quant
+ *     = 2 selects a float-like 8-bit code instead of k/255: E_c, c = 16 e +
+ *     m, is m 2^-18 for e = 0 and (16 + m) 2^(e - 19) otherwise (E_240 = 1;
+ *     codes above 240 exceed 1 and are never chosen), with the same nearest
+ *     rule; s_b = fl32(E[c2_b] * M_g). Its relative scale error stays below
+ *     1/32 down to a_b / M_g = 2^-14, where k/255 degrades for small ratios;
  *   - dequantized weight: w32 = fl32(L[code] * s_b); w16 = bf16 round-to-
  *     nearest-even of w32. Codes, c2, M_g, w32 and w16 are bit-exact with the
  *     CPU oracle;
@@ -88,13 +93,17 @@ typedef enum { QLORA_BF16 = 0, QLORA_F32 = 1, QLORA_F16 = 2 } qlora_dtype;
 #define QLORA_MAX_RANK 128 /* largest LoRA rank r the kernels take  */
 #define QLORA_MAX_PARTS 4  /* most linears in one grouped call      */
 
+#define QLORA_DQ_NONE 0    /* fp32 absmax per block                 */
+#define QLORA_DQ_LINEAR8 1 /* 8-bit scale codes k / 255 (default)   */
+#define QLORA_DQ_FLOAT8 2  /* 8-bit float-like scale codes E_c      */
+
 #define QLORA_CODEBOOK_NF4 0  /* normal-quantile levels (the default)  */
 #define QLORA_CODEBOOK_INT4 1 /* 16 evenly spaced levels on [-1, 1]    */
 
 /* A packed NF4 weight W (n x k, row-major, numel = n * k). Device pointers.
  *   codes        : ceil(numel / 2) bytes, packing as above.
- *   scale_codes  : double_quant = 1: ceil(numel / 64) uint8 codes c2_b.
- *   group_scale  : double_quant = 1: ceil(ceil(numel / 64) / 256) float M_g.
+ *   scale_codes  : double_quant = 1 or 2: ceil(numel / 64) uint8 codes c2_b.
+ *   group_scale  : double_quant = 1 or 2: ceil(ceil(numel / 64) / 256) float M_g.
  *   absmax       : double_quant = 0: ceil(numel / 64) float a_b.
  *   codebook     : QLORA_CODEBOOK_NF4 or QLORA_CODEBOOK_INT4, the level table
  *                  the codes index (a zero-initialised struct selects NF4).
@@ -120,7 +129,8 @@ typedef struct {
  *     if given receives the exact float a_b.
  *   double_quant = 0: absmax (ceil(numel/64) floats) is required;
  *     scale_codes and group_scale are ignored.
- * Errors: NULL / ALIGN / SHAPE (numel < 1) / UNSUPPORTED (flag not 0 or 1) / HIP. */
+ * double_quant = 2 is the same with the float-like scale code (QLORA_DQ_FLOAT8).
+ * Errors: NULL / ALIGN / SHAPE (numel < 1) / UNSUPPORTED (flag not 0, 1 or 2) / HIP. */
 qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant, uint8_t* codes,
                                 uint8_t* scale_codes, float* group_scale, float* absmax,
                                 hipStream_t stream);

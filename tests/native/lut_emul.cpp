@@ -23,3 +23,8 @@ extern "C" int u8_unit_emul(float* out) {
   for (uint32_t k = 0; k < 256; ++k) out[k] = qlora::u8_unit(k);
   return 256;
 }
+
+extern "C" int e4m4_unit_emul(float* out) {
+  for (uint32_t c = 0; c < 256; ++c) out[c] = qlora::e4m4_unit(c);
+  return 256;
+}

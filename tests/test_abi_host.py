@@ -81,7 +81,7 @@ def wstruct(n=64, k=64, dq=1, codes=P, sc=P, gs=P, am=None, codebook=0):
 def test_quantize_argument_errors():
     lib = binding.load()
     q = lib.qlora_nf4_quantize
-    assert q(P, 100, 2, P, P, P, None, None) == -4
+    assert q(P, 100, 3, P, P, P, None, None) == -4
     assert q(None, 100, 1, P, P, P, None, None) == -1
     assert q(P, 100, 1, P, None, P, None, None) == -1
     assert q(P, 100, 0, P, None, None, None, None) == -1
@@ -92,7 +92,7 @@ def test_quantize_argument_errors():
     qc = lib.qlora_quantize_codebook
     assert qc(P, 100, 1, 2, P, P, P, None, None) == -4
     assert qc(P, 100, 1, -1, P, P, P, None, None) == -4
-    assert qc(P, 100, 2, 1, P, P, P, None, None) == -4
+    assert qc(P, 100, 3, 1, P, P, P, None, None) == -4
     assert qc(None, 100, 1, 1, P, P, P, None, None) == -1
     assert qc(P, 0, 1, 1, P, P, P, None, None) == -2
     assert qc(P, 100, 1, 1, P + 8, P, P, None, None) == -3

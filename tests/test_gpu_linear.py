@@ -93,6 +93,19 @@ def test_linear_parity_int4(gpu_lib, case):
     _run_case(gpu_lib, *case, codebook=1)
 
 
+# The float-like 8-bit scale code (double_quant = 2) on every path.
+FLOAT8_CASES = [
+    ("f8scale_ragged_m300_n272_k320_r8", 300, 272, 320, 8, 16.0, 2),
+    ("f8scale_decode_m1_r8", 1, 256, 256, 8, 16.0, 2),
+    ("f8scale_decode_long_k_m2", 2, 64, 16384, 16, 32.0, 2),
+]
+
+
+@pytest.mark.parametrize("case", FLOAT8_CASES, ids=[c[0] for c in FLOAT8_CASES])
+def test_linear_parity_float8_scales(gpu_lib, case):
+    _run_case(gpu_lib, *case)
+
+
 @pytest.mark.parametrize("m", [1, 4, 16])
 @pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096)])
 def test_decode_7b_shapes(gpu_lib, m, n, k):

@@ -19,6 +19,7 @@ CASES = [
     ("r128", 40, 512, 128, 64.0, True, 0),
     ("r0", 24, 192, 0, 0.0, True, 0),
     ("int4_r16", 80, 640, 16, 32.0, True, 1),
+    ("float8_scales_r16", 64, 512, 16, 32.0, 2, 0),
     ("attn_4096x4096_r16", 4096, 4096, 16, 32.0, True, 0),
     ("mlp_11008x4096_r16", 11008, 4096, 16, 32.0, True, 0),
 ]

@@ -171,3 +171,27 @@ def test_quantize_deterministic(gpu_lib):
     a = gpu_lib.quantize(w)
     b = gpu_lib.quantize(w)
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scale_codes, b.scale_codes)
+
+
+@pytest.mark.parametrize("name", ["single_256x256", "attn_4096x4096_outliers", "ragged_1d", "numel_65", "denormals",
+                                  "zeros", "ties"])
+def test_float8_scale_code_bit_exact(gpu_lib, name):
+    """double_quant = 2 (the float-like scale code): scale codes, group
+    maxima, codes and dequantized values bit-equal to the oracle's."""
+    import torch
+
+    w = CASES[name]()
+    say(f"[quantize dq=2] case={name} numel={w.size}")
+    ref = O.quantize(w.reshape(-1), 2)
+    q = gpu_lib.quantize(torch.from_numpy(np.ascontiguousarray(w)).cuda(), double_quant=2, keep_absmax=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(_u8(q.codes), ref["codes"])
+    assert np.array_equal(_u8(q.scale_codes), ref["scale_codes"])
+    assert np.array_equal(_f32bits(q.group_scale), ref["group_scale"].view(np.uint32))
+    q.absmax = None
+    w32_ref, bits_ref = O.dequantize(ref)
+    d16 = gpu_lib.dequantize(q, torch.bfloat16)
+    d32 = gpu_lib.dequantize(q, torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(d16.reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16), bits_ref)
+    assert np.array_equal(d32.reshape(-1).cpu().numpy().view(np.uint32), w32_ref.view(np.uint32))

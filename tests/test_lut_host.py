@@ -70,3 +70,12 @@ def test_scale_code_unit_is_correctly_rounded(emul):
     f.argtypes = [ctypes.c_void_p]
     assert f(out.ctypes.data) == 256
     assert np.array_equal(out.view(np.uint32), O.u8_scale_levels().astype(np.float32).view(np.uint32))
+
+
+def test_e4m4_unit_matches_oracle_table(emul):
+    """The kernels' bit-built float-like scale values equal the oracle's."""
+    out = np.zeros(256, np.float32)
+    f = emul.e4m4_unit_emul
+    f.argtypes = [ctypes.c_void_p]
+    assert f(out.ctypes.data) == 256
+    assert np.array_equal(out.view(np.uint32), O.e4m4_scale_levels().view(np.uint32))

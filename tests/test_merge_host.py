@@ -25,7 +25,7 @@ def test_merge_argument_errors():
     assert f(w, P, P, 8, 16.0, 0, P + 4, None) == -3
     assert f(ctypes.byref(wstruct(k=100)), P, P, 8, 16.0, 0, P, None) == -2  # k % 64
     assert f(ctypes.byref(wstruct(codebook=3)), P, P, 8, 16.0, 0, P, None) == -4
-    assert f(ctypes.byref(wstruct(dq=2)), P, P, 8, 16.0, 0, P, None) == -4
+    assert f(ctypes.byref(wstruct(dq=3)), P, P, 8, 16.0, 0, P, None) == -4
     assert f(None, P, P, 8, 16.0, 0, P, None) == -1
 
 
@@ -44,7 +44,7 @@ def test_unmerge_argument_errors():
 def test_requantize_argument_errors():
     f = binding.load().qlora_requantize
     w = ctypes.byref(wstruct())
-    assert f(w, P, P, 8, 16.0, 2, 0, P, P, P, P, None, None) == -4   # dq flag
+    assert f(w, P, P, 8, 16.0, 3, 0, P, P, P, P, None, None) == -4   # dq flag
     assert f(w, P, P, 8, 16.0, 1, 4, P, P, P, P, None, None) == -4   # codebook
     assert f(w, P, P, 8, 16.0, 1, 0, None, P, P, P, None, None) == -1
     assert f(w, P, P, 8, 16.0, 1, 0, P, P, None, P, None, None) == -1
