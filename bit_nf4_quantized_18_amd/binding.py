@@ -27,7 +27,9 @@ EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "ql
            "qlora_linear_grouped_workspace_bytes", "qlora_status_string", "qlora_nf4_levels",
            "qlora_quantize_codebook", "qlora_codebook_levels", "qlora_merge", "qlora_unmerge",
            "qlora_requantize", "qlora_linear_dropout_workspace_bytes", "qlora_linear_fwd_dropout",
-           "qlora_linear_bwd_dropout", "qlora_dropout_mask", "qlora_linear_fwd_f16", "qlora_linear_bwd_f16")
+           "qlora_linear_bwd_dropout", "qlora_dropout_mask", "qlora_linear_fwd_f16", "qlora_linear_bwd_f16",
+           "qlora_linear_fwd_grouped_f16", "qlora_linear_bwd_grouped_f16", "qlora_linear_fwd_dropout_f16",
+           "qlora_linear_bwd_dropout_f16")
 
 CODEBOOK_NF4 = 0   # normal-quantile levels
 CODEBOOK_INT4 = 1  # 16 evenly spaced levels on [-1, 1]
@@ -101,6 +103,12 @@ def load():
     lib.qlora_linear_bwd_dropout.restype = i32
     lib.qlora_dropout_mask.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i64, f32, vp, vp]
     lib.qlora_dropout_mask.restype = i32
+    # the fp16 compute calls share their bf16 counterparts' signatures
+    for name in ("grouped", "dropout"):
+        for d in ("fwd", "bwd"):
+            f16 = getattr(lib, f"qlora_linear_{d}_{name}_f16")
+            f16.argtypes = getattr(lib, f"qlora_linear_{d}_{name}").argtypes
+            f16.restype = i32
     _LIB = lib
     return lib
 
@@ -360,12 +368,13 @@ def linear_fwd_dropout(q: PackedNF4, x, a, b, alpha: float, keep, p: float, want
     import torch
 
     m, r, dev = x.shape[0], a.shape[0], x.device
-    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=dev)
+    y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=dev)
     h = h_out if h_out is not None else (torch.empty((m, r), dtype=torch.float32, device=dev) if want_h else None)
     ws, nbytes = _drop_ws(ws, m, q.n, q.k, r, dev)
     wc = q.c_struct()
-    st = load().qlora_linear_fwd_dropout(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
-                                         _ptr(keep), float(p), _ptr(y), _ptr(h), _ptr(ws), nbytes, _stream())
+    fn = load().qlora_linear_fwd_dropout_f16 if x.dtype == torch.float16 else load().qlora_linear_fwd_dropout
+    st = fn(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
+            _ptr(keep), float(p), _ptr(y), _ptr(h), _ptr(ws), nbytes, _stream())
     _check(st, "qlora_linear_fwd_dropout")
     return y, h
 
@@ -377,14 +386,15 @@ def linear_bwd_dropout(q: PackedNF4, x, dy, a, b, alpha: float, keep, p: float, 
 
     m, r, dev = dy.shape[0], a.shape[0], dy.device
     if dx is None and need_dx:
-        dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((m, q.k), dtype=dy.dtype, device=dev)
     da = torch.empty((r, q.k), dtype=torch.float32, device=dev) if da is None else da
     db = torch.empty((q.n, r), dtype=torch.float32, device=dev) if db is None else db
     ws, nbytes = _drop_ws(ws, m, q.n, q.k, r, dev)
     wc = q.c_struct()
-    st = load().qlora_linear_bwd_dropout(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha),
-                                         _ptr(keep), float(p), _ptr(h), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
-                                         nbytes, _stream())
+    fn = load().qlora_linear_bwd_dropout_f16 if dy.dtype == torch.float16 else load().qlora_linear_bwd_dropout
+    st = fn(ctypes.byref(wc), _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r, float(alpha),
+            _ptr(keep), float(p), _ptr(h), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws),
+            nbytes, _stream())
     _check(st, "qlora_linear_bwd_dropout")
     return dx, da, db
 
@@ -407,7 +417,7 @@ def linear_fwd_grouped(q: PackedNF4, parts, x, a, b, alpha: float, want_h: bool 
 
     m, g, r = x.shape[0], len(parts), b.shape[1]
     dev = x.device
-    y = out if out is not None else torch.empty((m, q.n), dtype=torch.bfloat16, device=dev)
+    y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=dev)
     h = h_out if h_out is not None else (torch.empty((m, g * r), dtype=torch.float32, device=dev) if want_h else None)
     if ws is None:
         nbytes = grouped_workspace_bytes(m, q.n, q.k, g, r)
@@ -415,8 +425,9 @@ def linear_fwd_grouped(q: PackedNF4, parts, x, a, b, alpha: float, want_h: bool 
     nbytes = ws.numel()
     wc = q.c_struct()
     pa = _parts(parts)
-    st = load().qlora_linear_fwd_grouped(ctypes.byref(wc), g, pa, _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
-                                         _ptr(y), _ptr(h), _ptr(ws), nbytes, _stream())
+    fn = load().qlora_linear_fwd_grouped_f16 if x.dtype == torch.float16 else load().qlora_linear_fwd_grouped
+    st = fn(ctypes.byref(wc), g, pa, _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha),
+            _ptr(y), _ptr(h), _ptr(ws), nbytes, _stream())
     _check(st, "qlora_linear_fwd_grouped")
     return y, h
 
@@ -430,7 +441,7 @@ def linear_bwd_grouped(q: PackedNF4, parts, x, dy, a, b, alpha: float, h=None, n
     m, g, r = dy.shape[0], len(parts), b.shape[1]
     dev = dy.device
     if dx is None and need_dx:
-        dx = torch.empty((m, q.k), dtype=torch.bfloat16, device=dev)
+        dx = torch.empty((m, q.k), dtype=dy.dtype, device=dev)
     if da is None:
         da = torch.empty((g * r, q.k), dtype=torch.float32, device=dev)
     if db is None:
@@ -441,8 +452,9 @@ def linear_bwd_grouped(q: PackedNF4, parts, x, dy, a, b, alpha: float, h=None, n
     nbytes = ws.numel()
     wc = q.c_struct()
     pa = _parts(parts)
-    st = load().qlora_linear_bwd_grouped(ctypes.byref(wc), g, pa, _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r,
-                                         float(alpha), _ptr(h), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes,
-                                         _stream())
+    fn = load().qlora_linear_bwd_grouped_f16 if dy.dtype == torch.float16 else load().qlora_linear_bwd_grouped
+    st = fn(ctypes.byref(wc), g, pa, _ptr(x), _ptr(dy), m, _ptr(a), _ptr(b), r,
+            float(alpha), _ptr(h), _ptr(dx), _ptr(da), _ptr(db), _ptr(ws), nbytes,
+            _stream())
     _check(st, "qlora_linear_bwd_grouped")
     return dx, da, db

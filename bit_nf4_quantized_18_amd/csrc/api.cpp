@@ -371,9 +371,9 @@ qlora_status linear_bwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
   if (dx != nullptr) {
     if (drop != nullptr) {
       // dX = dY W16, then + (dH A) / (1 - p) where the input was kept
-      QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, nullptr, nullptr, 0, dx, stream));
+      QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, nullptr, nullptr, 0, dx, stream, f16));
       QLORA_TRY(qlora::launch_masked_lora_add(dx, drop->keep, reinterpret_cast<const float*>(base + L.dh32), a, m, k,
-                                              r, stream));
+                                              r, stream, f16));
     } else {
       QLORA_TRY(qlora::launch_gemm_dx(pw, dy, m, dhs, at, rp, dx, stream, f16));
     }
@@ -425,6 +425,15 @@ qlora_status qlora_linear_fwd_grouped(const qlora_nf4_weight* w, int g, const in
   return linear_fwd_impl(w, &lp, x, m, a, b, g * r, r, alpha, y, h_out, ws, ws_bytes, stream);
 }
 
+qlora_status qlora_linear_fwd_grouped_f16(const qlora_nf4_weight* w, int g, const int64_t* parts, const uint16_t* x,
+                                          int64_t m, const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                          uint16_t* y, float* h_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  qlora::LoraParts lp;
+  const qlora_status st = group_parts(w, g, parts, r, &lp);
+  if (st != QLORA_OK) return st;
+  return linear_fwd_impl(w, &lp, x, m, a, b, g * r, r, alpha, y, h_out, ws, ws_bytes, stream, nullptr, true);
+}
+
 qlora_status qlora_linear_bwd_grouped(const qlora_nf4_weight* w, int g, const int64_t* parts, const uint16_t* x,
                                       const uint16_t* dy, int64_t m, const uint16_t* a, const uint16_t* b, int r,
                                       float alpha, const float* h_saved, uint16_t* dx, float* da, float* db, void* ws,
@@ -434,6 +443,18 @@ qlora_status qlora_linear_bwd_grouped(const qlora_nf4_weight* w, int g, const in
   if (st != QLORA_OK) return st;
   if (r % 16 != 0) return QLORA_ERR_UNSUPPORTED;
   return linear_bwd_impl(w, &lp, x, dy, m, a, b, g * r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream);
+}
+
+qlora_status qlora_linear_bwd_grouped_f16(const qlora_nf4_weight* w, int g, const int64_t* parts, const uint16_t* x,
+                                          const uint16_t* dy, int64_t m, const uint16_t* a, const uint16_t* b, int r,
+                                          float alpha, const float* h_saved, uint16_t* dx, float* da, float* db,
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  qlora::LoraParts lp;
+  const qlora_status st = group_parts(w, g, parts, r, &lp);
+  if (st != QLORA_OK) return st;
+  if (r % 16 != 0) return QLORA_ERR_UNSUPPORTED;
+  return linear_bwd_impl(w, &lp, x, dy, m, a, b, g * r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream, nullptr,
+                         true);
 }
 
 
@@ -530,6 +551,31 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t*
   const qlora_status st = make_drop(keep, p, &d);
   if (st != QLORA_OK) return st;
   return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream, &d);
+}
+
+qlora_status qlora_linear_fwd_dropout_f16(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                                          const uint16_t* b, int r, float alpha, const uint8_t* keep, float p,
+                                          uint16_t* y, float* h_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (m == 0)
+    return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, ws, ws_bytes, stream, nullptr, true);
+  DropArg d{};
+  const qlora_status st = make_drop(keep, p, &d);
+  if (st != QLORA_OK) return st;
+  return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, ws, ws_bytes, stream, &d, true);
+}
+
+qlora_status qlora_linear_bwd_dropout_f16(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy,
+                                          int64_t m, const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                          const uint8_t* keep, float p, const float* h_saved, uint16_t* dx, float* da,
+                                          float* db, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (m == 0)
+    return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream,
+                           nullptr, true);
+  DropArg d{};
+  const qlora_status st = make_drop(keep, p, &d);
+  if (st != QLORA_OK) return st;
+  return linear_bwd_impl(w, nullptr, x, dy, m, a, b, r, r, alpha, h_saved, dx, da, db, ws, ws_bytes, stream, &d,
+                         true);
 }
 
 qlora_status qlora_dropout_mask(uint64_t seed, uint64_t offset, int64_t count, float p, uint8_t* keep,

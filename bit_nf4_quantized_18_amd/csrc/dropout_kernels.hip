@@ -14,6 +14,7 @@
 // as easy as 1, 2, 3", SC 2011), so a mask can be made on the device and
 // reproduced anywhere from (seed, offset).
 #include "internal.h"
+#include "mfma.h"
 #include "nf4_lut.h"
 
 namespace qlora {
@@ -98,6 +99,7 @@ __global__ __launch_bounds__(256) void mask_input_kernel(const uint16_t* __restr
 // 16 x 512 tile: dh's 16 rows in LDS, each lane 8 columns of 4 rows, A rows
 // read from L2 (16 bytes per rank step). k % 64 == 0, so a lane's 8 columns
 // are all inside the row or all past its end.
+template <bool kF16>
 __global__ __launch_bounds__(256) void masked_lora_add_kernel(uint16_t* __restrict__ dx,
                                                               const uint8_t* __restrict__ keep,
                                                               const float* __restrict__ dh,
@@ -128,8 +130,8 @@ __global__ __launch_bounds__(256) void masked_lora_add_kernel(uint16_t* __restri
     float av[8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      av[2 * c] = __uint_as_float(v[c] << 16);
-      av[2 * c + 1] = __uint_as_float(v[c] & 0xFFFF0000u);
+      av[2 * c] = lo16<kF16>(v[c]);
+      av[2 * c + 1] = hi16<kF16>(v[c]);
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
@@ -150,9 +152,9 @@ __global__ __launch_bounds__(256) void masked_lora_add_kernel(uint16_t* __restri
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t kw = kb[c >> 1] >> (16 * (c & 1));
-      const float lo = __uint_as_float(g[c] << 16) + ((kw & 0xFFu) ? d[rr][2 * c] : 0.0f);
-      const float hi = __uint_as_float(g[c] & 0xFFFF0000u) + ((kw & 0xFF00u) ? d[rr][2 * c + 1] : 0.0f);
-      o[c] = cvt_bf16x2(lo, hi);
+      const float lo = lo16<kF16>(g[c]) + ((kw & 0xFFu) ? d[rr][2 * c] : 0.0f);
+      const float hi = hi16<kF16>(g[c]) + ((kw & 0xFF00u) ? d[rr][2 * c + 1] : 0.0f);
+      o[c] = cvt_16x2<kF16>(lo, hi);
     }
     *dst = o;
   }
@@ -180,10 +182,15 @@ hipError_t launch_dropout_mask(uint64_t seed, uint64_t block0, int64_t count, fl
 }
 
 hipError_t launch_masked_lora_add(uint16_t* dx, const uint8_t* keep, const float* dh, const uint16_t* a, int64_t m,
-                                  int64_t k, int r, hipStream_t st) {
+                                  int64_t k, int r, hipStream_t st, bool f16) {
   const int64_t tiles = ((m + kRows - 1) / kRows) * ((k + kCols - 1) / kCols);
-  hipLaunchKernelGGL(masked_lora_add_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, st, dx, keep, dh, a,
-                     m, k, r);
+  if (f16) {
+    hipLaunchKernelGGL(masked_lora_add_kernel<true>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, st, dx, keep,
+                       dh, a, m, k, r);
+  } else {
+    hipLaunchKernelGGL(masked_lora_add_kernel<false>, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, st, dx, keep,
+                       dh, a, m, k, r);
+  }
   return hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ hipError_t launch_mask_input(const uint16_t* x, const uint8_t* keep, int64_t cou
 hipError_t launch_dropout_mask(uint64_t seed, uint64_t block0, int64_t count, float thr, uint8_t* keep,
                                hipStream_t st);
 hipError_t launch_masked_lora_add(uint16_t* dx, const uint8_t* keep, const float* dh, const uint16_t* a, int64_t m,
-                                  int64_t k, int r, hipStream_t st);
+                                  int64_t k, int r, hipStream_t st, bool f16 = false);
 
 hipError_t launch_unmerge(const void* merged, int src_f32, int64_t n, int64_t k, const uint16_t* a,
                           const uint16_t* b, int r, float s, void* out, hipStream_t st);

@@ -254,6 +254,20 @@ qlora_status qlora_linear_bwd_dropout(const qlora_nf4_weight* w, const uint16_t*
                                       float p, const float* h_saved, uint16_t* dx, float* da,
                                       float* db, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The two dropout calls with IEEE half as the compute type (X, A, B, dY,
+ * Y and dX fp16), as qlora_linear_fwd_f16 / qlora_linear_bwd_f16 are to the
+ * plain calls. Arguments, workspace and errors as the bf16 dropout calls. */
+qlora_status qlora_linear_fwd_dropout_f16(const qlora_nf4_weight* w, const uint16_t* x, int64_t m,
+                                          const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                          const uint8_t* keep, float p, uint16_t* y, float* h_out,
+                                          void* ws, size_t ws_bytes, hipStream_t stream);
+qlora_status qlora_linear_bwd_dropout_f16(const qlora_nf4_weight* w, const uint16_t* x,
+                                          const uint16_t* dy, int64_t m, const uint16_t* a,
+                                          const uint16_t* b, int r, float alpha,
+                                          const uint8_t* keep, float p, const float* h_saved,
+                                          uint16_t* dx, float* da, float* db, void* ws,
+                                          size_t ws_bytes, hipStream_t stream);
+
 /* Bytes of device workspace that qlora_linear_fwd and qlora_linear_bwd need
  * for these sizes (the larger of the two); 0 if none. Host only, no GPU use. */
 size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
@@ -293,6 +307,20 @@ qlora_status qlora_linear_bwd_grouped(const qlora_nf4_weight* w, int g, const in
                                       const uint16_t* a, const uint16_t* b, int r, float alpha,
                                       const float* h_saved, uint16_t* dx, float* da, float* db,
                                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The two grouped calls with IEEE half as the compute type (X, A, B, dY, Y
+ * and dX fp16), as qlora_linear_fwd_f16 / qlora_linear_bwd_f16 are to the
+ * plain calls. Arguments, workspace and errors as the bf16 grouped calls. */
+qlora_status qlora_linear_fwd_grouped_f16(const qlora_nf4_weight* w, int g, const int64_t* parts,
+                                          const uint16_t* x, int64_t m, const uint16_t* a,
+                                          const uint16_t* b, int r, float alpha, uint16_t* y,
+                                          float* h_out, void* ws, size_t ws_bytes,
+                                          hipStream_t stream);
+qlora_status qlora_linear_bwd_grouped_f16(const qlora_nf4_weight* w, int g, const int64_t* parts,
+                                          const uint16_t* x, const uint16_t* dy, int64_t m,
+                                          const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                          const float* h_saved, uint16_t* dx, float* da, float* db,
+                                          void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace bytes for the grouped calls (n = sum of parts); 0 for invalid
  * sizes. Host only, no GPU use. */

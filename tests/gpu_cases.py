@@ -42,6 +42,18 @@ def oracle_weight(w: np.ndarray, dq: bool = True, codebook: int = 0):
     return q, O.bf16_bits_to_f32(bits).reshape(w.shape)
 
 
+def oracle_weight_f16(w: np.ndarray, dq: bool = True):
+    """The fp16 compute variant's weight: the half rounding of fl32(L s)."""
+    w32, _ = O.dequantize(O.quantize(w.reshape(-1), dq))
+    return O.f16_rne_bits(w32).view(np.float16).astype(np.float64).reshape(w.shape)
+
+
+def to_f16(a: np.ndarray):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.float16)
+
+
 def layer_inputs(n, k, m, r, tag, std_w=0.02):
     """W (fp32), X, A, B, dY as bf16 torch CPU tensors (values also used by the oracle)."""
     w = synth.normal((n, k), std_w, tag, "W")

@@ -59,6 +59,34 @@ def test_dropout_parity(gpu_lib, case):
     assert torch.equal(dx2, dx) and torch.equal(da2, da) and torch.equal(db2, db)
 
 
+@pytest.mark.parametrize("case", CASES[:2], ids=[c[0] for c in CASES[:2]])
+def test_dropout_parity_f16(gpu_lib, case):
+    """The dropout calls with fp16 compute (qlora_linear_*_dropout_f16)."""
+    import torch
+
+    from gpu_cases import oracle_weight_f16, to_f16
+
+    name, m, n, k, r, alpha, p = case
+    say(f"[dropout f16] case={name}")
+    tag = "dropf16_" + name
+    w = synth.normal((n, k), 0.02, tag, "W")
+    x, a, b, dy = (to_f16(synth.normal(sh, sd, tag, nm)) for sh, sd, nm in
+                   (((m, k), 1.0, "X"), ((r, k), 1.0 / r, "A"), ((n, r), 0.01, "B"), ((m, n), 1.0, "dY")))
+    keep = synth.keep_mask((m, k), p, tag, "keep")
+    w16 = oracle_weight_f16(w, True)
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+    xc, dyc, ac, bc, kc = x.cuda(), dy.cuda(), a.cuda(), b.cuda(), torch.from_numpy(keep).cuda()
+    y, h = gpu_lib.linear_fwd_dropout(q, xc, ac, bc, alpha, kc, p)
+    dx, da, db = gpu_lib.linear_bwd_dropout(q, xc, dyc, ac, bc, alpha, kc, p, h=h)
+    torch.cuda.synchronize()
+    assert y.dtype == torch.float16 and dx.dtype == torch.float16
+    y_ref, h_ref = OD.linear_fwd_dropout(f64(x), w16, f64(a), f64(b), alpha, r, keep, p)
+    dx_ref, da_ref, db_ref = OD.linear_bwd_dropout(f64(x), w16, f64(a), f64(b), f64(dy), alpha, r, keep, p)
+    errs = [rel(f64(y), y_ref), rel(f64(h), h_ref), rel(f64(dx), dx_ref), rel(f64(da), da_ref), rel(f64(db), db_ref)]
+    say("   rel errs " + " ".join(f"{e:.2e}" for e in errs))
+    assert max(errs) <= TOL
+
+
 def test_keep_all_p0_matches_plain_call(gpu_lib):
     """Keeping every element with p = 0: the forward and dA, dB are the plain
     call's bit for bit (same kernels on the same values); dX takes another

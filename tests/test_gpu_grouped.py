@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_cases import TOL, f64, oracle_weight, rel, say, to_bf16
+from gpu_cases import TOL, f64, oracle_weight, oracle_weight_f16, rel, say, to_bf16, to_f16
 from oracle import linear as OL
 
 pytestmark = pytest.mark.gpu
@@ -19,16 +19,17 @@ CASES = [
 ]
 
 
-def run_case(gpu_lib, name, m, parts, k, r, alpha, check_bwd=True):
+def run_case(gpu_lib, name, m, parts, k, r, alpha, check_bwd=True, f16=False):
     import torch
 
     tag = f"grouped_{name}"
-    say(f"[grouped] case={name} m={m} parts={parts} k={k} r={r}")
+    say(f"[grouped] case={name} m={m} parts={parts} k={k} r={r} f16={f16}")
+    cv = to_f16 if f16 else to_bf16
     ws = [synth.normal((n, k), 0.02, tag, f"W{l}") for l, n in enumerate(parts)]
-    x = to_bf16(synth.normal((m, k), 1.0, tag, "X"))
-    a = [to_bf16(synth.normal((r, k), 1.0 / r, tag, f"A{l}")) for l in range(len(parts))]
-    b = [to_bf16(synth.normal((n, r), 0.01, tag, f"B{l}")) for l, n in enumerate(parts)]
-    dy = [to_bf16(synth.normal((m, n), 1.0, tag, f"dY{l}")) for l, n in enumerate(parts)]
+    x = cv(synth.normal((m, k), 1.0, tag, "X"))
+    a = [cv(synth.normal((r, k), 1.0 / r, tag, f"A{l}")) for l in range(len(parts))]
+    b = [cv(synth.normal((n, r), 0.01, tag, f"B{l}")) for l, n in enumerate(parts)]
+    dy = [cv(synth.normal((m, n), 1.0, tag, f"dY{l}")) for l, n in enumerate(parts)]
     q = gpu_lib.quantize(torch.from_numpy(np.concatenate(ws, axis=0)).cuda())
     xc, ac, bc = x.cuda(), torch.cat(a).cuda(), torch.cat(b).cuda()
     y, h = gpu_lib.linear_fwd_grouped(q, parts, xc, ac, bc, alpha)
@@ -38,7 +39,7 @@ def run_case(gpu_lib, name, m, parts, k, r, alpha, check_bwd=True):
     off, dx_ref, errs = 0, None, []
     x64 = f64(x)
     for l, n in enumerate(parts):
-        _, w16 = oracle_weight(ws[l], True)
+        w16 = oracle_weight_f16(ws[l], True) if f16 else oracle_weight(ws[l], True)[1]
         y_ref, h_ref = OL.linear_fwd(x64, w16, f64(a[l]), f64(b[l]), alpha, r)
         errs.append(("y", l, rel(f64(y)[:, off:off + n], y_ref)))
         errs.append(("h", l, rel(f64(h)[:, l * r:(l + 1) * r], h_ref)))
@@ -58,6 +59,12 @@ def run_case(gpu_lib, name, m, parts, k, r, alpha, check_bwd=True):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_grouped_parity(gpu_lib, case):
     run_case(gpu_lib, *case)
+
+
+@pytest.mark.parametrize("case", CASES[:2], ids=[c[0] for c in CASES[:2]])
+def test_grouped_parity_f16(gpu_lib, case):
+    """The grouped calls with fp16 compute (qlora_linear_*_grouped_f16)."""
+    run_case(gpu_lib, *case, f16=True)
 
 
 @pytest.mark.parametrize("parts", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv_7b", "gateup_7b"])
