@@ -167,3 +167,45 @@ def test_dropout_step_with_generated_mask(gpu_lib):
     y_ref, _ = OD.linear_fwd_dropout(f64(x), w16, f64(a), f64(b), alpha, r, keep, p)
     dx_ref, da_ref, db_ref = OD.linear_bwd_dropout(f64(x), w16, f64(a), f64(b), f64(dy), alpha, r, keep, p)
     assert max(rel(f64(y), y_ref), rel(f64(dx), dx_ref), rel(f64(da), da_ref), rel(f64(db), db_ref)) <= TOL
+
+
+def test_dropout_step_graph_replay_matches_eager(gpu_lib):
+    """Mask drawing + dropout forward + backward captured in a HIP graph: every
+    replay, with eager work and synchronisation in between, reproduces the
+    eager results bit for bit (the bench times this step as a graph)."""
+    import torch
+
+    m, n, k, r, alpha, p = 300, 256, 320, 16, 32.0, 0.1
+    q, w16, x, a, b, dy, _ = _inputs(gpu_lib, "graph_drop", m, n, k, r, p)
+    xc, dyc, ac, bc = x.cuda(), dy.cuda(), a.cuda(), b.cuda()
+    say("[dropout] graph replay")
+    ws = torch.empty(gpu_lib.dropout_workspace_bytes(m, n, k, r), dtype=torch.uint8, device="cuda")
+    bufs = dict(keep=torch.empty((m, k), dtype=torch.uint8, device="cuda"),
+                y=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+                h=torch.empty((m, r), dtype=torch.float32, device="cuda"),
+                dx=torch.empty((m, k), dtype=torch.bfloat16, device="cuda"),
+                da=torch.empty((r, k), dtype=torch.float32, device="cuda"),
+                db=torch.empty((n, r), dtype=torch.float32, device="cuda"))
+
+    def step():
+        gpu_lib.dropout_mask(5, 16 * 64, (m, k), p, out=bufs["keep"])
+        gpu_lib.linear_fwd_dropout(q, xc, ac, bc, alpha, bufs["keep"], p, out=bufs["y"], h_out=bufs["h"], ws=ws)
+        gpu_lib.linear_bwd_dropout(q, xc, dyc, ac, bc, alpha, bufs["keep"], p, h=bufs["h"], dx=bufs["dx"],
+                                   da=bufs["da"], db=bufs["db"], ws=ws)
+
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        step()
+        torch.cuda.synchronize()
+        eager = {key: v.clone() for key, v in bufs.items()}
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        for rep in range(3):
+            for v in bufs.values():
+                v.fill_(7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            for key in bufs:
+                assert torch.equal(bufs[key], eager[key]), (rep, key)
