@@ -264,7 +264,8 @@ def main():
                 tot_ms += ms
                 per.append({"layer": lay.name, "n": lay.n, "k": lay.k, "ms": ms, "tflops": fl / ms / 1e9})
             ach = tot_flops / tot_ms / 1e9
-            res[kind] = {"kernel": f"nf4_gemm_kernel<{'true' if kind == 'dx' else 'false'}>", "achieved_tflops": ach,
+            res[kind] = {"kernel": f"nf4_gemm_kernel<{'true' if kind == 'dx' else 'false'}, true, false>",
+                         "achieved_tflops": ach,
                          "frac": ach / BF16_PEAK_TFLOPS, "avg_launch_ms": tot_ms / len(layers), "per_layer": per}
             log(f"[bench] gemm {kind}: {ach:.1f} TFLOP/s ({100 * ach / BF16_PEAK_TFLOPS:.1f}% of bf16 peak)")
         parts["fused_gemm"] = res
