@@ -221,29 +221,74 @@ __global__ void skinny_final_kernel(const float* __restrict__ part, int64_t M, i
   if (out_bf16 != nullptr) out_bf16[idx] = to16<kF16>(scale2 * val);
 }
 
-// at (k x rpad) = A^T zero-padded; bt (rpad x n) = B^T zero-padded.
-__global__ void lora_transpose_kernel(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int64_t n,
-                                      int64_t k, int r, int rpad, LoraParts lp, uint16_t* __restrict__ at,
-                                      uint16_t* __restrict__ bt) {
-  int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t na = k * rpad;
-  if (idx < na) {
-    const int64_t kk = idx / rpad;
-    const int j = static_cast<int>(idx % rpad);
-    at[idx] = (j < r) ? a[static_cast<int64_t>(j) * k + kk] : uint16_t(0);
+// at (k x rpad) = A^T zero-padded; bt (rpad x n) = B^T zero-padded, both
+// through LDS so that global reads and writes are whole 16-byte runs. The
+// first k / 64 workgroups take 64 columns of A each, the rest 64 rows of B.
+// Grouped weights: row j of B^T is slot j, owned by part j / rpart, and is
+// zero outside that part's columns (b holds the parts' B stacked, rpart
+// columns each). k % 64 == 0, n % 16 == 0, rpad % 32 == 0, rpart % 8 == 0
+// or a single part.
+constexpr int kTrCols = 64;
+__global__ __launch_bounds__(256) void lora_transpose_kernel(const uint16_t* __restrict__ a,
+                                                             const uint16_t* __restrict__ b, int64_t n, int64_t k,
+                                                             int r, int rpad, LoraParts lp, uint16_t* __restrict__ at,
+                                                             uint16_t* __restrict__ bt) {
+  __shared__ uint16_t tile[QLORA_MAX_RANK * (kTrCols + 2)];
+  constexpr int kLd = kTrCols + 2;  // odd word stride: column reads spread over the banks
+  const int tid = threadIdx.x;
+  const int64_t at_tiles = k / kTrCols;
+  if (blockIdx.x < at_tiles) {
+    const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kTrCols;
+    // rows j < rpad of A's 64-column slice (zeros for j >= r), 8 elements per item
+    for (int it = tid; it < rpad * 8; it += 256) {
+      const int j = it >> 3, c8 = (it & 7) * 8;
+      const u32x4 v = (j < r) ? *reinterpret_cast<const u32x4*>(a + static_cast<int64_t>(j) * k + k0 + c8)
+                              : u32x4{0, 0, 0, 0};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(tile + j * kLd + c8);  // 4-byte aligned: kLd and c8 are even
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = v[e];
+    }
+    __syncthreads();
+    // at[k0 + kk][j .. j+7] for each output row kk of the slice
+    for (int it = tid; it < kTrCols * (rpad / 8); it += 256) {
+      const int kk = it / (rpad / 8), j8 = (it % (rpad / 8)) * 8;
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = static_cast<uint32_t>(tile[(j8 + 2 * e) * kLd + kk]) |
+               (static_cast<uint32_t>(tile[(j8 + 2 * e + 1) * kLd + kk]) << 16);
+      *reinterpret_cast<u32x4*>(at + (k0 + kk) * rpad + j8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
     return;
   }
-  idx -= na;
-  if (idx < static_cast<int64_t>(rpad) * n) {
-    // grouped weights: row j of B^T is slot j, owned by part j / rpart, and
-    // is zero outside that part's columns (b holds the parts' B stacked,
-    // rpart columns each)
-    const int j = static_cast<int>(idx / n);
-    const int64_t nn = idx % n;
-    const int part = j / lp.rpart;
+  const int64_t n0 = (static_cast<int64_t>(blockIdx.x) - at_tiles) * kTrCols;
+  const int rp = lp.rpart;
+  // B rows n0 .. n0+63 (rp slots each) into the tile as [slot][row]
+  for (int it = tid; it < kTrCols * rp; it += 256) {
+    const int row = it / rp, jj = it % rp;
+    const int64_t nn = n0 + row;
+    tile[jj * kLd + row] = (nn < n) ? b[nn * rp + jj] : uint16_t(0);
+  }
+  __syncthreads();
+  // bt[j][n0 .. n0+63], 8 columns per item
+  for (int it = tid; it < rpad * (kTrCols / 8); it += 256) {
+    const int j = it / (kTrCols / 8), c8 = (it % (kTrCols / 8)) * 8;
+    const int part = j / rp;
     const int64_t lo = part == 0 ? 0 : lp.end[part - 1 < 3 ? part - 1 : 3];
     const int64_t hi = part < lp.g ? lp.end[part] : 0;
-    bt[idx] = (j < r && nn >= lo && nn < hi) ? b[nn * lp.rpart + (j - part * lp.rpart)] : uint16_t(0);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t nn = n0 + c8 + 2 * e + h;
+        const uint16_t v = (j < r && nn >= lo && nn < hi) ? tile[(j - part * rp) * kLd + c8 + 2 * e + h] : 0;
+        pair |= static_cast<uint32_t>(v) << (16 * h);
+      }
+      w[e] = pair;
+    }
+    if (n0 + c8 < n) *reinterpret_cast<u32x4*>(bt + static_cast<int64_t>(j) * n + n0 + c8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -638,13 +683,13 @@ hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_
 
 hipError_t launch_lora_transpose(const uint16_t* a, const uint16_t* b, int64_t n, int64_t k, int r, int rpad,
                                  uint16_t* at, uint16_t* bt, hipStream_t st, const LoraParts* parts) {
-  const int64_t total = (k + n) * rpad;
   LoraParts lp;
   lp.g = 1;
   lp.rpart = r;
   lp.end[0] = static_cast<int>(n);
-  hipLaunchKernelGGL(lora_transpose_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, a, b,
-                     n, k, r, rpad, parts != nullptr ? *parts : lp, at, bt);
+  const int64_t tiles = k / kTrCols + (n + kTrCols - 1) / kTrCols;
+  hipLaunchKernelGGL(lora_transpose_kernel, dim3(static_cast<unsigned>(tiles)), dim3(256), 0, st, a, b, n, k, r, rpad,
+                     parts != nullptr ? *parts : lp, at, bt);
   return hipGetLastError();
 }
 
