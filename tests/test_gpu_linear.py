@@ -266,3 +266,28 @@ def test_graph_replay_matches_eager(gpu_lib, m):
             torch.cuda.synchronize()
             for key in bufs:
                 assert torch.equal(bufs[key], eager[key]), (rep, key)
+
+
+def _random_cases(count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for c in range(count):
+        m = int(rng.choice([1, 2, 5, 16, 17, 33, 64, 130, 257]))
+        n = 16 * int(rng.integers(1, 30))
+        k = 64 * int(rng.integers(1, 11))
+        r = int(rng.choice([0, 1, 3, 8, 16, 17, 31, 32, 48, 64, 65, 96]))
+        alpha = float(rng.choice([1.0, 8.0, 16.0, 32.0]))
+        dq = bool(rng.integers(0, 2))
+        cases.append((f"rand{c}_m{m}_n{n}_k{k}_r{r}_dq{int(dq)}", m, n, k, r, alpha, dq))
+    return cases
+
+
+RANDOM_CASES = _random_cases(24, 2026)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[c[0] for c in RANDOM_CASES])
+def test_linear_parity_random_shapes(gpu_lib, case):
+    """Seeded random shapes across both paths: m from 1 to 257, n and k on
+    their 16 / 64 grids, ranks from 0 to 96 (ragged and tile-aligned), DQ on
+    and off."""
+    _run_case(gpu_lib, *case)
