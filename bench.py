@@ -60,7 +60,7 @@ def main():
     ap.add_argument("--only", default="", help="comma list of parts to run (train,f16,dropout,gemm,library,copy,decode,dequant,quant,merge,cpu)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+        print(f"bench.py measures one GPU: the layer has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
         sys.exit(2)
     only = set(filter(None, args.only.split(",")))

@@ -21,7 +21,7 @@ stated (numpy float32 ops are correctly rounded, keep denormals and never
 contract), except the codebook itself, which is computed in float64 and
 rounded once to float32.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * the quantile offset is the printed literal 0.9677083, levels built in
     float64 and rounded once to float32;
   * nearest level = argmin of the float32 distance |x - L_k|, ties to the
