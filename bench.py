@@ -57,7 +57,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run (train,f16,dropout,gemm,library,copy,decode,dequant,quant,merge,cpu)")
+    ap.add_argument("--only", default="", help="comma list of parts to run (train,f16,dropout,gemm,library,copy,decode,decode_token,dequant,quant,merge,cpu)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -397,6 +397,60 @@ def main():
             del pool
             torch.cuda.empty_cache()
         parts["decode_gemv"] = dec
+
+    # One decode token through a 7B-shaped model: 32 distinct copies of the
+    # layer set (q/k/v/o, gate/up, down) at m = 1, every linear one GEMV call
+    # with its adapter (r = 16), captured as one graph. 3.3 GB of NF4 weights
+    # per token, far beyond the 256 MB Infinity Cache.
+    if want("decode_token"):
+        nlayers = 32
+        base_q = {}
+        for lay in wl.layers:
+            key = (lay.n, lay.k)
+            if key not in base_q:
+                base_q[key] = qn.quantize(torch.from_numpy(synth.weight(wl, lay)).to(dev))
+        model = []
+        for li in range(nlayers):
+            for lay in wl.layers:
+                q0 = base_q[(lay.n, lay.k)]
+                qc = qn.PackedNF4(lay.n, lay.k, q0.codes.clone(), True, q0.scale_codes.clone(),
+                                  q0.group_scale.clone())
+                a = torch.from_numpy(synth.lora_a(wl, lay)).to(torch.bfloat16).to(dev)
+                b = torch.from_numpy(synth.lora_b(wl, lay)).to(torch.bfloat16).to(dev)
+                x = torch.from_numpy(synth.normal((1, lay.k), 1.0, "decode_token", lay.name)).to(torch.bfloat16).to(dev)
+                y = torch.empty((1, lay.n), dtype=torch.bfloat16, device=dev)
+                ws = torch.empty(max(qn.workspace_bytes(1, lay.n, lay.k, R), 1), dtype=torch.uint8, device=dev)
+                model.append((qc, x, a, b, y, ws))
+        del base_q
+        tot_bytes = sum(gemv_bytes(1, q.n, q.k, R) for q, *_ in model)
+        log(f"[bench] decode token: {len(model)} GEMV calls over {tot_bytes / 1e9:.2f} GB")
+
+        def token():
+            for q, x, a, b, y, ws in model:
+                qn.linear_fwd(q, x, a, b, ALPHA, want_h=False, out=y, ws=ws)
+
+        token()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            token()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = tot_bytes / (ms * 1e-3) / 1e9
+        parts["decode_token_7b"] = {"layers": nlayers, "calls": len(model), "bytes": tot_bytes, "ms_per_token": ms,
+                                    "tokens_per_s": 1e3 / ms, "GBps": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+        log(f"[bench] decode token (32 x 7 linears, m=1, r=16): {ms:.3f} ms  {1e3 / ms:.0f} tokens/s  "
+            f"{gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+        del model, g
+        torch.cuda.empty_cache()
 
     if want("quant"):
         qres = []
