@@ -399,9 +399,11 @@ def main():
         parts["decode_gemv"] = dec
 
     # One decode token through a 7B-shaped model: 32 distinct copies of the
-    # layer set (q/k/v/o, gate/up, down) at m = 1, every linear one GEMV call
-    # with its adapter (r = 16), captured as one graph. 3.3 GB of NF4 weights
-    # per token, far beyond the 256 MB Infinity Cache.
+    # layer set (q/k/v/o, gate/up, down) at m = 1, every linear with its
+    # adapter (r = 16), captured as one graph. 3.4 GB of NF4 weights per
+    # token, far beyond the 256 MB Infinity Cache. Two launch plans: q/k/v
+    # and gate/up as grouped calls on their shared input (4 calls per layer
+    # set, the headline), and one call per linear (7 per layer set).
     if want("decode_token"):
         nlayers = 32
         base_q = {}
@@ -409,48 +411,64 @@ def main():
             key = (lay.n, lay.k)
             if key not in base_q:
                 base_q[key] = qn.quantize(torch.from_numpy(synth.weight(wl, lay)).to(dev))
-        model = []
-        for li in range(nlayers):
-            for lay in wl.layers:
-                q0 = base_q[(lay.n, lay.k)]
-                qc = qn.PackedNF4(lay.n, lay.k, q0.codes.clone(), True, q0.scale_codes.clone(),
-                                  q0.group_scale.clone())
-                a = torch.from_numpy(synth.lora_a(wl, lay)).to(torch.bfloat16).to(dev)
-                b = torch.from_numpy(synth.lora_b(wl, lay)).to(torch.bfloat16).to(dev)
-                x = torch.from_numpy(synth.normal((1, lay.k), 1.0, "decode_token", lay.name)).to(torch.bfloat16).to(dev)
-                y = torch.empty((1, lay.n), dtype=torch.bfloat16, device=dev)
-                ws = torch.empty(max(qn.workspace_bytes(1, lay.n, lay.k, R), 1), dtype=torch.uint8, device=dev)
-                model.append((qc, x, a, b, y, ws))
-        del base_q
-        tot_bytes = sum(gemv_bytes(1, q.n, q.k, R) for q, *_ in model)
-        log(f"[bench] decode token: {len(model)} GEMV calls over {tot_bytes / 1e9:.2f} GB")
+        byname = {lay.name: lay for lay in wl.layers}
+        plans = {"grouped": [("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",)],
+                 "per_linear": [(lay.name,) for lay in wl.layers]}
+        for plan, groups in plans.items():
+            model = []
+            for li in range(nlayers):
+                for grp in groups:
+                    lays = [byname[nm] for nm in grp]
+                    k = lays[0].k
+                    qs = [base_q[(lay.n, lay.k)] for lay in lays]
+                    qc = qn.PackedNF4(sum(lay.n for lay in lays), k, torch.cat([q.codes for q in qs]), True,
+                                      torch.cat([q.scale_codes for q in qs]), torch.cat([q.group_scale for q in qs]))
+                    a = torch.cat([torch.from_numpy(synth.lora_a(wl, lay)) for lay in lays]).to(torch.bfloat16).to(dev)
+                    b = torch.cat([torch.from_numpy(synth.lora_b(wl, lay)) for lay in lays]).to(torch.bfloat16).to(dev)
+                    x = torch.from_numpy(synth.normal((1, k), 1.0, "decode_token", grp[0])).to(torch.bfloat16).to(dev)
+                    y = torch.empty((1, qc.n), dtype=torch.bfloat16, device=dev)
+                    parts_n = [lay.n for lay in lays]
+                    nbytes = (qn.grouped_workspace_bytes(1, qc.n, k, len(lays), R) if len(lays) > 1
+                              else qn.workspace_bytes(1, qc.n, k, R))
+                    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+                    # bytes: codes, scales, X, Y, the stacked A (g r x k) and B (n x r)
+                    nb = gemv_bytes(1, qc.n, k, R) + 2 * (len(lays) - 1) * R * k
+                    model.append((qc, parts_n, x, a, b, y, ws, nb))
+            tot_bytes = sum(e[-1] for e in model)
+            log(f"[bench] decode token ({plan}): {len(model)} GEMV calls over {tot_bytes / 1e9:.2f} GB")
 
-        def token():
-            for q, x, a, b, y, ws in model:
-                qn.linear_fwd(q, x, a, b, ALPHA, want_h=False, out=y, ws=ws)
+            def token():
+                for q, parts_n, x, a, b, y, ws, _ in model:
+                    if len(parts_n) > 1:
+                        qn.linear_fwd_grouped(q, parts_n, x, a, b, ALPHA, want_h=False, out=y, ws=ws)
+                    else:
+                        qn.linear_fwd(q, x, a, b, ALPHA, want_h=False, out=y, ws=ws)
 
-        token()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
             token()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = ev(), ev()
-        reps = 5
-        e0.record()
-        for _ in range(reps):
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                token()
             g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        gbs = tot_bytes / (ms * 1e-3) / 1e9
-        parts["decode_token_7b"] = {"layers": nlayers, "calls": len(model), "bytes": tot_bytes, "ms_per_token": ms,
-                                    "tokens_per_s": 1e3 / ms, "GBps": gbs, "frac_hbm_peak": gbs / HBM_PEAK_GBS}
-        log(f"[bench] decode token (32 x 7 linears, m=1, r=16): {ms:.3f} ms  {1e3 / ms:.0f} tokens/s  "
-            f"{gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
-        del model, g
-        torch.cuda.empty_cache()
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            reps = 5
+            e0.record()
+            for _ in range(reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            gbs = tot_bytes / (ms * 1e-3) / 1e9
+            key = "decode_token_7b" if plan == "grouped" else "decode_token_7b_per_linear"
+            parts[key] = {"layers": nlayers, "launch_plan": plan, "calls": len(model), "bytes": tot_bytes,
+                          "ms_per_token": ms, "tokens_per_s": 1e3 / ms, "GBps": gbs,
+                          "frac_hbm_peak": gbs / HBM_PEAK_GBS}
+            log(f"[bench] decode token ({plan}, 32 layer sets, m=1, r=16): {ms:.3f} ms  {1e3 / ms:.0f} tokens/s  "
+                f"{gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+            del model, g
+            torch.cuda.empty_cache()
+        del base_q
 
     if want("quant"):
         qres = []

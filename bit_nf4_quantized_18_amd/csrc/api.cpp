@@ -29,11 +29,12 @@ struct Carve {
 struct FwdLayout {
   int64_t h32, hs, part, total;
 };
-FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r, bool grouped = false) {
+// gemm: the fused GEMM for every m (dropout calls)
+FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r, bool gemm = false) {
   (void)n;
   Carve c;
   FwdLayout L{};
-  if (m <= kGemvMaxM && !grouped) {
+  if (m <= kGemvMaxM && !gemm) {
     // decode: H partial sums, unless the GEMV computes H itself
     L.h32 = c.take(qlora::gemv_fuses_h(k, r) ? 0 : qlora::skinny_splits(m, k) * m * r * 4);
     L.hs = c.take(0);
@@ -169,7 +170,7 @@ size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
 
 size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int g, int r) {
   if (m <= 0 || n <= 0 || k <= 0 || g < 1 || g > QLORA_MAX_PARTS || r < 1 || g * r > QLORA_MAX_RANK) return 0;
-  const int64_t f = fwd_layout(m, n, k, g * r, true).total;
+  const int64_t f = fwd_layout(m, n, k, g * r).total;
   const int64_t b = bwd_layout(m, n, k, g * r, r).total;
   return static_cast<size_t>(f > b ? f : b);
 }
@@ -238,7 +239,7 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
 
   // with dropout: the GEMM path for every m, after the masked copy of X
-  const bool gemm_path = grouped || drop != nullptr;
+  const bool gemm_path = drop != nullptr;
   const FwdLayout L = fwd_layout(m, n, k, r, gemm_path);
   char* base = static_cast<char*>(ws);
   const uint16_t* xa = x;  // the adapter's input
@@ -261,7 +262,7 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
       hpart = reinterpret_cast<float*>(base + L.h32);
       QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, hpart, nullptr, splits, stream, f16));
     }
-    QLORA_TRY(qlora::launch_gemv(pw, x, m, a, hpart, splits, b, r, s, y, h_out, stream, f16));
+    QLORA_TRY(qlora::launch_gemv(pw, x, m, a, hpart, splits, b, r, s, y, h_out, stream, f16, grp));
   } else {
     float* h32 = (r == 0) ? nullptr : (h_out != nullptr ? h_out : reinterpret_cast<float*>(base + L.h32));
     uint16_t* hs = (r == 0) ? nullptr : reinterpret_cast<uint16_t*>(base + L.hs);

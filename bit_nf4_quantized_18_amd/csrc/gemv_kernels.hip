@@ -51,13 +51,22 @@ __device__ __forceinline__ u32x4 decode_order(u32x4 v) {
   return u32x4{out[0], out[1], out[2], out[3]};
 }
 
+// First H slot of output row p: part l (rows up to P.end[l]) owns slots
+// l rb .. (l+1) rb - 1; with one part, 0.
+__device__ __forceinline__ int part_slot0(const LoraParts& P, int p, int rb) {
+  int off = 0;
+#pragma unroll
+  for (int l = 0; l + 1 < 4; ++l) off += (l + 1 < P.g && p >= P.end[l]) ? rb : 0;
+  return off;
+}
+
 template <int WAVES, bool kDQ, bool kFuseH, bool kF16>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
                                                           const uint16_t* __restrict__ a,
                                                           const float* __restrict__ hpart, int hsplits,
-                                                          const uint16_t* __restrict__ b, int r, float s,
-                                                          uint16_t* __restrict__ y, float* __restrict__ h_out,
-                                                          Levels L) {
+                                                          const uint16_t* __restrict__ b, int rh, int rb,
+                                                          LoraParts P, float s, uint16_t* __restrict__ y,
+                                                          float* __restrict__ h_out, Levels L) {
   static_assert(WAVES == 16, "one pass covers 64 blocks; A is staged as 16 rows x 64 blocks");
   constexpr int kLaneGroups = WAVES * 4;
   // With kFuseH, the pass's slice of A (16 ranks x 4096 k, bf16) lives in LDS;
@@ -89,27 +98,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), static_cast<short>(0),
                                                                         M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), static_cast<short>(0),
-                                                                        kFuseH ? r * K * 2 : 0, 0x00020000);
+                                                                        kFuseH ? rh * K * 2 : 0, 0x00020000);
   const int wv_u = __builtin_amdgcn_readfirstlane(wave);
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 hacc = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kBPer = (16 * QLORA_MAX_RANK + WAVES * 64 - 1) / (WAVES * 64);  // B values per thread
   uint16_t bv[kBPer];
-  const int blast = N * r - 1;
+  const int blast = N * rb - 1;
 
   // One block per lane group per pass. All loads of a pass (codes, scale,
   // X) are issued unconditionally from clamped addresses before any is used;
   // a block past the row or past K gets a zero scale, so its weights are 0.
   for (int base = 0; base < nbk; base += kLaneGroups) {
-    if (base == 0 && r > 0) {
+    if (base == 0 && rb > 0) {
       // this workgroup's 16 rows of B (contiguous in memory), into registers
       // now and into LDS after the main product, so that no wait for them
       // holds up the weight loads (indices clamped to the last element of B;
       // rows past N are never stored). With r = 0 there is no B to read.
 #pragma unroll
       for (int u = 0; u < kBPer; ++u) {
-        const int e = n0 * r + tid + u * WAVES * 64;
+        const int e = n0 * rb + tid + u * WAVES * 64;
         bv[u] = b[e < blast ? e : blast];
       }
     }
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     for (int j = 0; j < 8; ++j) xa[j] = decode_order(__builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0));
     if (base == 0 && !kFuseH) {
       // H = sum of the LoRA-down partials (fixed order)
-      const int mr = M * r;
+      const int mr = M * rh;
       for (int idx = tid; idx < mr; idx += WAVES * 64) {
         float hv = 0.0f;
         for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
@@ -191,7 +200,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
 #pragma unroll
   for (int u = 0; u < kBPer; ++u) {
     const int idx = tid + u * WAVES * 64;
-    if (idx < 16 * r) b_lds[idx] = bv[u];  // r = 0: never, bv unset
+    if (idx < 16 * rb) b_lds[idx] = bv[u];  // rb = 0: never, bv unset
   }
 
   if (kFuseH) __syncthreads();  // the last slice of A has been read
@@ -207,9 +216,9 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
       float hv = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < WAVES; ++wv) hv += hredf[(wv * 64 + l2) * 4 + v];
-      if (mo < M && j < r) {
-        h_lds[mo * r + j] = hv;
-        if (h_out != nullptr && blockIdx.x == 0) h_out[mo * r + j] = hv;
+      if (mo < M && j < rh) {
+        h_lds[mo * rh + j] = hv;
+        if (h_out != nullptr && blockIdx.x == 0) h_out[mo * rh + j] = hv;
       }
     }
     __syncthreads();
@@ -220,11 +229,11 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   float sum = 0.0f;
 #pragma unroll
   for (int wv = 0; wv < WAVES; ++wv) sum += redf[(wv * 64 + l2) * 4 + v];
-  if (r > 0) {
+  if (rb > 0) {
     float lo = 0.0f;
-    const uint16_t* brow = b_lds + (l2 & 15) * r;
-    const float* hrow = h_lds + mo * r;
-    for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
+    const uint16_t* brow = b_lds + (l2 & 15) * rb;
+    const float* hrow = h_lds + mo * rh + part_slot0(P, no, rb);
+    for (int j = 0; j < rb; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
     sum = fmaf(s, lo, sum);
   }
   y[mo * N + no] = to16<kF16>(sum);
@@ -235,18 +244,29 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
 // software-pipelines them: the codes, scales and B rows of the next row group
 // are in flight while the current one is unpacked and multiplied. X is loaded
 // once (the same fragments serve every row group) and, with kFuseH, H is
-// computed once per workgroup, in its first row group, from A copied into LDS.
+// computed once per workgroup, in its first row group.
+//
+// X and A reach the fragments through LDS, one private 8 KB region per wave:
+// wave w's lane groups need the 256-k slice [256 w, 256 w + 256) of every
+// token (rank) row, 512 contiguous bytes per row, so the wave copies its
+// slice global -> LDS in whole 1 KB runs (two rows per copy) and reads its
+// fragments back. Read straight from global, each 16-byte fragment load
+// would touch a different cache line per lane group and token (64 lines per
+// load instead of 8 per copy). Piece p of row i is stored in slot p ^ i of
+// the row, so the 16 rows of one piece fall in 16 different bank groups. The
+// region holds X first; once X is in registers it receives the wave's slice
+// of A, which only that wave reads: H needs no barrier of its own.
 template <bool kDQ, bool kFuseH, bool kF16>
 __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
                                                                const uint16_t* __restrict__ a,
                                                                const float* __restrict__ hpart, int hsplits,
-                                                               const uint16_t* __restrict__ b, int r, float s,
-                                                               uint16_t* __restrict__ y, float* __restrict__ h_out,
-                                                               Levels L) {
-  constexpr int WAVES = 16, kLaneGroups = 64;
-  constexpr int kARow = kLaneGroups * 64 * 2;  // bytes of one rank row of A (k <= 4096)
+                                                               const uint16_t* __restrict__ b, int rh, int rb,
+                                                               LoraParts P, float s, uint16_t* __restrict__ y,
+                                                               float* __restrict__ h_out, Levels L) {
+  constexpr int WAVES = 16;
+  constexpr int kSlice = 16 * 512;  // one wave's region: 16 rows x 256 k of bf16
   constexpr int kRedBytes = (kFuseH ? 2 : 1) * WAVES * 64 * 16;
-  constexpr int kStage = kFuseH ? 16 * kARow : kRedBytes;
+  constexpr int kStage = WAVES * kSlice;
   constexpr int kBPer = (16 * QLORA_MAX_RANK + WAVES * 64 - 1) / (WAVES * 64);  // B values per thread
   __shared__ __attribute__((aligned(16))) unsigned char stage[kStage > kRedBytes ? kStage : kRedBytes];
   __shared__ float h_lds[16 * QLORA_MAX_RANK];
@@ -266,26 +286,28 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
   const bool kval = G < nbk;
   const int kb_c = kval ? G : nbk - 1;
   const int wv_u = __builtin_amdgcn_readfirstlane(wave);
-  const int blast = N * r - 1;
+  const int blast = N * rb - 1;
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), static_cast<short>(0),
                                                                         M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), static_cast<short>(0),
-                                                                        kFuseH ? r * K * 2 : 0, 0x00020000);
+                                                                        kFuseH ? rh * K * 2 : 0, 0x00020000);
 
   struct Loads {
     u32x4 c0, c1;
-    uint32_t scode;
+    uint8_t scode;  // widened where it is used, so that nothing waits for it earlier
     float gsc;
     uint16_t bv[kBPer];
   };
-  // loads of row group rg < nrg
-  auto issue = [&](int rgc, Loads& T) {
+  // loads of row group rg < nrg; with real = false the same instructions on
+  // the first element of every array (one cache line each, results unused)
+  auto issue = [&](int rgc, Loads& T, bool real) {
     const int n = rgc * 16 + i;
-    const int n_c = n < N ? n : N - 1;
-    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_c * 32));
+    const int n_c = real ? (n < N ? n : N - 1) : 0;
+    const int kb_r = real ? kb_c : 0;
+    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_r * 32));
     T.c0 = __builtin_nontemporal_load(cp);
-    T.c1 = __builtin_nontemporal_load(cp + 1);
-    const int bi = n_c * nbk + kb_c;
+    T.c1 = __builtin_nontemporal_load(cp + (real ? 1 : 0));
+    const int bi = n_c * nbk + kb_r;
     if (kDQ) {
       T.scode = w.scale_codes[bi];
       T.gsc = w.group_scale[static_cast<uint32_t>(bi) / kGroup];
@@ -293,41 +315,72 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
       T.scode = 0;
       T.gsc = w.absmax[bi];
     }
-    if (r > 0) {
+    // B rows: always kBPer loads (from X's first element when there is no
+    // B), so that every path issues the same number of loads per row group
 #pragma unroll
-      for (int u = 0; u < kBPer; ++u) {
-        const int e = rgc * 16 * r + tid + u * WAVES * 64;
-        T.bv[u] = b[e < blast ? e : blast];
+    for (int u = 0; u < kBPer; ++u) {
+      const int e = rgc * 16 * rb + tid + u * WAVES * 64;
+      const uint16_t* bp = (rb > 0 && real) ? b + (e < blast ? e : blast) : x;
+      T.bv[u] = *bp;
+    }
+  };
+  constexpr int kTaskLoads = 2 + (kDQ ? 2 : 1) + kBPer;  // per issue()
+
+  // This wave's region and its copies: copy t moves rows 2t and 2t+1; lane l
+  // fetches piece (l & 31) ^ row of row 2t + (l >> 5) into slot l of the copy.
+  // Rows past the matrix (tokens >= M, ranks >= rh) read zeros; a wave whose
+  // slice starts past K copies nothing (its lane groups have no block).
+  unsigned char* region = stage + wv_u * kSlice;
+  const bool has_slice = wave * 4 < nbk;  // wave-uniform
+  const int crow = lane >> 5;
+  auto copy_slice = [&](__amdgpu_buffer_rsrc_t rsrc, int rows) {
+    const int ncopy = (rows + 1) >> 1;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < ncopy) {
+        const int row = 2 * t + crow;
+        const int goff = row * K * 2 + wv_u * 512 + 16 * ((lane & 31) ^ row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(region + t * 1024), 16, goff, 0, 0, 0);
       }
     }
   };
-  constexpr int kTaskLoads = 2 + (kDQ ? 2 : 1) + kBPer;  // per issue() with r > 0
+  // fragment j of lane (i, g): piece 8 g + j of row i
+  auto read_frag = [&](int j) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(region + i * 512 + 16 * ((8 * g + j) ^ i));
+  };
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 hacc = f32x4{0.f, 0.f, 0.f, 0.f};
   Loads T0, T1;
   const int rg0 = blockIdx.x;
-  issue(rg0, T0);
+  // X slice first, then the first row group's loads; wait for the X copies
+  // only (every load issued after them may stay in flight)
+  __builtin_amdgcn_sched_barrier(0);
+  if (has_slice) copy_slice(xrsrc, M);
+  __builtin_amdgcn_sched_barrier(0);
+  issue(rg0, T0, true);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<kTaskLoads>();
+  __builtin_amdgcn_sched_barrier(0);
   u32x4 xa[8];  // X fragments of this lane's block: the same for every row group
-  {
-    const int xoff = (i * K + kb_c * 64) * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = decode_order(__builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0));
+  for (int j = 0; j < 8; ++j) xa[j] = u32x4{0, 0, 0, 0};
+  if (kval && i < M) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xa[j] = read_frag(j);
   }
-  if (kFuseH) {
-    // rank row `wave` of A, global -> LDS in 8 copies of 1 KB (whole cache
-    // lines); lane l of copy t fetches piece 64 t + (l ^ wave) into slot l,
-    // so the 16 ranks of one piece land in 16 different bank groups
-    __builtin_amdgcn_sched_barrier(0);
-    const int roff = wv_u * K * 2 + 16 * (lane ^ wave);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(stage + wv_u * kARow + t * 1024), 16,
-                                               roff + t * 1024, 0, 0, 0);
+  for (int j = 0; j < 8; ++j) xa[j] = decode_order(xa[j]);
+  if (kFuseH) {
+    // the region's X has been read into registers: A's slice replaces it
     __builtin_amdgcn_sched_barrier(0);
-  } else if (r > 0) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragment reads are done
+    if (has_slice) copy_slice(arsrc, rh);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!kFuseH && rh > 0) {
     // H = sum of the LoRA-down partials (fixed order)
-    const int mr = M * r;
+    const int mr = M * rh;
     for (int idx = tid; idx < mr; idx += WAVES * 64) {
       float hv = 0.0f;
       for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
@@ -338,7 +391,9 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
 
   auto step = [&](int rg, Loads& Tc, Loads& Tn) {
     const bool has_next = rg + static_cast<int>(gridDim.x) < nrg;  // uniform
-    if (has_next) issue(rg + gridDim.x, Tn);
+    // the next row group's loads, or after the last one the same number of
+    // stand-in loads: the waits below count the same on every path
+    issue(rg + static_cast<int>(gridDim.x), Tn, has_next);
     // wave-uniform guard; lane groups past the row's blocks get a zero scale
     if (wave * 4 < nbk) {
       const int n = rg * 16 + i;
@@ -356,23 +411,20 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
     const bool first = rg == rg0;
     if (kFuseH && first) {
       // H product, once: wait for this wave's copies of A (everything issued
-      // after them is the next row group's loads), then for every wave's
+      // after them is the next row group's loads); only this wave reads them
       __builtin_amdgcn_sched_barrier(0);
-      if (has_next) {
-        wait_vmcnt<kTaskLoads>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      wait_vmcnt<kTaskLoads>();
       __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      if (wave * 4 < nbk) {
-        const unsigned char* arow = stage + i * kARow;
+      if (has_slice) {
+        u32x4 af[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int p = 8 * G + j;
-          const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
-          hacc = mma16<kF16>(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
+        for (int j = 0; j < 8; ++j) af[j] = u32x4{0, 0, 0, 0};
+        if (kval && i < rh) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) af[j] = read_frag(j);
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hacc = mma16<kF16>(xa[j], decode_order(af[j]), hacc);
       }
     }
     // epilogue of row group rg
@@ -382,7 +434,7 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
 #pragma unroll
     for (int u = 0; u < kBPer; ++u) {
       const int idx = tid + u * WAVES * 64;
-      if (idx < 16 * r) b_lds[idx] = Tc.bv[u];
+      if (idx < 16 * rb) b_lds[idx] = Tc.bv[u];
     }
     __syncthreads();
     const int l2 = tid & 63, v = tid >> 6;
@@ -393,9 +445,9 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
         float hv = 0.0f;
 #pragma unroll
         for (int wv = 0; wv < WAVES; ++wv) hv += hredf[(wv * 64 + l2) * 4 + v];
-        if (mo < M && j < r) {
-          h_lds[mo * r + j] = hv;
-          if (h_out != nullptr && blockIdx.x == 0) h_out[mo * r + j] = hv;
+        if (mo < M && j < rh) {
+          h_lds[mo * rh + j] = hv;
+          if (h_out != nullptr && blockIdx.x == 0) h_out[mo * rh + j] = hv;
         }
       }
       __syncthreads();
@@ -405,11 +457,11 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
       float sum = 0.0f;
 #pragma unroll
       for (int wv = 0; wv < WAVES; ++wv) sum += redf[(wv * 64 + l2) * 4 + v];
-      if (r > 0) {
+      if (rb > 0) {
         float lo = 0.0f;
-        const uint16_t* brow = b_lds + (l2 & 15) * r;
-        const float* hrow = h_lds + mo * r;
-        for (int j = 0; j < r; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
+        const uint16_t* brow = b_lds + (l2 & 15) * rb;
+        const float* hrow = h_lds + mo * rh + part_slot0(P, no, rb);
+        for (int j = 0; j < rb; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
         sum = fmaf(s, lo, sum);
       }
       y[mo * N + no] = to16<kF16>(sum);
@@ -445,22 +497,24 @@ namespace {
 
 template <bool kF16>
 hipError_t launch_gemv_t(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
-                         int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st) {
+                         int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
+                         const LoraParts& P) {
   constexpr int kWaves = 16;
   const int64_t nrg = (w.n + 15) / 16;
   const bool fuse = gemv_fuses_h(w.k, r);
+  const int rb = P.g > 1 ? P.rpart : r;
   if (w.k <= 4096) {
     const unsigned grid = static_cast<unsigned>(nrg < device_cus() ? nrg : device_cus());
     auto kern = w.dq ? (fuse ? gemv_persistent_kernel<true, true, kF16> : gemv_persistent_kernel<true, false, kF16>)
                      : (fuse ? gemv_persistent_kernel<false, true, kF16> : gemv_persistent_kernel<false, false, kF16>);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a, hpart, hsplits, b,
-                       r, s, y, h_out, codebook_table(w.codebook));
+                       r, rb, P, s, y, h_out, codebook_table(w.codebook));
     return hipGetLastError();
   }
   auto kern = w.dq ? (fuse ? gemv_kernel<kWaves, true, true, kF16> : gemv_kernel<kWaves, true, false, kF16>)
                    : (fuse ? gemv_kernel<kWaves, false, true, kF16> : gemv_kernel<kWaves, false, false, kF16>);
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nrg)), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a,
-                     hpart, hsplits, b, r, s, y, h_out, codebook_table(w.codebook));
+                     hpart, hsplits, b, r, rb, P, s, y, h_out, codebook_table(w.codebook));
   return hipGetLastError();
 }
 
@@ -468,9 +522,14 @@ hipError_t launch_gemv_t(const PackedW& w, const uint16_t* x, int64_t m, const u
 
 hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
                        int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
-                       bool f16) {
-  return f16 ? launch_gemv_t<true>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st)
-             : launch_gemv_t<false>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st);
+                       bool f16, const LoraParts* parts) {
+  LoraParts one;
+  one.g = 1;
+  one.rpart = r;
+  one.end[0] = static_cast<int>(w.n);
+  const LoraParts& P = parts != nullptr ? *parts : one;
+  return f16 ? launch_gemv_t<true>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st, P)
+             : launch_gemv_t<false>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st, P);
 }
 
 }  // namespace qlora

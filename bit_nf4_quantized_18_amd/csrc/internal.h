@@ -69,15 +69,6 @@ hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m
                                  float scale, float scale2, float* part, float* out_f32, uint16_t* out_bf16,
                                  hipStream_t st, bool f16 = false);
 
-// Decode GEMV, m <= 16: y = x W16^T + s * h B^T in one launch when
-// gemv_fuses_h(k, r) (H = x A^T computed in the kernel from a); otherwise
-// hpart holds hsplits partial sums of H (hsplits x m x r float32, from
-// launch_skinny). r = 0: base only. h_out (m x r, may be null) receives H.
-bool gemv_fuses_h(int64_t k, int r);
-hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
-                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
-                       bool f16 = false);
-
 // A weight made of g row blocks (grouped linears sharing their input): part
 // l covers output rows end[l-1] .. end[l]-1 (end[-1] = 0) and owns adapter
 // slots l rpart .. (l+1) rpart - 1. g = 1 (the default): one part.
@@ -86,6 +77,17 @@ struct LoraParts {
   int rpart = 0;
   int end[4] = {0, 0, 0, 0};
 };
+
+// Decode GEMV, m <= 16: y = x W16^T + s * h B^T in one launch when
+// gemv_fuses_h(k, r) (H = x A^T computed in the kernel from a); otherwise
+// hpart holds hsplits partial sums of H (hsplits x m x r float32, from
+// launch_skinny). r = 0: base only. h_out (m x r, may be null) receives H.
+// Grouped weights (parts != null): r = g rpart slots of H (a is r x k), b is
+// n x rpart and row p of part l takes H's slots l rpart .. (l+1) rpart - 1.
+bool gemv_fuses_h(int64_t k, int r);
+hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
+                       int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
+                       bool f16 = false, const LoraParts* parts = nullptr);
 
 // Fused dequant-GEMM, forward: y = x W16^T + the LoRA term where hs is bf16
 // m x rpad (already scaled by s) and b is n x r bf16 (r = slots per part);

@@ -295,7 +295,8 @@ size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
  *   stacked, with dH_l = s dY_l B_l, dA_l = dH_l^T X, dB_l = s dY_l^T H_l;
  *   h_saved (float32 m x (g r), from h_out) may be NULL. The backward needs
  *   r % 16 == 0 (QLORA_ERR_UNSUPPORTED otherwise).
- * Both take the fused dequant-GEMM for every m; ws must hold
+ * The forward takes the decode (GEMV) kernels for m <= 16 and the fused
+ * dequant-GEMM above; the backward takes the GEMM for every m. ws must hold
  * qlora_linear_grouped_workspace_bytes(m, n, k, g, r) bytes.
  * Errors as for the single-linear calls; SHAPE also for bad parts. */
 qlora_status qlora_linear_fwd_grouped(const qlora_nf4_weight* w, int g, const int64_t* parts,

@@ -13,9 +13,21 @@ pytestmark = pytest.mark.gpu
 # (name, m, parts, k, r, alpha)
 CASES = [
     ("qkv_ragged_m300", 300, (256, 512, 256), 320, 16, 32.0),  # ragged m, odd number of k-steps
-    ("gateup_m17", 17, (512, 256), 192, 16, 16.0),             # small m: still the GEMM path
+    ("gateup_m17", 17, (512, 256), 192, 16, 16.0),             # smallest m on the GEMM path
     ("qkv_r32", 64, (256, 256, 256), 256, 32, 64.0),           # g r = 96: the general projection
     ("four_parts_m40", 40, (256, 256, 256, 256), 128, 16, 32.0),
+]
+
+# Decode sizes (m <= 16, the GEMV): H in the kernel when g r <= 16, else from
+# split partial sums; k <= 4096 takes the persistent form, larger k the
+# multi-pass one. The backward needs r % 16 == 0, so r = 4 cases check the
+# forward only.
+DECODE_CASES = [
+    ("qkv_decode_m1", 1, (256, 512, 256), 320, 4, 32.0),
+    ("four_parts_decode_m5", 5, (256, 256, 256, 256), 192, 4, 16.0),
+    ("gateup_decode_m16_k4160", 16, (512, 256), 4160, 16, 32.0),
+    ("qkv_decode_r32_m7", 7, (256, 256, 256), 256, 32, 64.0),
+    ("qkv_decode_r4_m3_k4608", 3, (256, 256, 512), 4608, 4, 8.0),
 ]
 
 
@@ -61,7 +73,15 @@ def test_grouped_parity(gpu_lib, case):
     run_case(gpu_lib, *case)
 
 
-@pytest.mark.parametrize("case", CASES[:2], ids=[c[0] for c in CASES[:2]])
+@pytest.mark.parametrize("case", DECODE_CASES, ids=[c[0] for c in DECODE_CASES])
+def test_grouped_parity_decode(gpu_lib, case):
+    run_case(gpu_lib, *case, check_bwd=case[4] % 16 == 0)
+
+
+F16_CASES = CASES[:2] + DECODE_CASES[2:3]
+
+
+@pytest.mark.parametrize("case", F16_CASES, ids=[c[0] for c in F16_CASES])
 def test_grouped_parity_f16(gpu_lib, case):
     """The grouped calls with fp16 compute (qlora_linear_*_grouped_f16)."""
     run_case(gpu_lib, *case, f16=True)
@@ -73,12 +93,13 @@ def test_grouped_7b_layers(gpu_lib, parts):
     run_case(gpu_lib, f"7b_{len(parts)}", 2048, parts, 4096, 16, 32.0)
 
 
-def test_grouped_equals_separate_calls(gpu_lib):
+@pytest.mark.parametrize("m", [96, 3], ids=["gemm_m96", "gemv_m3"])
+def test_grouped_equals_separate_calls(gpu_lib, m):
     """One part of a grouped call and the single-linear call on that part's
     own packed weight give the same Y within float32 accumulation order."""
     import torch
 
-    parts, k, m, r, alpha = (256, 512), 256, 96, 16, 32.0
+    parts, k, r, alpha = (256, 512), 256, 16, 32.0
     ws = [synth.normal((n, k), 0.02, "grouped_sep", f"W{l}") for l, n in enumerate(parts)]
     x = to_bf16(synth.normal((m, k), 1.0, "grouped_sep", "X")).cuda()
     a = [to_bf16(synth.normal((r, k), 1.0 / r, "grouped_sep", f"A{l}")).cuda() for l in range(2)]
