@@ -8,27 +8,20 @@
 // bound by the HBM stream of the packed weight (0.5 B of codes + 1/64 B of
 // scale codes per weight) and by the latency of one trip to memory, so the
 // kernel is built around that stream:
-//   * a workgroup owns 16 weight rows; its WAVES x 4 lane groups split the
+//   * a workgroup owns 16 weight rows; its 16 waves x 4 lane groups split the
 //     row's 64-blocks round-robin, so every lane loads whole blocks (32 B of
-//     codes, two 16-byte loads); all loads of a pass are issued
-//     unconditionally (clamped addresses; an out-of-range block gets a zero
-//     scale) before the first is used, so a pass costs one memory round
-//     trip -- a guarded load would make the compiler wait for every
-//     outstanding load at the guard;
+//     codes, two 16-byte loads), from clamped addresses (an out-of-range block
+//     gets a zero scale) so that no load sits behind a guard;
 //   * per block a lane decodes the scale, builds a 16-entry bf16 table in
-//     registers (nf4_lut.h) and looks up 8 weights per table access, in
-//     natural order, so X is used as it lies in memory;
+//     registers (nf4_lut.h) and looks up 8 weights per table access;
 //   * the dot products run on the matrix cores (16x16x32 bf16 MFMA with the
 //     tokens padded to 16), so the vector ALU only unpacks;
-//   * with kFuseH every workgroup computes H = X A^T for itself, so the
-//     LoRA-down product needs no launch of its own: in each pass a wave
-//     multiplies 8 consecutive 32-wide chunks of X and A (lanes of one
-//     16-byte load cover 16 rows x 64 contiguous bytes, so a cache line is
-//     consumed by two neighbouring loads). The first 4 chunks are loaded
-//     before the weight codes and multiplied while the codes are still in
-//     flight; the other 4 are loaded behind the codes and multiplied after
-//     the main product. Without kFuseH (large r * k), H arrives as partial
-//     sums from the skinny kernel;
+//   * the X fragments (and, with kFuseH, the A fragments of the LoRA-down
+//     product H = X A^T) come through LDS: each wave copies the 256-k slice
+//     its lane groups multiply into a private region in whole runs, so every
+//     workgroup computes H for itself without a launch or a barrier of its
+//     own. Without kFuseH (r > 16), H arrives as partial sums from the
+//     skinny kernel;
 //   * partial sums of the waves are reduced in a fixed order in LDS, so
 //     results do not depend on scheduling.
 #include "bufmem.h"
@@ -60,6 +53,11 @@ __device__ __forceinline__ int part_slot0(const LoraParts& P, int p, int rb) {
   return off;
 }
 
+// Multi-pass form for k > 4096: one workgroup per group of 16 weight rows,
+// passes of 64 blocks (one per lane group). In each pass a wave stages the
+// 256-k slice of X, then of A, that its lane groups multiply through its own
+// LDS region (see the persistent form below for the layout), so neither the
+// fragment loads nor the H product need anything from another wave.
 template <int WAVES, bool kDQ, bool kFuseH, bool kF16>
 __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
                                                           const uint16_t* __restrict__ a,
@@ -67,14 +65,13 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
                                                           const uint16_t* __restrict__ b, int rh, int rb,
                                                           LoraParts P, float s, uint16_t* __restrict__ y,
                                                           float* __restrict__ h_out, Levels L) {
-  static_assert(WAVES == 16, "one pass covers 64 blocks; A is staged as 16 rows x 64 blocks");
+  static_assert(WAVES == 16, "one pass covers 64 blocks, four per wave");
   constexpr int kLaneGroups = WAVES * 4;
-  // With kFuseH, the pass's slice of A (16 ranks x 4096 k, bf16) lives in LDS;
-  // after the last pass the same bytes hold the cross-wave reductions.
-  constexpr int kARow = kLaneGroups * 64 * 2;  // bytes of one rank row of the slice
+  constexpr int kSlice = 16 * 512;  // one wave's region: 16 rows x 256 k of bf16
   constexpr int kRedBytes = (kFuseH ? 2 : 1) * WAVES * 64 * 16;
-  constexpr int kStage = kFuseH ? 16 * kARow : kRedBytes;
-  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage > kRedBytes ? kStage : kRedBytes];
+  constexpr int kStage = WAVES * kSlice;
+  static_assert(kStage >= kRedBytes, "the reductions reuse the staging regions");
+  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage];
   __shared__ float h_lds[16 * QLORA_MAX_RANK];
   __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
   f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(stage);
@@ -92,58 +89,74 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
   const int n0 = blockIdx.x * 16;
   const int n = n0 + i;
   const int n_c = n < N ? n : N - 1;  // clamped: every load is unconditional
-  // X through a buffer resource sized to its M rows: the lanes of padding
-  // tokens (i >= M) read zeros without touching memory (with one token, 15 of
-  // every 16 lanes). A likewise with its r rows.
+  // X through a buffer resource sized to its M rows, A to its rh rows: rows
+  // past them read zeros without touching memory
   const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), static_cast<short>(0),
                                                                         M * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), static_cast<short>(0),
                                                                         kFuseH ? rh * K * 2 : 0, 0x00020000);
   const int wv_u = __builtin_amdgcn_readfirstlane(wave);
+  unsigned char* region = stage + wv_u * kSlice;
+  const int crow = lane >> 5;
+  // the wave's slice of pass `base`: copy t moves rows 2t and 2t+1, lane l
+  // fetches piece (l & 31) ^ row of row 2t + (l >> 5) into slot l of the copy
+  auto copy_slice = [&](__amdgpu_buffer_rsrc_t rsrc, int rows, int base) {
+    const int ncopy = (rows + 1) >> 1;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t < ncopy) {
+        const int row = 2 * t + crow;
+        const int goff = row * K * 2 + (base + 4 * wv_u) * 128 + 16 * ((lane & 31) ^ row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(region + t * 1024), 16, goff, 0, 0, 0);
+      }
+    }
+  };
+  // fragment j of lane (i, g): piece 8 g + j of row i
+  auto read_frag = [&](int j) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(region + i * 512 + 16 * ((8 * g + j) ^ i));
+  };
 
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 hacc = f32x4{0.f, 0.f, 0.f, 0.f};
   constexpr int kBPer = (16 * QLORA_MAX_RANK + WAVES * 64 - 1) / (WAVES * 64);  // B values per thread
   uint16_t bv[kBPer];
   const int blast = N * rb - 1;
+  if (rb > 0) {
+    // this workgroup's 16 rows of B (contiguous in memory), into registers
+    // now and into LDS after the main product (indices clamped to the last
+    // element of B; rows past N are never stored)
+#pragma unroll
+    for (int u = 0; u < kBPer; ++u) {
+      const int e = n0 * rb + tid + u * WAVES * 64;
+      bv[u] = b[e < blast ? e : blast];
+    }
+  }
+  if (!kFuseH && rh > 0) {
+    // H = sum of the LoRA-down partials (fixed order)
+    const int mr = M * rh;
+    for (int idx = tid; idx < mr; idx += WAVES * 64) {
+      float hv = 0.0f;
+      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
+      h_lds[idx] = hv;
+      if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
+    }
+  }
 
-  // One block per lane group per pass. All loads of a pass (codes, scale,
-  // X) are issued unconditionally from clamped addresses before any is used;
-  // a block past the row or past K gets a zero scale, so its weights are 0.
   for (int base = 0; base < nbk; base += kLaneGroups) {
-    if (base == 0 && rb > 0) {
-      // this workgroup's 16 rows of B (contiguous in memory), into registers
-      // now and into LDS after the main product, so that no wait for them
-      // holds up the weight loads (indices clamped to the last element of B;
-      // rows past N are never stored). With r = 0 there is no B to read.
-#pragma unroll
-      for (int u = 0; u < kBPer; ++u) {
-        const int e = n0 * rb + tid + u * WAVES * 64;
-        bv[u] = b[e < blast ? e : blast];
-      }
-    }
-    if (kFuseH) {
-      // Rank row `wave` of the pass's slice of A, global -> LDS in 8 copies
-      // of 1 KB (contiguous in memory: whole cache lines). Lane l of copy t
-      // fetches 16-byte piece 64 t + (l ^ wave) of the row into LDS slot l,
-      // so the 16 ranks of one piece land in 16 different bank groups.
-      // Bytes past the end of the row's k range are never multiplied.
-      if (base > 0) __syncthreads();  // the previous slice has been read
-      const int roff = (wv_u * K + base * 64) * 2 + 16 * (lane ^ wave);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(stage + wv_u * kARow + t * 1024), 16,
-                                                 roff + t * 1024, 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    const bool has_slice = base + wave * 4 < nbk;  // wave-uniform
     const int kb = base + G;
-    const int kb_c = kb < nbk ? kb : nbk - 1;
+    const bool kval = kb < nbk;
+    const int kb_c = kval ? kb : nbk - 1;
+    // this pass's X slice, then its codes and scales; wait for the copies
+    // only (the previous pass's reads of the region are done: lgkmcnt below)
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_slice) copy_slice(xrsrc, M, base);
+    __builtin_amdgcn_sched_barrier(0);
     const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_c * 32));
     const u32x4 c0 = __builtin_nontemporal_load(cp);
     const u32x4 c1 = __builtin_nontemporal_load(cp + 1);
     const int bi = n_c * nbk + kb_c;
-    uint32_t scode = 0;
+    uint8_t scode = 0;
     float gsc;
     if (kDQ) {
       scode = w.scale_codes[bi];
@@ -151,23 +164,27 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     } else {
       gsc = w.absmax[bi];
     }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 + (kDQ ? 2 : 1)>();
+    __builtin_amdgcn_sched_barrier(0);
     u32x4 xa[8];
-    const int xoff = (i * K + kb_c * 64) * 2;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = decode_order(__builtin_amdgcn_raw_buffer_load_b128(xrsrc, xoff + 16 * j, 0, 0));
-    if (base == 0 && !kFuseH) {
-      // H = sum of the LoRA-down partials (fixed order)
-      const int mr = M * rh;
-      for (int idx = tid; idx < mr; idx += WAVES * 64) {
-        float hv = 0.0f;
-        for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
-        h_lds[idx] = hv;
-        if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
-      }
+    for (int j = 0; j < 8; ++j) xa[j] = u32x4{0, 0, 0, 0};
+    if (has_slice && kval && i < M) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xa[j] = read_frag(j);
     }
-    // wave-uniform: skip a pass slot no lane group of this wave uses
-    if (base + wave * 4 < nbk) {
-      const bool ok = (n < N) && (kb < nbk);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) xa[j] = decode_order(xa[j]);
+    if (kFuseH) {
+      // the region's X is in registers: this pass's slice of A replaces it
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragment reads are done
+      if (has_slice) copy_slice(arsrc, rh, base);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (has_slice) {
+      const bool ok = (n < N) && kval;
       const float sc = kDQ ? dq_unit(scode, w.dq) * gsc : gsc;
       const BlockLut lut = make_block_lut<kF16>(L.v, ok ? sc : 0.0f);
 #pragma unroll
@@ -179,23 +196,26 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
       }
     }
     if (kFuseH) {
-      // H product of the pass, after the main one so that the copies of A
-      // overlap it. All loads are consumed by now; wait for the copies, and
-      // for every wave's through the barrier.
+      // H product of the pass from the wave's own copies of A
+      __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<0>();
-      __syncthreads();
-      if (base + wave * 4 < nbk) {
-        const bool kval = kb < nbk;
-        // this lane's A fragments: rank i, pieces 8 G + j of the slice
-        const unsigned char* arow = stage + i * kARow;
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_slice) {
+        u32x4 af[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int p = 8 * G + j;
-          const u32x4 af = *reinterpret_cast<const u32x4*>(arow + (p >> 6) * 1024 + 16 * ((p & 63) ^ i));
-          hacc = mma16<kF16>(xa[j], kval ? decode_order(af) : u32x4{0, 0, 0, 0}, hacc);
+        for (int j = 0; j < 8; ++j) af[j] = u32x4{0, 0, 0, 0};
+        if (kval && i < rh) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) af[j] = read_frag(j);
         }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hacc = mma16<kF16>(xa[j], decode_order(af[j]), hacc);
       }
     }
+    // the next pass's copies overwrite the region: its reads must be done
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
   }
 #pragma unroll
   for (int u = 0; u < kBPer; ++u) {
@@ -203,7 +223,7 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     if (idx < 16 * rb) b_lds[idx] = bv[u];  // rb = 0: never, bv unset
   }
 
-  if (kFuseH) __syncthreads();  // the last slice of A has been read
+  __syncthreads();  // every wave is done with its region
   red[wave][lane] = acc;
   if (kFuseH) hred[wave][lane] = hacc;
   __syncthreads();

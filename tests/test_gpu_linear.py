@@ -107,9 +107,10 @@ def test_linear_parity_float8_scales(gpu_lib, case):
 
 
 @pytest.mark.parametrize("m", [1, 4, 16])
-@pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096)])
+@pytest.mark.parametrize("n,k", [(4096, 4096), (11008, 4096), (4096, 11008)])
 def test_decode_7b_shapes(gpu_lib, m, n, k):
-    """The decode (GEMV) path at the 7B layer shapes, forward only."""
+    """The decode (GEMV) path at the 7B layer shapes, forward only (k = 11008:
+    the multi-pass form, three passes, the last one partial)."""
     _run_case(gpu_lib, f"decode_{n}x{k}_m{m}", m, n, k, 16, 32.0, True, check_bwd=False)
 
 
