@@ -136,7 +136,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     const int mr = M * rh;
     for (int idx = tid; idx < mr; idx += WAVES * 64) {
       float hv = 0.0f;
-      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
+#pragma unroll 8
+      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];  // loads in flight together, sums in order
       h_lds[idx] = hv;
       if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
     }
@@ -403,7 +404,8 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
     const int mr = M * rh;
     for (int idx = tid; idx < mr; idx += WAVES * 64) {
       float hv = 0.0f;
-      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];
+#pragma unroll 8
+      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];  // loads in flight together, sums in order
       h_lds[idx] = hv;
       if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
     }

@@ -663,7 +663,9 @@ hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m
 
 int skinny_splits(int64_t m, int64_t qn) {
   if (m > 16) return 1;
-  const int64_t s = (qn + 511) / 512;  // ~512 contraction elements per workgroup
+  // ~128 contraction elements per workgroup: the decode projection is one
+  // memory round trip per workgroup, so it wants many of them
+  const int64_t s = (qn + 127) / 128;
   return static_cast<int>(s < 1 ? 1 : (s > 64 ? 64 : s));
 }
 
