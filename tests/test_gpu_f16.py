@@ -53,6 +53,7 @@ CASES = [
     ("m1_r8", 1, 256, 256, 8, 16.0, True),                         # decode, H inside the GEMV
     ("m16_r16", 16, 512, 320, 16, 32.0, True),
     ("decode_rank24_m8", 8, 128, 256, 24, 48.0, True),             # decode, H from the skinny kernel
+    ("decode_k4608_m3_r16", 3, 256, 4608, 16, 32.0, True),         # decode, k > 4096: two passes
     ("rank5_m40", 40, 128, 256, 5, 10.0, True),                    # rank gradients without the fused kernel
     ("rank64_m64", 64, 256, 512, 64, 16.0, True),
     ("no_dq_m96", 96, 384, 448, 16, 32.0, False),

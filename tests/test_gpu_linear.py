@@ -84,6 +84,7 @@ INT4_CASES = [
     ("int4_ragged_m300_n272_k320_r8", 300, 272, 320, 8, 16.0, True),
     ("int4_decode_m1_r8", 1, 256, 256, 8, 16.0, True),
     ("int4_decode_rank24_m8", 8, 128, 256, 24, 48.0, True),
+    ("int4_decode_k4608_m16", 16, 256, 4608, 16, 32.0, True),   # k > 4096: two passes
     ("int4_no_dq_m96", 96, 384, 448, 16, 32.0, False),
 ]
 
