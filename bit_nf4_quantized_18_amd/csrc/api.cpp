@@ -260,7 +260,7 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     const int splits = qlora::skinny_splits(m, k);
     if (r > 0 && !qlora::gemv_fuses_h(k, r)) {
       hpart = reinterpret_cast<float*>(base + L.h32);
-      QLORA_TRY(qlora::launch_skinny(x, a, m, k, r, rp, 1.0f, 1.0f, hpart, nullptr, splits, stream, f16));
+      QLORA_TRY(qlora::launch_skinny_decode(x, a, m, k, r, rp, hpart, splits, stream, f16));
     }
     QLORA_TRY(qlora::launch_gemv(pw, x, m, a, hpart, splits, b, r, s, y, h_out, stream, f16, grp));
   } else {

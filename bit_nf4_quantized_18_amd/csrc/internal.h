@@ -58,6 +58,11 @@ hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_
                          float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits, hipStream_t s,
                          bool f16 = false);
 int skinny_splits(int64_t m, int64_t qn);
+// Decode (m <= 16) partial sums of the same projection with scale 1: part is
+// splits x m x r float32, splits = skinny_splits(m, qn); rpad / 16 in
+// {2, 4, 6, 8} (the GEMV computes H itself for r <= 16).
+hipError_t launch_skinny_decode(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
+                                float* part, int splits, hipStream_t s, bool f16 = false);
 
 // Prefill (m > 16) form of the same projection, split over the contraction
 // for parallelism: raw partials in part (skinny_prefill_splits(m, qn, r) x m x r

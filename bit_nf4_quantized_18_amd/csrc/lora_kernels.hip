@@ -21,7 +21,7 @@ namespace {
 // output column tiles (0: only the reordered copy of P is produced). Narrow
 // ranks get more waves per row block, so that each wave makes only one or
 // two trips to memory.
-template <int RT, int WAVES, bool kF16>
+template <int RT, int WAVES, bool kF16, int kU = 0>
 __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Q,
                                                      int64_t M, int64_t qn, int r, int rpad, float scale,
                                                      float scale2, float* __restrict__ out_f32,
@@ -41,10 +41,11 @@ __global__ __launch_bounds__(WAVES * 64) void skinny_kernel(const uint16_t* __re
 #pragma unroll
   for (int t = 0; t < kRT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // U chunks per wave per trip. Loads are unconditional from clamped
-  // addresses (a guarded load makes the compiler wait for all outstanding
-  // loads); chunks past the split and ranks past r are zeroed at the operand.
-  constexpr int U = (RT <= 2) ? 4 : (RT <= 4 ? 8 : 4);
+  // U chunks per wave per trip (kU if given). Loads are unconditional from
+  // clamped addresses (a guarded load makes the compiler wait for all
+  // outstanding loads); chunks past the split and ranks past r are zeroed at
+  // the operand.
+  constexpr int U = kU > 0 ? kU : ((RT <= 2) ? 4 : (RT <= 4 ? 8 : 4));
   const int64_t m_c = m < M ? m : M - 1;
   for (int64_t c0 = c_begin + wave; c0 < c_end; c0 += WAVES * U) {
     u32x4 a[U], b[U][kRT];
@@ -567,6 +568,21 @@ __global__ void rank_grad_final_kernel(const float* __restrict__ part0, const fl
   db[idx] = scale * sum;
 }
 
+// Decode form (m <= 16, partial sums only): 4 waves, one 32-wide chunk per
+// wave, splits of 4 chunks (skinny_splits), so every wave makes exactly one
+// trip to memory with only the loads its chunk needs.
+template <int RT>
+void launch_skinny_decode_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn,
+                             int r, int rpad, float* out_f32, int splits, bool f16) {
+  if (f16) {
+    hipLaunchKernelGGL((skinny_kernel<RT, 4, true, 1>), grid, dim3(256), 0, st, P, Q, m, qn, r, rpad, 1.0f, 1.0f,
+                       out_f32, nullptr, splits);
+  } else {
+    hipLaunchKernelGGL((skinny_kernel<RT, 4, false, 1>), grid, dim3(256), 0, st, P, Q, m, qn, r, rpad, 1.0f, 1.0f,
+                       out_f32, nullptr, splits);
+  }
+}
+
 template <int RT>
 void launch_skinny_rt(dim3 grid, hipStream_t st, const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r,
                       int rpad, float scale, float scale2, float* out_f32, uint16_t* out_bf16, int splits, bool f16) {
@@ -663,10 +679,24 @@ hipError_t launch_skinny_prefill(const uint16_t* P, const uint16_t* Q, int64_t m
 
 int skinny_splits(int64_t m, int64_t qn) {
   if (m > 16) return 1;
-  // ~128 contraction elements per workgroup: the decode projection is one
-  // memory round trip per workgroup, so it wants many of them
-  const int64_t s = (qn + 127) / 128;
-  return static_cast<int>(s < 1 ? 1 : (s > 64 ? 64 : s));
+  // four 32-wide chunks (one per wave) per workgroup: the decode projection
+  // is one memory round trip per workgroup, so it wants many of them
+  const int64_t s = ((qn + 31) / 32 + 3) / 4;
+  return static_cast<int>(s < 1 ? 1 : (s > 128 ? 128 : s));
+}
+
+hipError_t launch_skinny_decode(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad,
+                                float* part, int splits, hipStream_t s, bool f16) {
+  if (m > 16) return hipErrorInvalidValue;
+  const dim3 grid(1, static_cast<unsigned>(splits));
+  switch (rpad / 16) {
+    case 2: launch_skinny_decode_rt<2>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
+    case 4: launch_skinny_decode_rt<4>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
+    case 6: launch_skinny_decode_rt<6>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
+    case 8: launch_skinny_decode_rt<8>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_skinny(const uint16_t* P, const uint16_t* Q, int64_t m, int64_t qn, int r, int rpad, float scale,
