@@ -28,6 +28,7 @@ DECODE_CASES = [
     ("gateup_decode_m16_k4160", 16, (512, 256), 4160, 16, 32.0),
     ("qkv_decode_r32_m7", 7, (256, 256, 256), 256, 32, 64.0),
     ("qkv_decode_r4_m3_k4608", 3, (256, 256, 512), 4608, 4, 8.0),
+    ("qkv_decode_r7_m2", 2, (256, 512, 256), 320, 7, 14.0),  # g r = 21: split partials, padded to 32 slots
 ]
 
 
