@@ -118,6 +118,22 @@ __global__ __launch_bounds__(256) void masked_lora_add_kernel(uint16_t* __restri
   const int64_t q0 = col0 + 8 * lane;
   if (q0 >= k) return;  // no barrier follows
 
+  // this lane's dX and keep bytes of its 4 rows, loaded before the rank
+  // loop so that their trip to memory overlaps it (rows past m: not loaded)
+  u32x4 gx[4];
+  u32x2 kx[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int64_t i = row0 + 4 * wave + rr;
+    gx[rr] = u32x4{0, 0, 0, 0};
+    kx[rr] = u32x2{0, 0};
+    if (i < m) {
+      const int64_t e0 = i * k + q0;
+      gx[rr] = *reinterpret_cast<const u32x4*>(dx + e0);
+      kx[rr] = *reinterpret_cast<const u32x2*>(keep + e0);
+    }
+  }
+
   float d[4][8];
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr)
@@ -146,8 +162,8 @@ __global__ __launch_bounds__(256) void masked_lora_add_kernel(uint16_t* __restri
     if (i >= m) break;
     const int64_t e0 = i * k + q0;
     u32x4* dst = reinterpret_cast<u32x4*>(dx + e0);
-    const u32x4 g = *dst;
-    const u32x2 kb = *reinterpret_cast<const u32x2*>(keep + e0);
+    const u32x4 g = gx[rr];
+    const u32x2 kb = kx[rr];
     u32x4 o;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
