@@ -113,13 +113,16 @@ def test_grouped_equals_separate_calls(gpu_lib, m):
     assert rel(f64(yg)[:, parts[0]:], f64(y1)) <= 1e-3
 
 
-def test_grouped_graph_replay_matches_eager(gpu_lib):
+@pytest.mark.parametrize("m", [96, 3], ids=["gemm_m96", "gemv_m3"])
+def test_grouped_graph_replay_matches_eager(gpu_lib, m):
     """Grouped forward + backward captured in a HIP graph: every replay
-    reproduces the eager results bit for bit."""
+    reproduces the eager results bit for bit, with the outputs and the
+    workspace overwritten between replays (m = 3: the decode GEMV with H from
+    split partials in the workspace)."""
     import torch
 
-    m, parts, k, r = 96, (256, 256, 256), 256, 16
-    tag = "grouped_graph"
+    parts, k, r = (256, 256, 256), 256, 16
+    tag = f"grouped_graph_m{m}"
     w = np.concatenate([synth.normal((n, k), 0.02, tag, f"W{l}") for l, n in enumerate(parts)], axis=0)
     q = gpu_lib.quantize(torch.from_numpy(w).cuda())
     x = to_bf16(synth.normal((m, k), 1.0, tag, "X")).cuda()
@@ -150,6 +153,7 @@ def test_grouped_graph_replay_matches_eager(gpu_lib):
         for rep in range(3):
             for v in bufs.values():
                 v.fill_(7)
+            ws.fill_(0xA5)
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
