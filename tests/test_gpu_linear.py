@@ -230,15 +230,17 @@ def test_fused_gemm_matches_dequantize_then_matmul(gpu_lib):
     assert rel(f64(y), f64(ref)) <= 4e-3
 
 
-@pytest.mark.parametrize("m", [4, 300])
-def test_graph_replay_matches_eager(gpu_lib, m):
+@pytest.mark.parametrize("m,k,r", [(4, 320, 16), (300, 320, 16), (4, 4608, 32)],
+                         ids=["gemv_fused_h", "gemm", "gemv_multipass_split_h"])
+def test_graph_replay_matches_eager(gpu_lib, m, k, r):
     """Forward + backward captured in a HIP graph: every replay (with eager
-    work and synchronisation in between) reproduces the eager results."""
+    work and synchronisation in between, outputs and workspace overwritten)
+    reproduces the eager results."""
     import torch
 
-    n, k, r = 256, 320, 16
-    w, x, a, b, dy = layer_inputs(n, k, m, r, f"graph{m}")
-    say(f"[linear] graph replay m={m}")
+    n = 256
+    w, x, a, b, dy = layer_inputs(n, k, m, r, f"graph{m}_{k}_{r}")
+    say(f"[linear] graph replay m={m} k={k} r={r}")
     q = gpu_lib.quantize(torch.from_numpy(w).cuda())
     xc, ac, bc, dyc = x.cuda(), a.cuda(), b.cuda(), dy.cuda()
     ws = torch.empty(gpu_lib.workspace_bytes(m, n, k, r), dtype=torch.uint8, device="cuda")
@@ -263,6 +265,7 @@ def test_graph_replay_matches_eager(gpu_lib, m):
         for rep in range(3):
             for v in bufs.values():
                 v.fill_(7)  # eager work between replays
+            ws.fill_(0xA5)
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
