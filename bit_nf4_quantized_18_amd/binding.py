@@ -29,7 +29,8 @@ EXPORTS = ("qlora_nf4_quantize", "qlora_nf4_dequantize", "qlora_linear_fwd", "ql
            "qlora_requantize", "qlora_linear_dropout_workspace_bytes", "qlora_linear_fwd_dropout",
            "qlora_linear_bwd_dropout", "qlora_dropout_mask", "qlora_linear_fwd_f16", "qlora_linear_bwd_f16",
            "qlora_linear_fwd_grouped_f16", "qlora_linear_bwd_grouped_f16", "qlora_linear_fwd_dropout_f16",
-           "qlora_linear_bwd_dropout_f16")
+           "qlora_linear_bwd_dropout_f16", "qlora_linear_fwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20  # QLORA_NOALLOC_SCRATCH_BYTES
 
 CODEBOOK_NF4 = 0   # normal-quantile levels
 CODEBOOK_INT4 = 1  # 16 evenly spaced levels on [-1, 1]
@@ -72,6 +73,8 @@ def load():
     lib.qlora_linear_fwd_f16.restype = i32
     lib.qlora_linear_bwd_f16.argtypes = lib.qlora_linear_bwd.argtypes
     lib.qlora_linear_bwd_f16.restype = i32
+    lib.qlora_linear_fwd_noalloc.argtypes = [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp]
+    lib.qlora_linear_fwd_noalloc.restype = i32
     lib.qlora_linear_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.qlora_linear_workspace_bytes.restype = sz
     p64 = ctypes.POINTER(ctypes.c_int64)
@@ -306,6 +309,22 @@ def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool
             _stream())
     _check(st, "qlora_linear_fwd_f16" if f16 else "qlora_linear_fwd")
     return y, h
+
+
+def linear_fwd_noalloc(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, out=None, h_out=None):
+    """qlora_linear_fwd_noalloc: the bf16 forward on the library's own scratch
+    array (no workspace). ``out`` (bf16 (m, n)) and ``h_out`` (float32
+    (m, r)) may be preallocated; h is returned only when ``h_out`` is given."""
+    import torch
+
+    m = x.shape[0]
+    r = 0 if a is None else a.shape[0]
+    y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=x.device)
+    wc = q.c_struct()
+    st = load().qlora_linear_fwd_noalloc(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(y),
+                                         _ptr(h_out), _stream())
+    _check(st, "qlora_linear_fwd_noalloc")
+    return y, h_out
 
 
 def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, need_dx: bool = True,

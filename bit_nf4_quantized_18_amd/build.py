@@ -35,6 +35,7 @@ SOURCES = {
     "dropout_kernels.hip": DEVICE,
     "gemv_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
     "gemm_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
+    "noalloc.hip": DEVICE,
 }
 
 

@@ -216,7 +216,7 @@ namespace {
 qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x, int64_t m,
                              const uint16_t* a, const uint16_t* b, int r, int rpart, float alpha, uint16_t* y,
                              float* h_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                             const DropArg* drop = nullptr, bool f16 = false) {
+                             const DropArg* drop = nullptr, bool f16 = false, bool fwd_sized_ws = false) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
@@ -232,9 +232,12 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
   const int64_t n = w->n, k = w->k;
   const bool grouped = grp != nullptr;
   if (drop != nullptr && r == 0) drop = nullptr;  // no adapter, nothing to drop
-  const size_t need = drop != nullptr ? static_cast<size_t>(drop_total(m, n, k, r))
-                      : grouped       ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
-                                      : qlora_linear_workspace_bytes(m, n, k, r);
+  // the public calls size one workspace for both directions; a caller-owned
+  // scratch area is checked against the forward's own layout
+  const size_t need = fwd_sized_ws    ? static_cast<size_t>(fwd_layout(m, n, k, r).total)
+                      : drop != nullptr ? static_cast<size_t>(drop_total(m, n, k, r))
+                      : grouped         ? qlora_linear_grouped_workspace_bytes(m, n, k, grp->g, rpart)
+                                        : qlora_linear_workspace_bytes(m, n, k, r);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return QLORA_ERR_WORKSPACE;
   if (ws != nullptr && !aligned16(ws)) return QLORA_ERR_ALIGN;
 
@@ -410,6 +413,26 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int6
                               size_t ws_bytes, hipStream_t stream) {
   return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, ws, ws_bytes, stream);
 }
+
+}  // extern "C"
+
+namespace qlora {
+
+size_t linear_fwd_scratch_bytes(int64_t m, int64_t n, int64_t k, int r) {
+  if (m <= 0 || n <= 0 || k <= 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  return static_cast<size_t>(fwd_layout(m, n, k, r).total);
+}
+
+qlora_status linear_fwd_scratch(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                                const uint16_t* b, int r, float alpha, uint16_t* y, float* h_out, void* scratch,
+                                size_t scratch_bytes, hipStream_t stream) {
+  return linear_fwd_impl(w, nullptr, x, m, a, b, r, r, alpha, y, h_out, scratch, scratch_bytes, stream, nullptr, false,
+                         true);
+}
+
+}  // namespace qlora
+
+extern "C" {
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight* w, const uint16_t* x, const uint16_t* dy, int64_t m,
                               const uint16_t* a, const uint16_t* b, int r, float alpha, const float* h_saved,

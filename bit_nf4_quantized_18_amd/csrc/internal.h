@@ -156,4 +156,13 @@ hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, cons
                              int64_t n, int64_t m, int r0, const LoraParts* parts, float scale, int splits, float* part,
                              float* da, float* db, hipStream_t st, bool f16 = false);
 
+// The plain forward (qlora_linear_fwd) on a scratch area the caller
+// provides, checked against the forward's own workspace layout
+// (linear_fwd_scratch_bytes) rather than the two-direction size of the
+// public calls; QLORA_ERR_WORKSPACE if it is too small.
+size_t linear_fwd_scratch_bytes(int64_t m, int64_t n, int64_t k, int r);
+qlora_status linear_fwd_scratch(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                                const uint16_t* b, int r, float alpha, uint16_t* y, float* h_out, void* scratch,
+                                size_t scratch_bytes, hipStream_t stream);
+
 }  // namespace qlora

@@ -272,6 +272,33 @@ qlora_status qlora_linear_bwd_dropout_f16(const qlora_nf4_weight* w, const uint1
  * for these sizes (the larger of the two); 0 if none. Host only, no GPU use. */
 size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 
+/* Largest scratch area qlora_linear_fwd_noalloc uses (16 MiB per device). */
+#define QLORA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The call itself allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine). The forward's
+ * scratch (split partial sums of H and the padded bf16 s H of the matmul
+ * path; partial sums of H on the decode path when r > 16) lives in a
+ * library-owned device array of QLORA_NOALLOC_SCRATCH_BYTES, one per
+ * device, held until the process ends; its device address is looked up on
+ * the first call on each device.
+ *   Arguments, layouts, limits and results are those of qlora_linear_fwd
+ *   (the same kernels: outputs are bit-identical to qlora_linear_fwd's on the
+ *   same inputs). The caller still allocates x, a, b, y and h_out.
+ *   Every call on one device shares that device's array, and the array keeps
+ *   the last call's contents (nothing in it needs to start at zero): calls
+ *   that overlap on one device (different streams or threads without
+ *   ordering) race and give undefined results. Order them on one stream.
+ * Errors: as qlora_linear_fwd; QLORA_ERR_WORKSPACE when these sizes need
+ * more than QLORA_NOALLOC_SCRATCH_BYTES (checked on the host before
+ * anything is enqueued); QLORA_ERR_HIP if the array's address cannot be
+ * found on the current device. */
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t* x, int64_t m,
+                                      const uint16_t* a, const uint16_t* b, int r, float alpha,
+                                      uint16_t* y, float* h_out, hipStream_t stream);
+
 /* Grouped linears that read the same input: the adapted projections of one
  * block ("LoRA y QLoRA en Profundidad", "Modulos Objetivo": q/k/v of the
  * attention, gate/up of the MLP), run as one call over their stacked weights.
