@@ -327,12 +327,16 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------- decode GEMV
-    shapes = [(4096, 4096), (11008, 4096)]
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
+
+    def dlay(n, k):
+        return next(l for l in synth.DECODE_7B.layers if (l.n, l.k) == (n, k))
+
     if want("decode"):
         dec = []
         for (n, k) in shapes:
-            lay = synth.Linear(f"{n}x{k}", n, k)
-            w = torch.from_numpy(synth.weight(synth.DECODE_7B, synth.DECODE_7B.layers[0 if n == 4096 else 1]))
+            lay = dlay(n, k)
+            w = torch.from_numpy(synth.weight(synth.DECODE_7B, lay))
             q0 = qn.quantize(w.to(dev))
             del w
             per_copy = q0.codes.numel() + q0.scale_codes.numel() + 4 * q0.group_scale.numel()
@@ -342,7 +346,7 @@ def main():
                     for _ in range(copies)]
             a = torch.from_numpy(synth.lora_a(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
             b = torch.from_numpy(synth.lora_b(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
-            for m in (1, 4, 16):
+            for m in (1, 2, 4, 16):
                 x = torch.from_numpy(synth.activations(synth.DECODE_7B, lay, m)).to(torch.bfloat16).to(dev)
                 y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
                 ws = torch.empty(qn.workspace_bytes(m, n, k, 16), dtype=torch.uint8, device=dev)
@@ -472,8 +476,8 @@ def main():
 
     if want("quant"):
         qres = []
-        for (n, k) in shapes:
-            w = torch.from_numpy(synth.weight(synth.DECODE_7B, synth.DECODE_7B.layers[0 if n == 4096 else 1])).to(dev)
+        for (n, k) in shapes[:2]:
+            w = torch.from_numpy(synth.weight(synth.DECODE_7B, dlay(n, k))).to(dev)
             copies = max(2, int(1.2e9 // (4 * n * k)))
             ws_pool = [w.clone() for _ in range(copies)]
             codes = torch.empty(n * k // 2, dtype=torch.uint8, device=dev)
@@ -505,8 +509,8 @@ def main():
     # ------------------------------------------- merge / unmerge / re-quantize
     if want("merge"):
         mres = []
-        for (n, k) in shapes:
-            lay = synth.DECODE_7B.layers[0 if n == 4096 else 1]
+        for (n, k) in shapes[:2]:
+            lay = dlay(n, k)
             q = qn.quantize(torch.from_numpy(synth.weight(synth.DECODE_7B, lay)).to(dev))
             a = torch.from_numpy(synth.lora_a(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
             b = (torch.from_numpy(synth.lora_b(synth.DECODE_7B, lay)) + 0.01).to(torch.bfloat16).to(dev)

@@ -34,6 +34,7 @@ SOURCES = {
     "lora_kernels.hip": DEVICE,
     "dropout_kernels.hip": DEVICE,
     "gemv_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
+    "gemv_mfma.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
     "gemm_kernels.hip": DEVICE + ["-fhip-fp32-correctly-rounded-divide-sqrt"],
     "noalloc.hip": DEVICE,
 }

@@ -35,8 +35,9 @@ FwdLayout fwd_layout(int64_t m, int64_t n, int64_t k, int r, bool gemm = false) 
   Carve c;
   FwdLayout L{};
   if (m <= kGemvMaxM && !gemm) {
-    // decode: H partial sums, unless the GEMV computes H itself
-    L.h32 = c.take(qlora::gemv_fuses_h(k, r) ? 0 : qlora::skinny_splits(m, k) * m * r * 4);
+    // decode: H partial sums, unless the GEMV computes H itself (a grouped
+    // call fuses whenever the ungrouped rule does)
+    L.h32 = c.take(r == 0 || qlora::gemv_fuses_h(m, k, r, nullptr) ? 0 : qlora::skinny_splits(m, k) * m * r * 4);
     L.hs = c.take(0);
   } else {
     L.h32 = c.take(m * r * 4);
@@ -261,7 +262,7 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
     // partial sums in the workspace, which the GEMV sums.
     float* hpart = nullptr;
     const int splits = qlora::skinny_splits(m, k);
-    if (r > 0 && !qlora::gemv_fuses_h(k, r)) {
+    if (r > 0 && !qlora::gemv_fuses_h(m, k, r, grp)) {
       hpart = reinterpret_cast<float*>(base + L.h32);
       QLORA_TRY(qlora::launch_skinny_decode(x, a, m, k, r, rp, hpart, splits, stream, f16));
     }

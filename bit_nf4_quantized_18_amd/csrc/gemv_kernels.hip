@@ -1,29 +1,32 @@
-// Decode path (m <= 16 tokens): Y = X W16^T + s H B^T with W read straight
-// from its packed NF4 form, in one launch.
+// Decode path, one or two tokens and k <= 4096: Y = X W16^T + s H B^T with
+// W read straight from its packed NF4 form (3 to 16 tokens, and k > 4096:
+// gemv_mfma.hip).
 //
 // Ultralytics glossary "QLoRA", section "Come funziona QLoRA": each frozen
-// layer dequantizes its NF4 weights to bfloat16 right before the matmul and
-// adds the LoRA path output ("LoRA y QLoRA en Profundidad", "La Idea Central":
-// H = X A^T, then (alpha / r) H B^T). At a handful of tokens the layer is
-// bound by the HBM stream of the packed weight (0.5 B of codes + 1/64 B of
-// scale codes per weight) and by the latency of one trip to memory, so the
-// kernel is built around that stream:
-//   * a workgroup owns 16 weight rows; its 16 waves x 4 lane groups split the
-//     row's 64-blocks round-robin, so every lane loads whole blocks (32 B of
-//     codes, two 16-byte loads), from clamped addresses (an out-of-range block
-//     gets a zero scale) so that no load sits behind a guard;
-//   * per block a lane decodes the scale, builds a 16-entry bf16 table in
-//     registers (nf4_lut.h) and looks up 8 weights per table access;
-//   * the dot products run on the matrix cores (16x16x32 bf16 MFMA with the
-//     tokens padded to 16), so the vector ALU only unpacks;
-//   * the X fragments (and, with kFuseH, the A fragments of the LoRA-down
-//     product H = X A^T) come through LDS: each wave copies the 256-k slice
-//     its lane groups multiply into a private region in whole runs, so every
-//     workgroup computes H for itself without a launch or a barrier of its
-//     own. Without kFuseH (r > 16), H arrives as partial sums from the
-//     skinny kernel;
-//   * partial sums of the waves are reduced in a fixed order in LDS, so
-//     results do not depend on scheduling.
+// layer restores its weights as level[code] * block scale, in bfloat16,
+// right before the matmul, and adds the LoRA path ("LoRA y QLoRA en
+// Profundidad", "La Idea Central": H = X A^T, then (alpha / r) H B^T). At one
+// or two tokens the layer is bound by the HBM stream of the packed weight
+// (0.5 B of codes + 1/64 B of scale codes per weight) and by how few vector
+// instructions per weight the kernel spends on it:
+//   * the 16-entry codebook is expanded once per workgroup into a 256-entry
+//     LDS table indexed by a whole code byte: entry e holds the two 16-bit
+//     levels of its nibbles (low nibble -> low half), so one byte-permute (to
+//     form the address) and one LDS read give two weights. The table is
+//     stored 64 times, interleaved, and lane l reads copy l, so the 64 lanes
+//     of a read always hit 64 different banks;
+//   * the per-block scale is applied to the block's float32 partial sum,
+//     after the products of X with the 16-bit levels. In exact arithmetic
+//     that is sum_k x_k L[c_k] s_b, the restored weight; the operand carries
+//     the 16-bit rounding of the level rather than of level * scale (relative
+//     difference at most 2^-8 per weight, inside the layer's 1e-2 bound);
+//   * one wave per weight row, 2-wide dot products on the vector ALU, no
+//     partial sums across waves; H = X A^T (r <= 32, or 16 slots per part
+//     for grouped weights) is computed by every workgroup for the slots it
+//     needs, in the prologue; above that, H arrives as split partial sums of
+//     the decode projection kernel.
+#include <type_traits>
+
 #include "bufmem.h"
 #include "internal.h"
 #include "mfma.h"
@@ -32,476 +35,439 @@
 namespace qlora {
 namespace {
 
-constexpr int kGroup = 256;
+constexpr int kWaves = 16;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTabBytes = 256 * 64 * 4;          // 256 code bytes x 64 lane copies x 4 B
+struct GemvArgs {
+  PackedW w;
+  const uint16_t* x;
+  int M;
+  const uint16_t* a;   // fused H: the A rows (r x k, or g rpart x k)
+  int rh;              // rows of A / slots of H in total
+  const float* hpart;  // partial-sum H: hsplits x M x rh float32
+  int hsplits;
+  const uint16_t* b;   // n x rb
+  int rb;              // slots per output row (r, or rpart)
+  LoraParts P;
+  float s;
+  uint16_t* y;
+  float* h_out;
+  Levels L;
+};
 
-// 8 consecutive bf16 (x0x1, x2x3, x4x5, x6x7) -> the order lut8_decode_order
-// produces weights in, (x0x2, x4x6, x1x3, x5x7): an MFMA pairs operand slots
-// by position, so both operands only need the same order.
-__device__ __forceinline__ u32x4 decode_order(u32x4 v) {
-  const uint32_t in[4] = {v[0], v[1], v[2], v[3]};
-  uint32_t out[4];
-  to_decode_order(in, out);
-  return u32x4{out[0], out[1], out[2], out[3]};
+__device__ __forceinline__ int part_of(const LoraParts& P, int row) {
+  int l = 0;
+#pragma unroll
+  for (int q = 0; q + 1 < 4; ++q) l += (q + 1 < P.g && row >= P.end[q]) ? 1 : 0;
+  return l;
 }
 
-// First H slot of output row p: part l (rows up to P.end[l]) owns slots
-// l rb .. (l+1) rb - 1; with one part, 0.
-__device__ __forceinline__ int part_slot0(const LoraParts& P, int p, int rb) {
-  int off = 0;
+__device__ __forceinline__ int part_begin(const LoraParts& P, int l) { return l == 0 ? 0 : P.end[l - 1]; }
+
+// 16-bit level c of the table (bf16 or IEEE half, round to nearest even).
+template <bool kF16>
+__device__ __forceinline__ uint32_t level16(const Levels& L, int c) {
+  float v = L.v[0];
 #pragma unroll
-  for (int l = 0; l + 1 < 4; ++l) off += (l + 1 < P.g && p >= P.end[l]) ? rb : 0;
-  return off;
+  for (int q = 1; q < 16; ++q) v = (c == q) ? L.v[q] : v;
+  return to16<kF16>(v);
 }
 
-// Multi-pass form for k > 4096: one workgroup per group of 16 weight rows,
-// passes of 64 blocks (one per lane group). In each pass a wave stages the
-// 256-k slice of X, then of A, that its lane groups multiply through its own
-// LDS region (see the persistent form below for the layout), so neither the
-// fragment loads nor the H product need anything from another wave.
-template <int WAVES, bool kDQ, bool kFuseH, bool kF16>
-__global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
-                                                          const uint16_t* __restrict__ a,
-                                                          const float* __restrict__ hpart, int hsplits,
-                                                          const uint16_t* __restrict__ b, int rh, int rb,
-                                                          LoraParts P, float s, uint16_t* __restrict__ y,
-                                                          float* __restrict__ h_out, Levels L) {
-  static_assert(WAVES == 16, "one pass covers 64 blocks, four per wave");
-  constexpr int kLaneGroups = WAVES * 4;
-  constexpr int kSlice = 16 * 512;  // one wave's region: 16 rows x 256 k of bf16
-  constexpr int kRedBytes = (kFuseH ? 2 : 1) * WAVES * 64 * 16;
-  constexpr int kStage = WAVES * kSlice;
-  static_assert(kStage >= kRedBytes, "the reductions reuse the staging regions");
-  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage];
-  __shared__ float h_lds[16 * QLORA_MAX_RANK];
-  __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
-  f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(stage);
-  f32x4(*hred)[64] = reinterpret_cast<f32x4(*)[64]>(stage + WAVES * 64 * 16);
-  // the same buffers as floats: the reduction reads one component per lane
-  const float* redf = reinterpret_cast<const float*>(stage);
-  const float* hredf = reinterpret_cast<const float*>(stage + WAVES * 64 * 16);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  const int G = wave * 4 + g;
-  // 32-bit offsets: the host guarantees n * k <= 2^31
-  const int K = static_cast<int>(w.k), N = static_cast<int>(w.n);
-  const int nbk = K / 64;
-  const int n0 = blockIdx.x * 16;
-  const int n = n0 + i;
-  const int n_c = n < N ? n : N - 1;  // clamped: every load is unconditional
-  // X through a buffer resource sized to its M rows, A to its rh rows: rows
-  // past them read zeros without touching memory
-  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), static_cast<short>(0),
-                                                                        M * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), static_cast<short>(0),
-                                                                        kFuseH ? rh * K * 2 : 0, 0x00020000);
-  const int wv_u = __builtin_amdgcn_readfirstlane(wave);
-  unsigned char* region = stage + wv_u * kSlice;
-  const int crow = lane >> 5;
-  // the wave's slice of pass `base`: copy t moves rows 2t and 2t+1, lane l
-  // fetches piece (l & 31) ^ row of row 2t + (l >> 5) into slot l of the copy
-  auto copy_slice = [&](__amdgpu_buffer_rsrc_t rsrc, int rows, int base) {
-    const int ncopy = (rows + 1) >> 1;
+// The pair table: dword (e * 64 + copy) = level16(e & 15) | level16(e >> 4) << 16.
+// Thread tid writes dwords tid + 1024 i, i = 0..15: entry e = wave + 16 i,
+// so its low nibble is the (uniform) wave index and its high nibble is i.
+template <bool kF16>
+__device__ __forceinline__ void build_pair_table(unsigned char* tab, const Levels& L, int tid, int wv) {
+  const uint32_t lo = level16<kF16>(L, wv);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t < ncopy) {
-        const int row = 2 * t + crow;
-        const int goff = row * K * 2 + (base + 4 * wv_u) * 128 + 16 * ((lane & 31) ^ row);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(region + t * 1024), 16, goff, 0, 0, 0);
-      }
-    }
-  };
-  // fragment j of lane (i, g): piece 8 g + j of row i
-  auto read_frag = [&](int j) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(region + i * 512 + 16 * ((8 * g + j) ^ i));
-  };
-
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 hacc = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kBPer = (16 * QLORA_MAX_RANK + WAVES * 64 - 1) / (WAVES * 64);  // B values per thread
-  uint16_t bv[kBPer];
-  const int blast = N * rb - 1;
-  if (rb > 0) {
-    // this workgroup's 16 rows of B (contiguous in memory), into registers
-    // now and into LDS after the main product (indices clamped to the last
-    // element of B; rows past N are never stored)
-#pragma unroll
-    for (int u = 0; u < kBPer; ++u) {
-      const int e = n0 * rb + tid + u * WAVES * 64;
-      bv[u] = b[e < blast ? e : blast];
-    }
+  for (int q = 0; q < 16; ++q) {
+    const uint32_t hi = level16<kF16>(L, q);
+    *reinterpret_cast<uint32_t*>(tab + 4 * (tid + kThreads * q)) = lo | (hi << 16);
   }
-  if (!kFuseH && rh > 0) {
-    // H = sum of the LoRA-down partials (fixed order)
-    const int mr = M * rh;
-    for (int idx = tid; idx < mr; idx += WAVES * 64) {
-      float hv = 0.0f;
-#pragma unroll 8
-      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];  // loads in flight together, sums in order
-      h_lds[idx] = hv;
-      if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
-    }
-  }
-
-  for (int base = 0; base < nbk; base += kLaneGroups) {
-    const bool has_slice = base + wave * 4 < nbk;  // wave-uniform
-    const int kb = base + G;
-    const bool kval = kb < nbk;
-    const int kb_c = kval ? kb : nbk - 1;
-    // this pass's X slice, then its codes and scales; wait for the copies
-    // only (the previous pass's reads of the region are done: lgkmcnt below)
-    __builtin_amdgcn_sched_barrier(0);
-    if (has_slice) copy_slice(xrsrc, M, base);
-    __builtin_amdgcn_sched_barrier(0);
-    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_c * 32));
-    const u32x4 c0 = __builtin_nontemporal_load(cp);
-    const u32x4 c1 = __builtin_nontemporal_load(cp + 1);
-    const int bi = n_c * nbk + kb_c;
-    uint8_t scode = 0;
-    float gsc;
-    if (kDQ) {
-      scode = w.scale_codes[bi];
-      gsc = w.group_scale[static_cast<uint32_t>(bi) / kGroup];
-    } else {
-      gsc = w.absmax[bi];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<2 + (kDQ ? 2 : 1)>();
-    __builtin_amdgcn_sched_barrier(0);
-    u32x4 xa[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = u32x4{0, 0, 0, 0};
-    if (has_slice && kval && i < M) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) xa[j] = read_frag(j);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = decode_order(xa[j]);
-    if (kFuseH) {
-      // the region's X is in registers: this pass's slice of A replaces it
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragment reads are done
-      if (has_slice) copy_slice(arsrc, rh, base);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (has_slice) {
-      const bool ok = (n < N) && kval;
-      const float sc = kDQ ? dq_unit(scode, w.dq) * gsc : gsc;
-      const BlockLut lut = make_block_lut<kF16>(L.v, ok ? sc : 0.0f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t cw = (j < 4) ? c0[j] : c1[j - 4];
-        uint32_t wv[4];
-        lut8_decode_order(lut, cw, wv);
-        acc = mma16<kF16>(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
-      }
-    }
-    if (kFuseH) {
-      // H product of the pass from the wave's own copies of A
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<0>();
-      __builtin_amdgcn_sched_barrier(0);
-      if (has_slice) {
-        u32x4 af[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) af[j] = u32x4{0, 0, 0, 0};
-        if (kval && i < rh) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) af[j] = read_frag(j);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hacc = mma16<kF16>(xa[j], decode_order(af[j]), hacc);
-      }
-    }
-    // the next pass's copies overwrite the region: its reads must be done
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int u = 0; u < kBPer; ++u) {
-    const int idx = tid + u * WAVES * 64;
-    if (idx < 16 * rb) b_lds[idx] = bv[u];  // rb = 0: never, bv unset
-  }
-
-  __syncthreads();  // every wave is done with its region
-  red[wave][lane] = acc;
-  if (kFuseH) hred[wave][lane] = hacc;
-  __syncthreads();
-  const int l2 = tid & 63, v = tid >> 6;  // used by the first 256 threads
-  const int mo = 4 * (l2 >> 4) + v;       // token row of the 16 x 16 tile
-  if (kFuseH) {
-    // H[mo][j] of the (token, rank) tile, j = l2 & 15
-    if (tid < 256) {
-      const int j = l2 & 15;
-      float hv = 0.0f;
-#pragma unroll
-      for (int wv = 0; wv < WAVES; ++wv) hv += hredf[(wv * 64 + l2) * 4 + v];
-      if (mo < M && j < rh) {
-        h_lds[mo * rh + j] = hv;
-        if (h_out != nullptr && blockIdx.x == 0) h_out[mo * rh + j] = hv;
-      }
-    }
-    __syncthreads();
-  }
-  if (tid >= 256) return;
-  const int no = n0 + (l2 & 15);
-  if (mo >= M || no >= N) return;
-  float sum = 0.0f;
-#pragma unroll
-  for (int wv = 0; wv < WAVES; ++wv) sum += redf[(wv * 64 + l2) * 4 + v];
-  if (rb > 0) {
-    float lo = 0.0f;
-    const uint16_t* brow = b_lds + (l2 & 15) * rb;
-    const float* hrow = h_lds + mo * rh + part_slot0(P, no, rb);
-    for (int j = 0; j < rb; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
-    sum = fmaf(s, lo, sum);
-  }
-  y[mo * N + no] = to16<kF16>(sum);
 }
 
-// Persistent form for k <= 4096 (one pass covers a row): a workgroup takes
-// row groups rg = blockIdx.x, + gridDim.x, ... (grid = number of CUs) and
-// software-pipelines them: the codes, scales and B rows of the next row group
-// are in flight while the current one is unpacked and multiplied. X is loaded
-// once (the same fragments serve every row group) and, with kFuseH, H is
-// computed once per workgroup, in its first row group.
+// 8 weights (one dword of codes: element 2b in the low nibble of byte b) as
+// four dwords of 16-bit levels in natural order, from the pair table. The
+// byte-permute forms the LDS address (code byte << 8) | (lane << 2).
+__device__ __forceinline__ u32x4 lookup8(const unsigned char* tab, uint32_t cw, uint32_t lane4) {
+  u32x4 r;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    const uint32_t addr = __builtin_amdgcn_perm(cw, lane4, 0x0C0C0400u | ((4u + bb) << 8));
+    r[bb] = *reinterpret_cast<const uint32_t*>(tab + addr);
+  }
+  return r;
+}
+
+// Buffer resources of one call: out-of-range offsets read zeros.
+struct Rsrc {
+  __amdgpu_buffer_rsrc_t codes, sc, gs, am, x, a, b, hp;
+  int codes_oob, x_oob, a_oob, b_oob, hp_oob;
+};
+
+__device__ __forceinline__ Rsrc make_rsrcs(const GemvArgs& g, int nbk) {
+  Rsrc R;
+  const int N = static_cast<int>(g.w.n), K = static_cast<int>(g.w.k);
+  const int nb = N * nbk;
+  R.codes_oob = N * (K / 2);
+  R.codes = make_rsrc(g.w.codes, R.codes_oob);
+  R.sc = make_rsrc(g.w.scale_codes, g.w.dq ? nb : 0);
+  R.gs = make_rsrc(g.w.group_scale, g.w.dq ? 4 * ((nb + 255) / 256) : 0);
+  R.am = make_rsrc(g.w.absmax, g.w.dq ? 0 : 4 * nb);
+  R.x_oob = g.M * K * 2;
+  R.x = make_rsrc(g.x, R.x_oob);
+  R.a_oob = g.rh * K * 2;
+  R.a = make_rsrc(g.a, g.a != nullptr ? R.a_oob : 0);
+  R.b_oob = N * g.rb * 2;
+  R.b = make_rsrc(g.b, g.b != nullptr ? R.b_oob : 0);
+  R.hp_oob = g.hsplits * g.M * g.rh * 4;
+  R.hp = make_rsrc(g.hpart, g.hpart != nullptr ? R.hp_oob : 0);
+  return R;
+}
+
+// H from split partial sums (hsplits x M x rh float32). Thread t takes
+// output o = t % (M rh) and the splits grp, grp + groups, ... (grp = t /
+// (M rh), at most eight each), issued in the prologue with the other early
+// loads; the group sums meet in the partial-sum area and are added in group
+// order: a fixed order, so results do not depend on scheduling.
+struct HPart {
+  float v[8];
+  bool fast;
+  int groups;
+};
+
+__device__ __forceinline__ HPart issue_hpart(const GemvArgs& g, const Rsrc& R, int tid) {
+  HPart H;
+  const int mr = g.M * g.rh;
+  H.groups = mr <= kThreads ? kThreads / mr : 0;
+  if (H.groups > g.hsplits) H.groups = g.hsplits;
+  H.fast = H.groups > 0 && g.hsplits <= 8 * H.groups;
+  const int o = H.fast ? tid % mr : 0, grp = H.fast ? tid / mr : 0;
+  const bool active = H.fast && grp < H.groups;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int sp = grp + H.groups * u;
+    const int off = (active && sp < g.hsplits) ? 4 * (sp * mr + o) : R.hp_oob;
+    H.v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(R.hp, off, 0, 0));
+  }
+  return H;
+}
+
+// Before a barrier: the group sums into the partial-sum area, from float
+// offset off.
+__device__ __forceinline__ void put_hpart(const GemvArgs& g, float* red, const HPart& H, int tid) {
+  const int mr = g.M * g.rh;
+  if (H.fast && tid < H.groups * mr) {
+    float v = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += H.v[u];
+    red[tid] = v;
+  }
+}
+
+// Calls f(integral_constant<int, t>) for t = T .. E-1.
+template <int T, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (T < E) {
+    f(std::integral_constant<int, T>{});
+    static_for<T + 1, E>(f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// m <= 2 tokens, k <= 4096: one wave per weight row.
 //
-// X and A reach the fragments through LDS, one private 8 KB region per wave:
-// wave w's lane groups need the 256-k slice [256 w, 256 w + 256) of every
-// token (rank) row, 512 contiguous bytes per row, so the wave copies its
-// slice global -> LDS in whole 1 KB runs (two rows per copy) and reads its
-// fragments back. Read straight from global, each 16-byte fragment load
-// would touch a different cache line per lane group and token (64 lines per
-// load instead of 8 per copy). Piece p of row i is stored in slot p ^ i of
-// the row, so the 16 rows of one piece fall in 16 different bank groups. The
-// region holds X first; once X is in registers it receives the wave's slice
-// of A, which only that wave reads: H needs no barrier of its own.
-template <bool kDQ, bool kFuseH, bool kF16>
-__global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const uint16_t* __restrict__ x, int M,
-                                                               const uint16_t* __restrict__ a,
-                                                               const float* __restrict__ hpart, int hsplits,
-                                                               const uint16_t* __restrict__ b, int rh, int rb,
-                                                               LoraParts P, float s, uint16_t* __restrict__ y,
-                                                               float* __restrict__ h_out, Levels L) {
-  constexpr int WAVES = 16;
-  constexpr int kSlice = 16 * 512;  // one wave's region: 16 rows x 256 k of bf16
-  constexpr int kRedBytes = (kFuseH ? 2 : 1) * WAVES * 64 * 16;
-  constexpr int kStage = WAVES * kSlice;
-  constexpr int kBPer = (16 * QLORA_MAX_RANK + WAVES * 64 - 1) / (WAVES * 64);  // B values per thread
-  __shared__ __attribute__((aligned(16))) unsigned char stage[kStage > kRedBytes ? kStage : kRedBytes];
-  __shared__ float h_lds[16 * QLORA_MAX_RANK];
-  __shared__ uint16_t b_lds[16 * QLORA_MAX_RANK];
-  f32x4(*red)[64] = reinterpret_cast<f32x4(*)[64]>(stage);
-  f32x4(*hred)[64] = reinterpret_cast<f32x4(*)[64]>(stage + WAVES * 64 * 16);
-  // the same buffers as floats: the reduction reads one component per lane
-  const float* redf = reinterpret_cast<const float*>(stage);
-  const float* hredf = reinterpret_cast<const float*>(stage + WAVES * 64 * 16);
+// Lane l takes the 32 weights [2048 h + 32 l, 2048 h + 32 l + 32) of the row
+// for h = 0, 1: each code load is a whole 1 KB run of the row (16 bytes per
+// lane), the lane's weights are half of block 32 h + l / 2 (one scale each),
+// and the products are 2-wide dot products (v_dot2_f32_bf16) with X held in
+// registers in the same order; per half block the float32 sum is multiplied
+// by the block scale. The LoRA-up term enters as lane j's share s H[j] B[row][j]
+// (j < rb), and one butterfly sum over the 64 lanes gives the output. No
+// partial sums cross waves: the only barriers are the pair table's and H's.
+// H (fused, up to 32 slots) is one contiguous A row per wave, read in whole
+// 1 KB runs and dotted with X read from LDS in the same order.
+constexpr int kRowsX = 2 * 2 * 4096;  // X staging: up to 2 tokens x 4096 bf16
+constexpr int kRowsH = 2 * QLORA_MAX_RANK;  // H: up to 2 tokens x 128 slots
+constexpr int kRowsSmem = kTabBytes + kRowsX + 4 * kRowsH + 4 * kThreads;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <bool kF16>
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  if constexpr (kF16) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, a), __builtin_bit_cast(h2, b), c, false);
+  } else {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, a), __builtin_bit_cast(b2, b), c, false);
+  }
+}
+
+// Loads of one weight row for lane l (two 1 KB runs, the two scale codes or
+// absmax values, the row's two candidate group scales, B[row][l]).
+struct RowLoads {
+  u32x4 c[2];
+  uint32_t s[2];  // scale code bytes (DQ) or absmax bits
+  u32x2 gs;       // group scales of (row nbk) >> 8 and the next (DQ)
+  uint32_t b;     // B[row][lane] for lane < rb
+};
+
+// six vector loads in every form: two code runs, two scale codes (or absmax
+// values), the group scales (a second B load without double quantization),
+// B; the prologue's explicit wait counts on it
+constexpr int kRowLoads = 6;
+
+template <bool kDQ>
+__device__ __forceinline__ void load_row(RowLoads& L, const Rsrc& R, const GemvArgs& g, int row, int lane, int K,
+                                         int nbk) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int k0 = 2048 * h + 32 * lane;
+    const int off = k0 < K ? row * (K / 2) + (k0 >> 1) : R.codes_oob;
+    L.c[h] = __builtin_amdgcn_raw_buffer_load_b128(R.codes, off, 0, 0);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int blk = 32 * h + (lane >> 1);
+    if (kDQ) {
+      L.s[h] = __builtin_amdgcn_raw_buffer_load_b8(R.sc, blk < nbk ? row * nbk + blk : 0x7FFFFFF0, 0, 0);
+    } else {
+      L.s[h] = __builtin_amdgcn_raw_buffer_load_b32(R.am, blk < nbk ? 4 * (row * nbk + blk) : 0x7FFFFFF0, 0, 0);
+    }
+  }
+  if (kDQ) {
+    L.gs = __builtin_amdgcn_raw_buffer_load_b64(R.gs, 4 * ((row * nbk) >> 8), 0, 0);
+  } else {
+    L.gs = __builtin_amdgcn_raw_buffer_load_b64(R.b, R.b_oob, 0, 0);  // stand-in: same load count
+  }
+  L.b = __builtin_amdgcn_raw_buffer_load_b16(R.b, lane < g.rb ? 2 * (row * g.rb + lane) : R.b_oob, 0, 0);
+}
+
+template <bool kF16, bool kDQ, int kM, int kH, int kRPW>
+__global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvArgs g) {
+  static_assert(kM == 1 || kM == 2, "one or two tokens");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kRowsSmem];
+  unsigned char* tab = smem;
+  unsigned char* xst = smem + kTabBytes;
+  float* hl = reinterpret_cast<float*>(smem + kTabBytes + kRowsX);
+  float* scratch = reinterpret_cast<float*>(smem + kTabBytes + kRowsX + 4 * kRowsH);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  const int G = wave * 4 + g;  // this lane group's block of every row group
-  const int K = static_cast<int>(w.k), N = static_cast<int>(w.n);
-  const int nbk = K / 64;  // <= 64
-  const int nrg = (N + 15) / 16;
-  const bool kval = G < nbk;
-  const int kb_c = kval ? G : nbk - 1;
-  const int wv_u = __builtin_amdgcn_readfirstlane(wave);
-  const int blast = N * rb - 1;
-  const __amdgpu_buffer_rsrc_t xrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), static_cast<short>(0),
-                                                                        M * K * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a), static_cast<short>(0),
-                                                                        kFuseH ? rh * K * 2 : 0, 0x00020000);
-
-  struct Loads {
-    u32x4 c0, c1;
-    uint8_t scode;  // widened where it is used, so that nothing waits for it earlier
-    float gsc;
-    uint16_t bv[kBPer];
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
+  const int K = static_cast<int>(g.w.k), N = static_cast<int>(g.w.n);
+  const int nbk = K >> 6;
+  const int row0 = blockIdx.x * (kWaves * kRPW);
+  const int row_end = row0 + kWaves * kRPW < N ? row0 + kWaves * kRPW : N;
+  const Rsrc rs = make_rsrcs(g, nbk);
+  const int dq_mode = g.w.dq;
+  // row of step q (stand-ins past the end reload the last row)
+  auto row_of = [&](int q) {
+    const int r = row0 + wv + kWaves * q;
+    return r < N ? r : N - 1;
   };
-  // loads of row group rg < nrg; with real = false the same instructions on
-  // the first element of every array (one cache line each, results unused)
-  auto issue = [&](int rgc, Loads& T, bool real) {
-    const int n = rgc * 16 + i;
-    const int n_c = real ? (n < N ? n : N - 1) : 0;
-    const int kb_r = real ? kb_c : 0;
-    const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_r * 32));
-    T.c0 = __builtin_nontemporal_load(cp);
-    T.c1 = __builtin_nontemporal_load(cp + (real ? 1 : 0));
-    const int bi = n_c * nbk + kb_r;
-    if (kDQ) {
-      T.scode = w.scale_codes[bi];
-      T.gsc = w.group_scale[static_cast<uint32_t>(bi) / kGroup];
+
+  // X into LDS in the order of the lanes' weights: copy t = (tok, h, c)
+  // holds, for every lane l, the 8 values X[tok][2048 h + 32 l + 8 c ..], so
+  // each later fragment read is one contiguous 1 KB (no bank conflicts).
+  // One copy per wave (at most 2 tokens x 2 halves x 4).
+  const int nh = K > 2048 ? 2 : 1;
+  const int ncopy = kM * nh * 4;
+  if (wv < ncopy) {
+    const int tok = wv / (nh * 4), h = (wv >> 2) % nh, c = wv & 3;
+    const int kk = 2048 * h + 32 * lane + 8 * c;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.x, (lds_void*)(xst + wv * 1024), 16,
+                                             kk < K ? (tok * K + kk) * 2 : rs.x_oob, 0, 0, 0);
+  }
+  // the first rows' loads, so that HBM is busy while the table is built
+  // (two ahead with the fused H, whose A row and X fragments need registers
+  // while these rows are in flight; three otherwise)
+  constexpr int kAheadMax = kH == 1 ? 2 : 3;
+  constexpr int kAhead = kRPW < kAheadMax ? kRPW : kAheadMax;
+  RowLoads rl[kRPW];
+  static_for<0, kAhead>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    load_row<kDQ>(rl[q], rs, g, row_of(q), lane, K, nbk);
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  build_pair_table<kF16>(tab, g.L, tid, wv);
+  // this wave's X copy has landed (it was issued before the row loads: the
+  // compiler does not track global -> LDS copies, so the count is explicit)
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<kAhead * kRowLoads>();
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  // X staging offset of (tok, h, c) for lane l: ((tok nh + h) 4 + c) 1024 + 16 l
+  auto xoff = [&](int tok, int kk) {
+    const int h = kk >> 11, l = (kk & 2047) >> 5, c = (kk & 31) >> 3;
+    return ((tok * nh + h) * 4 + c) * 1024 + 16 * l;
+  };
+
+  // H's slots for this workgroup: [s0, s0 + ns); wave w takes slot s0 + w
+  // (and s0 + 16 + w when ns > 16)
+  int s0 = 0, ns = 0, hl0 = 0;
+  bool own_out = blockIdx.x == 0;
+  if (kH == 1) {
+    if (g.P.g > 1) {
+      const int l0 = part_of(g.P, row0), l1 = part_of(g.P, row_end - 1);
+      s0 = l0 * g.rb;
+      ns = (l1 - l0 + 1) * g.rb;
+      hl0 = l0;
     } else {
-      T.scode = 0;
-      T.gsc = w.absmax[bi];
+      ns = g.rh;
     }
-    // B rows: always kBPer loads (from X's first element when there is no
-    // B), so that every path issues the same number of loads per row group
+  }
+  // A row of slot j in whole 1 KB runs: lane l holds 8 values of every run
+  auto load_a = [&](u32x4 (&af)[8], int j) {
 #pragma unroll
-    for (int u = 0; u < kBPer; ++u) {
-      const int e = rgc * 16 * rb + tid + u * WAVES * 64;
-      const uint16_t* bp = (rb > 0 && real) ? b + (e < blast ? e : blast) : x;
-      T.bv[u] = *bp;
+    for (int q = 0; q < 8; ++q) {
+      const int off = q * 1024 + lane * 16;
+      af[q] = __builtin_amdgcn_raw_buffer_load_b128(rs.a, off < K * 2 ? j * K * 2 + off : rs.a_oob, 0, 0);
     }
   };
-  constexpr int kTaskLoads = 2 + (kDQ ? 2 : 1) + kBPer;  // per issue()
+  u32x4 af[8];
+  const bool has_slot = kH == 1 && wv < ns;
+  if (has_slot) load_a(af, s0 + wv);
 
-  // This wave's region and its copies: copy t moves rows 2t and 2t+1; lane l
-  // fetches piece (l & 31) ^ row of row 2t + (l >> 5) into slot l of the copy.
-  // Rows past the matrix (tokens >= M, ranks >= rh) read zeros; a wave whose
-  // slice starts past K copies nothing (its lane groups have no block).
-  unsigned char* region = stage + wv_u * kSlice;
-  const bool has_slice = wave * 4 < nbk;  // wave-uniform
-  const int crow = lane >> 5;
-  auto copy_slice = [&](__amdgpu_buffer_rsrc_t rsrc, int rows) {
-    const int ncopy = (rows + 1) >> 1;
+  HPart HP{};
+  if (kH == 2) HP = issue_hpart(g, rs, tid);
+
+  // H: dot of the A row with X read from LDS in the same order
+  auto h_slot = [&](int j) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      if (t < ncopy) {
-        const int row = 2 * t + crow;
-        const int goff = row * K * 2 + wv_u * 512 + 16 * ((lane & 31) ^ row);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(region + t * 1024), 16, goff, 0, 0, 0);
+    for (int tok = 0; tok < kM; ++tok) {
+      float p = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int kk = 512 * q + 8 * lane;
+        u32x4 xv = u32x4{0, 0, 0, 0};
+        if (kk < K) xv = *reinterpret_cast<const u32x4*>(xst + xoff(tok, kk));
+#pragma unroll
+        for (int d = 0; d < 4; ++d) p = dot2<kF16>(af[q][d], xv[d], p);
       }
-    }
-  };
-  // fragment j of lane (i, g): piece 8 g + j of row i
-  auto read_frag = [&](int j) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(region + i * 512 + 16 * ((8 * g + j) ^ i));
-  };
-
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 hacc = f32x4{0.f, 0.f, 0.f, 0.f};
-  Loads T0, T1;
-  const int rg0 = blockIdx.x;
-  // X slice first, then the first row group's loads; wait for the X copies
-  // only (every load issued after them may stay in flight)
-  __builtin_amdgcn_sched_barrier(0);
-  if (has_slice) copy_slice(xrsrc, M);
-  __builtin_amdgcn_sched_barrier(0);
-  issue(rg0, T0, true);
-  __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<kTaskLoads>();
-  __builtin_amdgcn_sched_barrier(0);
-  u32x4 xa[8];  // X fragments of this lane's block: the same for every row group
-#pragma unroll
-  for (int j = 0; j < 8; ++j) xa[j] = u32x4{0, 0, 0, 0};
-  if (kval && i < M) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) xa[j] = read_frag(j);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) xa[j] = decode_order(xa[j]);
-  if (kFuseH) {
-    // the region's X has been read into registers: A's slice replaces it
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the fragment reads are done
-    if (has_slice) copy_slice(arsrc, rh);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (!kFuseH && rh > 0) {
-    // H = sum of the LoRA-down partials (fixed order)
-    const int mr = M * rh;
-    for (int idx = tid; idx < mr; idx += WAVES * 64) {
-      float hv = 0.0f;
-#pragma unroll 8
-      for (int sp = 0; sp < hsplits; ++sp) hv += hpart[sp * mr + idx];  // loads in flight together, sums in order
-      h_lds[idx] = hv;
-      if (h_out != nullptr && blockIdx.x == 0) h_out[idx] = hv;
-    }
-  }
-
-  auto step = [&](int rg, Loads& Tc, Loads& Tn) {
-    const bool has_next = rg + static_cast<int>(gridDim.x) < nrg;  // uniform
-    // the next row group's loads, or after the last one the same number of
-    // stand-in loads: the waits below count the same on every path
-    issue(rg + static_cast<int>(gridDim.x), Tn, has_next);
-    // wave-uniform guard; lane groups past the row's blocks get a zero scale
-    if (wave * 4 < nbk) {
-      const int n = rg * 16 + i;
-      const bool ok = (n < N) && kval;
-      const float sc = kDQ ? dq_unit(Tc.scode, w.dq) * Tc.gsc : Tc.gsc;
-      const BlockLut lut = make_block_lut<kF16>(L.v, ok ? sc : 0.0f);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t cw = (j < 4) ? Tc.c0[j] : Tc.c1[j - 4];
-        uint32_t wv[4];
-        lut8_decode_order(lut, cw, wv);
-        acc = mma16<kF16>(xa[j], u32x4{wv[0], wv[1], wv[2], wv[3]}, acc);
-      }
-    }
-    const bool first = rg == rg0;
-    if (kFuseH && first) {
-      // H product, once: wait for this wave's copies of A (everything issued
-      // after them is the next row group's loads); only this wave reads them
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<kTaskLoads>();
-      __builtin_amdgcn_sched_barrier(0);
-      if (has_slice) {
-        u32x4 af[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) af[j] = u32x4{0, 0, 0, 0};
-        if (kval && i < rh) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) af[j] = read_frag(j);
+      p = wave_sum(p);
+      if (lane == 0) {
+        hl[tok * 32 + (j - s0)] = p;
+        if (g.h_out != nullptr) {
+          // single linear: the first workgroup writes H; grouped: the
+          // workgroup that holds the part's first row
+          bool own = own_out;
+          if (g.P.g > 1) {
+            const int l = j / g.rb, pb = part_begin(g.P, l);
+            own = pb >= row0 && pb < row_end;
+          }
+          if (own) g.h_out[tok * g.rh + j] = p;
         }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hacc = mma16<kF16>(xa[j], decode_order(af[j]), hacc);
       }
     }
-    // epilogue of row group rg
-    __syncthreads();  // LDS free: the previous epilogue's reads (and the A slice's) are done
-    red[wave][lane] = acc;
-    if (kFuseH && first) hred[wave][lane] = hacc;
-#pragma unroll
-    for (int u = 0; u < kBPer; ++u) {
-      const int idx = tid + u * WAVES * 64;
-      if (idx < 16 * rb) b_lds[idx] = Tc.bv[u];
+  };
+  if (has_slot) {
+    h_slot(s0 + wv);
+    if (wv + kWaves < ns) {
+      load_a(af, s0 + kWaves + wv);
+      h_slot(s0 + kWaves + wv);
+    }
+  }
+  if (kH == 2) put_hpart(g, scratch, HP, tid);
+  __syncthreads();
+  if (kH == 2) {
+    // H from the split partial sums into hl[tok * rh + j]
+    const int mr = g.M * g.rh;
+    for (int idx = tid; idx < mr; idx += kThreads) {
+      float hv = 0.0f;
+      if (HP.fast) {
+        for (int grp = 0; grp < HP.groups; ++grp) hv += scratch[grp * mr + idx];
+      } else {
+#pragma unroll 8
+        for (int sp = 0; sp < g.hsplits; ++sp) hv += g.hpart[sp * mr + idx];
+      }
+      hl[idx] = hv;
+      if (g.h_out != nullptr && blockIdx.x == 0) g.h_out[idx] = hv;
     }
     __syncthreads();
-    const int l2 = tid & 63, v = tid >> 6;
-    const int mo = 4 * (l2 >> 4) + v;
-    if (kFuseH && first) {
-      if (tid < 256) {
-        const int j = l2 & 15;
-        float hv = 0.0f;
+  }
+
+  // X in registers, in the order of the lane's weights (zeros past K)
+  u32x4 xr[kM][2][4];
 #pragma unroll
-        for (int wv = 0; wv < WAVES; ++wv) hv += hredf[(wv * 64 + l2) * 4 + v];
-        if (mo < M && j < rh) {
-          h_lds[mo * rh + j] = hv;
-          if (h_out != nullptr && blockIdx.x == 0) h_out[mo * rh + j] = hv;
+  for (int tok = 0; tok < kM; ++tok)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        xr[tok][h][c] = h < nh ? *reinterpret_cast<const u32x4*>(xst + ((tok * nh + h) * 4 + c) * 1024 + 16 * lane)
+                               : u32x4{0, 0, 0, 0};
+  const int hstride = kH == 1 ? 32 : g.rh;
+
+  static_for<0, kRPW>([&](auto qc) {
+    constexpr int q = decltype(qc)::value;
+    if constexpr (q >= 1 && q + kAhead - 1 < kRPW) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_row<kDQ>(rl[q + kAhead - 1], rs, g, row_of(q + kAhead - 1), lane, K, nbk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int row = row0 + wv + kWaves * q;
+    if (row < N) {
+      const RowLoads& L = rl[q];
+      float acc[kM];
+#pragma unroll
+      for (int tok = 0; tok < kM; ++tok) acc[tok] = 0.0f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h < nh) {
+          float p[kM];
+#pragma unroll
+          for (int tok = 0; tok < kM; ++tok) p[tok] = 0.0f;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            const u32x4 wv4 = lookup8(tab, L.c[h][d], lane4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int tok = 0; tok < kM; ++tok) p[tok] = dot2<kF16>(wv4[e], xr[tok][h][d][e], p[tok]);
+          }
+          const int blk = 32 * h + (lane >> 1);
+          float sc;
+          if (kDQ) {
+            const int grp = (row * nbk + blk) >> 8;
+            const float gsv = __builtin_bit_cast(float, grp == ((row * nbk) >> 8) ? L.gs[0] : L.gs[1]);
+            sc = dq_unit(L.s[h] & 0xFFu, dq_mode) * gsv;
+          } else {
+            sc = __builtin_bit_cast(float, L.s[h]);
+          }
+          sc = blk < nbk ? sc : 0.0f;
+#pragma unroll
+          for (int tok = 0; tok < kM; ++tok) acc[tok] = fmaf(sc, p[tok], acc[tok]);
         }
       }
-      __syncthreads();
-    }
-    const int no = rg * 16 + (l2 & 15);
-    if (tid < 256 && mo < M && no < N) {
-      float sum = 0.0f;
+      if (kH != 0 && lane < g.rb) {
+        // lane j's share of s H B^T: the slot of this row's part
+        int off;
+        if (kH == 1) {
+          off = g.P.g > 1 ? (part_of(g.P, row) - hl0) * g.rb : 0;
+        } else {
+          off = g.P.g > 1 ? part_of(g.P, row) * g.rb : 0;
+        }
+        const float bj = to_f32<kF16>(static_cast<uint16_t>(L.b));
 #pragma unroll
-      for (int wv = 0; wv < WAVES; ++wv) sum += redf[(wv * 64 + l2) * 4 + v];
-      if (rb > 0) {
-        float lo = 0.0f;
-        const uint16_t* brow = b_lds + (l2 & 15) * rb;
-        const float* hrow = h_lds + mo * rh + part_slot0(P, no, rb);
-        for (int j = 0; j < rb; ++j) lo = fmaf(hrow[j], to_f32<kF16>(brow[j]), lo);
-        sum = fmaf(s, lo, sum);
+        for (int tok = 0; tok < kM; ++tok) acc[tok] = fmaf(g.s * hl[tok * hstride + off + lane], bj, acc[tok]);
       }
-      y[mo * N + no] = to16<kF16>(sum);
+#pragma unroll
+      for (int tok = 0; tok < kM; ++tok) {
+        const float v = wave_sum(acc[tok]);
+        if (lane == 0) g.y[static_cast<int64_t>(tok) * N + row] = to16<kF16>(v);
+      }
     }
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  };
-  for (int rg = rg0; rg < nrg; rg += 2 * gridDim.x) {
-    step(rg, T0, T1);
-    if (rg + gridDim.x < nrg) step(rg + gridDim.x, T1, T0);
-  }
+  });
 }
 
 }  // namespace
-
-bool gemv_fuses_h(int64_t k, int r) {
-  (void)k;
-  return r > 0 && r <= 16;
-}
 
 int device_cus() {
   static int cus[64] = {0};
@@ -515,28 +481,53 @@ int device_cus() {
   return cus[dev];
 }
 
+bool gemv_fuses_h(int64_t m, int64_t k, int r, const LoraParts* parts) {
+  if (r <= 0) return false;
+  // 3 to 16 tokens, or k > 4096 (the matrix-core kernels of gemv_mfma.hip):
+  // up to 16 slots
+  if (m > 2 || k > 4096) return r <= 16;
+  const bool grouped = parts != nullptr && parts->g > 1;
+  return grouped ? parts->rpart <= 16 : r <= 32;
+}
+
 namespace {
 
-template <bool kF16>
-hipError_t launch_gemv_t(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
-                         int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
-                         const LoraParts& P) {
-  constexpr int kWaves = 16;
-  const int64_t nrg = (w.n + 15) / 16;
-  const bool fuse = gemv_fuses_h(w.k, r);
-  const int rb = P.g > 1 ? P.rpart : r;
-  if (w.k <= 4096) {
-    const unsigned grid = static_cast<unsigned>(nrg < device_cus() ? nrg : device_cus());
-    auto kern = w.dq ? (fuse ? gemv_persistent_kernel<true, true, kF16> : gemv_persistent_kernel<true, false, kF16>)
-                     : (fuse ? gemv_persistent_kernel<false, true, kF16> : gemv_persistent_kernel<false, false, kF16>);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a, hpart, hsplits, b,
-                       r, rb, P, s, y, h_out, codebook_table(w.codebook));
-    return hipGetLastError();
+template <bool kF16, bool kDQ, int kM, int kRPW>
+void launch_rows_rpw(const GemvArgs& g, int kh, hipStream_t st) {
+  const unsigned grid = static_cast<unsigned>((g.w.n + kWaves * kRPW - 1) / (kWaves * kRPW));
+  auto kern = kh == 0   ? gemv_rows_kernel<kF16, kDQ, kM, 0, kRPW>
+              : kh == 1 ? gemv_rows_kernel<kF16, kDQ, kM, 1, kRPW>
+                        : gemv_rows_kernel<kF16, kDQ, kM, 2, kRPW>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, st, g);
+}
+
+// rows per wave for the one-wave-per-row form: enough waves for one
+// workgroup per CU
+template <bool kF16, bool kDQ, int kM>
+void launch_rows(const GemvArgs& g, int kh, hipStream_t st) {
+  const int64_t per = (g.w.n + int64_t(kWaves) * device_cus() - 1) / (int64_t(kWaves) * device_cus());
+  if (per <= 1) {
+    launch_rows_rpw<kF16, kDQ, kM, 1>(g, kh, st);
+  } else if (per <= 2) {
+    launch_rows_rpw<kF16, kDQ, kM, 2>(g, kh, st);
+  } else if (per <= 3) {
+    launch_rows_rpw<kF16, kDQ, kM, 3>(g, kh, st);
+  } else if (per <= 4) {
+    launch_rows_rpw<kF16, kDQ, kM, 4>(g, kh, st);
+  } else if (per <= 6) {
+    launch_rows_rpw<kF16, kDQ, kM, 6>(g, kh, st);
+  } else {
+    launch_rows_rpw<kF16, kDQ, kM, 8>(g, kh, st);
   }
-  auto kern = w.dq ? (fuse ? gemv_kernel<kWaves, true, true, kF16> : gemv_kernel<kWaves, true, false, kF16>)
-                   : (fuse ? gemv_kernel<kWaves, false, true, kF16> : gemv_kernel<kWaves, false, false, kF16>);
-  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(nrg)), dim3(kWaves * 64), 0, st, w, x, static_cast<int>(m), a,
-                     hpart, hsplits, b, r, rb, P, s, y, h_out, codebook_table(w.codebook));
+}
+
+template <bool kF16, bool kDQ>
+hipError_t launch_gemv_dq(const GemvArgs& g, int kh, hipStream_t st) {
+  if (g.M == 1) {
+    launch_rows<kF16, kDQ, 1>(g, kh, st);
+  } else {
+    launch_rows<kF16, kDQ, 2>(g, kh, st);
+  }
   return hipGetLastError();
 }
 
@@ -545,13 +536,36 @@ hipError_t launch_gemv_t(const PackedW& w, const uint16_t* x, int64_t m, const u
 hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
                        int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
                        bool f16, const LoraParts* parts) {
-  LoraParts one;
-  one.g = 1;
-  one.rpart = r;
-  one.end[0] = static_cast<int>(w.n);
-  const LoraParts& P = parts != nullptr ? *parts : one;
-  return f16 ? launch_gemv_t<true>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st, P)
-             : launch_gemv_t<false>(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st, P);
+  if (m < 1 || m > 16 || w.n % 16 != 0 || w.k % 64 != 0 || r < 0 || r > QLORA_MAX_RANK) return hipErrorInvalidValue;
+  if (m > 2 || w.k > 4096) return launch_gemv_mfma(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st, f16, parts);
+  GemvArgs g;
+  g.w = w;
+  g.x = x;
+  g.M = static_cast<int>(m);
+  g.a = a;
+  g.rh = r;
+  g.hpart = hpart;
+  g.hsplits = hsplits;
+  g.b = b;
+  if (parts != nullptr && parts->g > 1) {
+    g.P = *parts;
+    g.rb = parts->rpart;
+  } else {
+    g.P = LoraParts{};
+    g.P.g = 1;
+    g.P.rpart = r;
+    g.P.end[0] = static_cast<int>(w.n);
+    g.rb = r;
+  }
+  g.s = s;
+  g.y = y;
+  g.h_out = h_out;
+  g.L = codebook_table(w.codebook);
+  const bool fuse = gemv_fuses_h(m, w.k, r, parts);
+  if (r > 0 && !fuse && hpart == nullptr) return hipErrorInvalidValue;
+  const int kh = r == 0 ? 0 : (fuse ? 1 : 2);
+  if (f16) return w.dq ? launch_gemv_dq<true, true>(g, kh, st) : launch_gemv_dq<true, false>(g, kh, st);
+  return w.dq ? launch_gemv_dq<false, true>(g, kh, st) : launch_gemv_dq<false, false>(g, kh, st);
 }
 
 }  // namespace qlora

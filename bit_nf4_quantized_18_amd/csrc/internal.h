@@ -84,15 +84,24 @@ struct LoraParts {
 };
 
 // Decode GEMV, m <= 16: y = x W16^T + s * h B^T in one launch when
-// gemv_fuses_h(k, r) (H = x A^T computed in the kernel from a); otherwise
-// hpart holds hsplits partial sums of H (hsplits x m x r float32, from
-// launch_skinny). r = 0: base only. h_out (m x r, may be null) receives H.
-// Grouped weights (parts != null): r = g rpart slots of H (a is r x k), b is
-// n x rpart and row p of part l takes H's slots l rpart .. (l+1) rpart - 1.
-bool gemv_fuses_h(int64_t k, int r);
+// gemv_fuses_h(n, k, r, parts) (H = x A^T computed in the kernel from a);
+// otherwise hpart holds hsplits partial sums of H (hsplits x m x r float32,
+// from launch_skinny_decode). r = 0: base only. h_out (m x r, may be null)
+// receives H. Grouped weights (parts != null): r = g rpart slots of H (a is
+// r x k), b is n x rpart and row p of part l takes H's slots l rpart ..
+// (l+1) rpart - 1. H is fused for 3..16 tokens or k > 4096 when r <= 16;
+// for one or two tokens at k <= 4096 when r <= 32 (one part) or rpart <= 16
+// (grouped).
+// A call with parts fuses whenever the same call without them would.
+bool gemv_fuses_h(int64_t m, int64_t k, int r, const LoraParts* parts);
+int device_cus();
 hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
                        int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
                        bool f16 = false, const LoraParts* parts = nullptr);
+// The matrix-core form (3..16 tokens, or k > 4096); same arguments as launch_gemv.
+hipError_t launch_gemv_mfma(const PackedW& w, const uint16_t* x, int64_t m, const uint16_t* a, const float* hpart,
+                            int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
+                            bool f16, const LoraParts* parts);
 
 // Fused dequant-GEMM, forward: y = x W16^T + the LoRA term where hs is bf16
 // m x rpad (already scaled by s) and b is n x r bf16 (r = slots per part);

@@ -99,7 +99,8 @@ class Workload:
 
 
 SMALL = Workload("single_256x256_m16_r8", (Linear("single", 256, 256),), 16, 8, 16.0, "normal")
-DECODE_7B = Workload("decode_7b_4096x4096_11008x4096", (Linear("attn", 4096, 4096), Linear("mlp_up", 11008, 4096)),
+DECODE_7B = Workload("decode_7b_4096x4096_11008x4096", (Linear("attn", 4096, 4096), Linear("mlp_up", 11008, 4096),
+                                                       Linear("mlp_down", 4096, 11008)),
                      1, 16, 32.0, "normal_outliers")
 LAYERS_7B = Workload("llama7b_layer_set_m2048_r16", layer_set(4096, 11008), 2048, 16, 32.0, "normal")
 LAYERS_65B = Workload("llama65b_layer_set_m4096_r64", layer_set(8192, 22016), 4096, 64, 16.0, "student_t")
