@@ -29,7 +29,9 @@ FWD_BWD_CASES = [
     ("decode_rank5_m2", 2, 96, 192, 5, 10.0, True),              # H inside the GEMV, ragged rank
     ("decode_k8192_r4_m5", 5, 48, 8192, 4, 8.0, True),           # H inside the GEMV, two passes over k
     ("decode_rank24_m8", 8, 128, 256, 24, 48.0, True),           # r > 16: H from the skinny kernel
-    ("decode_long_k_m2", 2, 64, 16384, 16, 32.0, True),          # r * k > 2^17: H from the skinny kernel
+    ("decode_long_k_m2", 2, 64, 16384, 16, 32.0, True),          # k > 4096 at two tokens: H from the skinny kernel
+    ("decode_rank32_m1", 1, 160, 4096, 32, 64.0, True),          # one token, two fused H tiles, full k
+    ("decode_rank20_m2_k2112", 2, 48, 2112, 20, 40.0, True),     # two tokens, ragged k past one 2048 half
 ]
 
 
@@ -122,14 +124,17 @@ def test_7b_layer_full(gpu_lib, n, k):
     _run_case(gpu_lib, f"layer7b_{n}x{k}", 2048, n, k, 16, 32.0, True)
 
 
-def test_65b_layer_sampled(gpu_lib):
-    """65B-shaped gate/up projection (22016 x 8192, r = 64, alpha = 16,
-    Student-t weights, 4096 tokens): dA and dB checked in full, Y and dX on
-    64 sampled token rows."""
+@pytest.mark.parametrize("proj,n,k", [("q", 8192, 8192), ("down", 8192, 22016), ("gate", 22016, 8192)],
+                         ids=["q_k_v_o_8192x8192", "down_8192x22016", "gate_up_22016x8192"])
+def test_65b_layer_sampled(gpu_lib, proj, n, k):
+    """The 65B-shaped layer set at its training size (4096 tokens, r = 64,
+    alpha = 16, Student-t(4) weights scaled by 0.02): the 8192 x 8192 shape of
+    q/k/v/o, down (8192 x 22016: the longest k) and gate/up (22016 x 8192).
+    dA and dB are checked in full, Y and dX on 64 sampled token rows."""
     import torch
 
-    m, n, k, r, alpha = 4096, 22016, 8192, 64, 16.0
-    tag = "layer65b_gate"
+    m, r, alpha = 4096, 64, 16.0
+    tag = f"layer65b_{proj}"
     w = synth.student_t((n, k), 4, 0.02, tag, "W")
     from gpu_cases import to_bf16
     x = to_bf16(synth.normal((m, k), 1.0, tag, "X"))
