@@ -151,6 +151,72 @@ def _check(status: int, where: str):
         raise QloraError(status, where)
 
 
+def _need(t, name, shape, dtypes, device, optional=False):
+    """Raise unless ``t`` is a contiguous tensor of one of ``dtypes`` on
+    ``device`` with exactly ``shape`` (None allowed only when ``optional``).
+    The library takes raw pointers and sizes, so a tensor that does not match
+    what the call assumes is refused here rather than read out of bounds."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the weight on {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_packed(q):
+    """The packed weight's buffers: uint8 codes / scale codes, float32 group
+    scales / absmax, contiguous, on one device, at least as long as n x k needs."""
+    import torch
+
+    dev = q.codes.device
+    numel = q.n * q.k
+    nb = -(-numel // BLOCK)
+    ng = -(-nb // DQ_GROUP)
+    for name, t, dt, need in (("codes", q.codes, torch.uint8, (numel + 1) // 2),
+                              ("scale_codes", q.scale_codes, torch.uint8, nb if q.double_quant else 0),
+                              ("group_scale", q.group_scale, torch.float32, ng if q.double_quant else 0),
+                              ("absmax", q.absmax, torch.float32, 0 if q.double_quant else nb)):
+        if t is None:
+            if need:
+                raise ValueError(f"packed weight: {name} is required")
+            continue
+        if t.device != dev or t.dtype != dt or not t.is_contiguous() or t.numel() < need:
+            raise ValueError(f"packed weight: {name} must be a contiguous {dt} tensor on {dev} "
+                             f"with at least {need} elements")
+    return dev
+
+
+def _half_types(t, name):
+    import torch
+
+    if t.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
+    return (t.dtype,)
+
+
+def _need_ws(ws, device):
+    import torch
+
+    if ws is not None and (ws.device != device or ws.dtype != torch.uint8 or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous uint8 tensor on the weight's device")
+
+
+def _need_adapter(a, b, r, k, n, types, device, rb=None):
+    if (a is None) != (b is None):
+        raise ValueError("a and b are given together or not at all")
+    if a is None:
+        return
+    _need(a, "a", (r, k), types, device)
+    _need(b, "b", (n, r if rb is None else rb), types, device)
+
+
 @dataclasses.dataclass
 class PackedNF4:
     """A packed NF4 weight on the device (n x k row-major)."""
@@ -213,16 +279,20 @@ def dequantize(q: PackedNF4, dtype=None):
 
     dtype = torch.bfloat16 if dtype is None else dtype
     code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32, torch.float16: QLORA_F16}[dtype]
-    out = torch.empty((q.n, q.k), dtype=dtype, device=q.codes.device)
+    dev = _need_packed(q)
+    out = torch.empty((q.n, q.k), dtype=dtype, device=dev)
     ws = q.c_struct()
     _check(load().qlora_nf4_dequantize(ctypes.byref(ws), code, _ptr(out), _stream()), "qlora_nf4_dequantize")
     return out
 
 
-def _adapter(a, b):
-    if a is None:
-        return 0, None, None
-    return a.shape[0], _ptr(a.contiguous()), _ptr(b.contiguous())
+def _adapter(a, b, n, k, device):
+    """(r, a pointer, b pointer) of a bf16 adapter a (r, k), b (n, r), or none."""
+    import torch
+
+    r = 0 if a is None else a.shape[0]
+    _need_adapter(a, b, r, k, n, (torch.bfloat16,), device)
+    return r, _ptr(a), _ptr(b)
 
 
 def merge(q: PackedNF4, a, b, alpha: float, dtype=None, out=None):
@@ -232,8 +302,10 @@ def merge(q: PackedNF4, a, b, alpha: float, dtype=None, out=None):
 
     dtype = torch.bfloat16 if dtype is None else dtype
     code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32}[dtype]
-    out = torch.empty((q.n, q.k), dtype=dtype, device=q.codes.device) if out is None else out
-    r, ap, bp = _adapter(a, b)
+    dev = _need_packed(q)
+    out = torch.empty((q.n, q.k), dtype=dtype, device=dev) if out is None else out
+    _need(out, "out", (q.n, q.k), (dtype,), dev)
+    r, ap, bp = _adapter(a, b, q.n, q.k, dev)
     ws = q.c_struct()
     _check(load().qlora_merge(ctypes.byref(ws), ap, bp, r, float(alpha), code, _ptr(out), _stream()), "qlora_merge")
     return out
@@ -245,9 +317,13 @@ def unmerge(merged, a, b, alpha: float, out=None):
     import torch
 
     code = {torch.bfloat16: QLORA_BF16, torch.float32: QLORA_F32}[merged.dtype]
-    merged = merged.contiguous()
+    if merged.dim() != 2:
+        raise ValueError("merged must be 2-D (n, k)")
+    dev = merged.device
+    _need(merged, "merged", tuple(merged.shape), (merged.dtype,), dev)
     out = torch.empty_like(merged) if out is None else out
-    r, ap, bp = _adapter(a, b)
+    _need(out, "out", tuple(merged.shape), (merged.dtype,), dev)
+    r, ap, bp = _adapter(a, b, merged.shape[0], merged.shape[1], dev)
     _check(load().qlora_unmerge(_ptr(merged), code, merged.shape[0], merged.shape[1], ap, bp, r, float(alpha),
                                 _ptr(out), _stream()), "qlora_unmerge")
     return out
@@ -259,7 +335,7 @@ def requantize(q: PackedNF4, a, b, alpha: float, double_quant: bool = True, code
     (PackedNF4 of the merged weight, merged float32 (n, k))."""
     import torch
 
-    dev = q.codes.device
+    dev = _need_packed(q)
     numel = q.n * q.k
     nb = -(-numel // BLOCK)
     ng = -(-nb // DQ_GROUP)
@@ -268,7 +344,7 @@ def requantize(q: PackedNF4, a, b, alpha: float, double_quant: bool = True, code
     sc = _empty(nb, torch.uint8, dev) if double_quant else None
     gs = _empty(ng, torch.float32, dev) if double_quant else None
     am = _empty(nb, torch.float32, dev) if (keep_absmax or not double_quant) else None
-    r, ap, bp = _adapter(a, b)
+    r, ap, bp = _adapter(a, b, q.n, q.k, dev)
     ws = q.c_struct()
     _check(load().qlora_requantize(ctypes.byref(ws), ap, bp, r, float(alpha), int(double_quant), int(codebook),
                                    _ptr(merged), _ptr(codes), _ptr(sc), _ptr(gs), _ptr(am), _stream()),
@@ -292,13 +368,19 @@ def linear_fwd(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, want_h: bool
     ``out``, ``h_out`` and ``ws`` (uint8 workspace) may be preallocated."""
     import torch
 
+    dev = _need_packed(q)
     m = x.shape[0]
     r = 0 if a is None else a.shape[0]
-    dev = x.device
+    t16 = _half_types(x, "x")
     f16 = x.dtype == torch.float16  # fp16 compute: the _f16 entry point
+    _need(x, "x", (m, q.k), t16, dev)
+    _need_adapter(a, b, r, q.k, q.n, t16, dev)
     y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=dev)
     h = h_out if h_out is not None else (
         torch.empty((m, r), dtype=torch.float32, device=dev) if (want_h and r > 0) else None)
+    _need(y, "out", (m, q.n), t16, dev)
+    _need(h, "h_out", (m, r), (torch.float32,), dev, optional=True)
+    _need_ws(ws, dev)
     if ws is None:
         ws, nbytes = _workspace(m, q.n, q.k, r, dev)
     else:
@@ -317,9 +399,14 @@ def linear_fwd_noalloc(q: PackedNF4, x, a=None, b=None, alpha: float = 0.0, out=
     (m, r)) may be preallocated; h is returned only when ``h_out`` is given."""
     import torch
 
+    dev = _need_packed(q)
     m = x.shape[0]
     r = 0 if a is None else a.shape[0]
-    y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=x.device)
+    _need(x, "x", (m, q.k), (torch.bfloat16,), dev)
+    _need_adapter(a, b, r, q.k, q.n, (torch.bfloat16,), dev)
+    y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=dev)
+    _need(y, "out", (m, q.n), (torch.bfloat16,), dev)
+    _need(h_out, "h_out", (m, r), (torch.float32,), dev, optional=True)
     wc = q.c_struct()
     st = load().qlora_linear_fwd_noalloc(ctypes.byref(wc), _ptr(x), m, _ptr(a), _ptr(b), r, float(alpha), _ptr(y),
                                          _ptr(h_out), _stream())
@@ -334,16 +421,25 @@ def linear_bwd(q: PackedNF4, x, dy, a=None, b=None, alpha: float = 0.0, h=None, 
     workspace may be preallocated."""
     import torch
 
+    dev = _need_packed(q)
     m = dy.shape[0]
     r = 0 if a is None else a.shape[0]
-    dev = dy.device
+    t16 = _half_types(dy, "dy")
     f16 = dy.dtype == torch.float16
+    _need(dy, "dy", (m, q.n), t16, dev)
+    _need(x, "x", (m, q.k), t16, dev, optional=r == 0)
+    _need_adapter(a, b, r, q.k, q.n, t16, dev)
+    _need(h, "h", (m, r), (torch.float32,), dev, optional=True)
     if dx is None and need_dx:
         dx = torch.empty((m, q.k), dtype=dy.dtype, device=dev)
     if r and da is None:
         da = torch.empty((r, q.k), dtype=torch.float32, device=dev)
     if r and db is None:
         db = torch.empty((q.n, r), dtype=torch.float32, device=dev)
+    _need(dx, "dx", (m, q.k), t16, dev, optional=True)
+    _need(da, "da", (r, q.k), (torch.float32,), dev, optional=r == 0)
+    _need(db, "db", (q.n, r), (torch.float32,), dev, optional=r == 0)
+    _need_ws(ws, dev)
     if ws is None:
         ws, nbytes = _workspace(m, q.n, q.k, r, dev)
     else:
@@ -386,9 +482,17 @@ def linear_fwd_dropout(q: PackedNF4, x, a, b, alpha: float, keep, p: float, want
     kept; p: drop probability. Returns (y, h) with h from the dropped input."""
     import torch
 
-    m, r, dev = x.shape[0], a.shape[0], x.device
+    dev = _need_packed(q)
+    m, r = x.shape[0], a.shape[0]
+    t16 = _half_types(x, "x")
+    _need(x, "x", (m, q.k), t16, dev)
+    _need_adapter(a, b, r, q.k, q.n, t16, dev)
+    _need(keep, "keep", (m, q.k), (torch.uint8,), dev)
     y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=dev)
     h = h_out if h_out is not None else (torch.empty((m, r), dtype=torch.float32, device=dev) if want_h else None)
+    _need(y, "out", (m, q.n), t16, dev)
+    _need(h, "h_out", (m, r), (torch.float32,), dev, optional=True)
+    _need_ws(ws, dev)
     ws, nbytes = _drop_ws(ws, m, q.n, q.k, r, dev)
     wc = q.c_struct()
     fn = load().qlora_linear_fwd_dropout_f16 if x.dtype == torch.float16 else load().qlora_linear_fwd_dropout
@@ -403,11 +507,22 @@ def linear_bwd_dropout(q: PackedNF4, x, dy, a, b, alpha: float, keep, p: float, 
     """qlora_linear_bwd_dropout with the forward's mask. Returns (dx, dA, dB)."""
     import torch
 
-    m, r, dev = dy.shape[0], a.shape[0], dy.device
+    dev = _need_packed(q)
+    m, r = dy.shape[0], a.shape[0]
+    t16 = _half_types(dy, "dy")
+    _need(dy, "dy", (m, q.n), t16, dev)
+    _need(x, "x", (m, q.k), t16, dev)
+    _need_adapter(a, b, r, q.k, q.n, t16, dev)
+    _need(keep, "keep", (m, q.k), (torch.uint8,), dev)
+    _need(h, "h", (m, r), (torch.float32,), dev, optional=True)
     if dx is None and need_dx:
         dx = torch.empty((m, q.k), dtype=dy.dtype, device=dev)
     da = torch.empty((r, q.k), dtype=torch.float32, device=dev) if da is None else da
     db = torch.empty((q.n, r), dtype=torch.float32, device=dev) if db is None else db
+    _need(dx, "dx", (m, q.k), t16, dev, optional=True)
+    _need(da, "da", (r, q.k), (torch.float32,), dev)
+    _need(db, "db", (q.n, r), (torch.float32,), dev)
+    _need_ws(ws, dev)
     ws, nbytes = _drop_ws(ws, m, q.n, q.k, r, dev)
     wc = q.c_struct()
     fn = load().qlora_linear_bwd_dropout_f16 if dy.dtype == torch.float16 else load().qlora_linear_bwd_dropout
@@ -434,10 +549,16 @@ def linear_fwd_grouped(q: PackedNF4, parts, x, a, b, alpha: float, want_h: bool 
     stacked (g r, k) A, b the stacked (n, r) B. Returns (y, h (m, g r))."""
     import torch
 
+    dev = _need_packed(q)
     m, g, r = x.shape[0], len(parts), b.shape[1]
-    dev = x.device
+    t16 = _half_types(x, "x")
+    _need(x, "x", (m, q.k), t16, dev)
+    _need_adapter(a, b, g * r, q.k, q.n, t16, dev, rb=r)
     y = out if out is not None else torch.empty((m, q.n), dtype=x.dtype, device=dev)
     h = h_out if h_out is not None else (torch.empty((m, g * r), dtype=torch.float32, device=dev) if want_h else None)
+    _need(y, "out", (m, q.n), t16, dev)
+    _need(h, "h_out", (m, g * r), (torch.float32,), dev, optional=True)
+    _need_ws(ws, dev)
     if ws is None:
         nbytes = grouped_workspace_bytes(m, q.n, q.k, g, r)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
@@ -457,14 +578,23 @@ def linear_bwd_grouped(q: PackedNF4, parts, x, dy, a, b, alpha: float, h=None, n
     dB stacked (n, r))."""
     import torch
 
+    dev = _need_packed(q)
     m, g, r = dy.shape[0], len(parts), b.shape[1]
-    dev = dy.device
+    t16 = _half_types(dy, "dy")
+    _need(dy, "dy", (m, q.n), t16, dev)
+    _need(x, "x", (m, q.k), t16, dev)
+    _need_adapter(a, b, g * r, q.k, q.n, t16, dev, rb=r)
+    _need(h, "h", (m, g * r), (torch.float32,), dev, optional=True)
     if dx is None and need_dx:
         dx = torch.empty((m, q.k), dtype=dy.dtype, device=dev)
     if da is None:
         da = torch.empty((g * r, q.k), dtype=torch.float32, device=dev)
     if db is None:
         db = torch.empty((q.n, r), dtype=torch.float32, device=dev)
+    _need(dx, "dx", (m, q.k), t16, dev, optional=True)
+    _need(da, "da", (g * r, q.k), (torch.float32,), dev)
+    _need(db, "db", (q.n, r), (torch.float32,), dev)
+    _need_ws(ws, dev)
     if ws is None:
         nbytes = grouped_workspace_bytes(m, q.n, q.k, g, r)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
