@@ -64,22 +64,30 @@ ZERO_CODE = 7                    # index of the exact-zero level
 def nf4_levels(inv_cdf=None) -> np.ndarray:
     """16 NF4 levels, ascending, float32 [U].
 
-    Positive side: the standard-normal quantiles at 8 probabilities evenly
-    spaced from the offset down to 0.5 (0.5 itself excluded). Negative side:
-    minus the quantiles at 7 such probabilities. Add an exact 0, sort, divide
-    by the largest level so the table spans [-1, 1].
+    With Phi^-1 the standard-normal quantile function and o the quantile
+    offset, the levels are, before normalisation,
+        Phi^-1(p)  for p = o - i (o - 1/2) / 8,  i = 0 .. 7   (8 positive),
+        0                                                      (exact zero),
+        -Phi^-1(p) for p = o - j (o - 1/2) / 7,  j = 0 .. 6   (7 negative),
+    i.e. probabilities evenly spaced from o towards 1/2 with 1/2 itself left
+    out on each side (its quantile is the zero level). All 16 are divided by
+    the largest, Phi^-1(o), so the table spans [-1, 1] with 1 at the top;
+    the values are formed in float64 and rounded once to float32.
     ``inv_cdf`` is the float64 standard-normal quantile function; by default
     Python's ``statistics.NormalDist().inv_cdf``.
     """
     if inv_cdf is None:
         inv_cdf = statistics.NormalDist(0.0, 1.0).inv_cdf
     o = NF4_QUANTILE_OFFSET
-    pos_p = np.linspace(o, 0.5, 9)[:-1]   # 9 points from o down to 0.5, 0.5 dropped
-    neg_p = np.linspace(o, 0.5, 8)[:-1]   # 8 points from o down to 0.5, 0.5 dropped
-    values = [float(inv_cdf(p)) for p in pos_p] + [0.0] + [-float(inv_cdf(p)) for p in neg_p]
-    values.sort()
-    top = values[-1]
-    return np.array([v / top for v in values], dtype=np.float64).astype(np.float32)
+
+    def side(count):
+        # quantiles at `count` probabilities stepping from o towards 1/2
+        return [float(inv_cdf(o - i * (o - 0.5) / count)) for i in range(count)]
+
+    positive, negative = side(8), side(7)
+    top = positive[0]  # Phi^-1(o), the largest level
+    raw = sorted([-q for q in negative] + [0.0] + positive)
+    return np.array([q / top for q in raw], dtype=np.float64).astype(np.float32)
 
 
 def int4_levels() -> np.ndarray:
