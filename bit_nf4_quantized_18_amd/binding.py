@@ -607,3 +607,38 @@ def linear_bwd_grouped(q: PackedNF4, parts, x, dy, a, b, alpha: float, h=None, n
             _stream())
     _check(st, "qlora_linear_bwd_grouped")
     return dx, da, db
+
+
+# ---------------------------------------------------------------- storage
+# A packed weight on disk: one .npz of plain arrays (no pickled objects), the
+# buffers byte for byte as the kernels read them plus n, k, the scale-code kind
+# and the codebook id.
+def save_packed(path, q: PackedNF4):
+    """Write ``q``'s buffers (copied to the host) and sizes to ``path`` (.npz)."""
+    import numpy as np
+
+    _need_packed(q)
+    arrays = {"n": np.int64(q.n), "k": np.int64(q.k), "double_quant": np.int32(int(q.double_quant)),
+              "codebook": np.int32(int(q.codebook)), "codes": q.codes.cpu().numpy()}
+    for name in ("scale_codes", "group_scale", "absmax"):
+        t = getattr(q, name)
+        if t is not None:
+            arrays[name] = t.cpu().numpy()
+    np.savez(path, **arrays)
+
+
+def load_packed(path, device="cuda") -> PackedNF4:
+    """Read a packed weight written by ``save_packed`` onto ``device``; the
+    buffer lengths are checked against n and k."""
+    import numpy as np
+    import torch
+
+    with np.load(path, allow_pickle=False) as f:
+        n, k = int(f["n"]), int(f["k"])
+        dq, cb = int(f["double_quant"]), int(f["codebook"])
+        get = (lambda name, dt: torch.from_numpy(np.ascontiguousarray(f[name], dtype=dt)).to(device)
+               if name in f.files else None)
+        q = PackedNF4(n, k, get("codes", np.uint8), dq, get("scale_codes", np.uint8),
+                      get("group_scale", np.float32), get("absmax", np.float32), cb)
+    _need_packed(q)
+    return q

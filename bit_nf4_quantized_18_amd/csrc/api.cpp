@@ -86,6 +86,13 @@ int64_t drop_total(int64_t m, int64_t n, int64_t k, int r) {
   return drop_xm_bytes(m, k) + (f > b ? f : b);
 }
 
+// The sizes every linear entry point accepts (m <= 2^31, n and k <= 2^22):
+// workspace queries beyond them return 0 instead of a size whose products
+// overflow 64 bits.
+bool linear_sizes_ok(int64_t m, int64_t n, int64_t k) {
+  return m > 0 && n > 0 && k > 0 && m <= (INT64_C(1) << 31) && n <= (INT64_C(1) << 22) && k <= (INT64_C(1) << 22);
+}
+
 // Adapter dropout: keep mask (m x k bytes, non-zero = kept) and 1 / (1 - p).
 struct DropArg {
   const uint8_t* keep;
@@ -142,7 +149,9 @@ bool gemm_tiles_fit(int64_t m, int64_t p) { return ((m + 255) / 256) * ((p + 127
 
 extern "C" {
 
-const char* qlora_status_string(qlora_status status) {
+const char* qlora_status_string(int status) {
+  // an int, not the enum: callers pass values from other code, and a C++
+  // enum object outside its enumerators' range is undefined behaviour
   switch (status) {
     case QLORA_OK:
       return "ok";
@@ -163,14 +172,14 @@ const char* qlora_status_string(qlora_status status) {
 }
 
 size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
-  if (m <= 0 || n <= 0 || k <= 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (!linear_sizes_ok(m, n, k) || r < 0 || r > QLORA_MAX_RANK) return 0;
   const int64_t f = fwd_layout(m, n, k, r).total;
   const int64_t b = bwd_layout(m, n, k, r, r).total;
   return static_cast<size_t>(f > b ? f : b);
 }
 
 size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int g, int r) {
-  if (m <= 0 || n <= 0 || k <= 0 || g < 1 || g > QLORA_MAX_PARTS || r < 1 || g * r > QLORA_MAX_RANK) return 0;
+  if (!linear_sizes_ok(m, n, k) || g < 1 || g > QLORA_MAX_PARTS || r < 1 || g * r > QLORA_MAX_RANK) return 0;
   const int64_t f = fwd_layout(m, n, k, g * r).total;
   const int64_t b = bwd_layout(m, n, k, g * r, r).total;
   return static_cast<size_t>(f > b ? f : b);
@@ -197,7 +206,7 @@ qlora_status qlora_nf4_quantize(const float* w, int64_t numel, int double_quant,
                                  stream);
 }
 
-qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dtype, void* out,
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, int out_dtype, void* out,
                                   hipStream_t stream) {
   const qlora_status st = check_weight(w, false);
   if (st != QLORA_OK) return st;
@@ -214,10 +223,9 @@ namespace {
 
 // Both linear calls in one form: a weight of grp->g parts (grp null: one
 // part) with r adapter slots in total, rpart per part, s = alpha / rpart.
-qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x, int64_t m,
-                             const uint16_t* a, const uint16_t* b, int r, int rpart, float alpha, uint16_t* y,
-                             float* h_out, void* ws, size_t ws_bytes, hipStream_t stream,
-                             const DropArg* drop = nullptr, bool f16 = false, bool fwd_sized_ws = false) {
+// The forward's checks of everything but the workspace.
+qlora_status check_fwd_args(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                            const uint16_t* b, int r, const uint16_t* y, const float* h_out) {
   qlora_status st = check_weight(w, true);
   if (st != QLORA_OK) return st;
   if (m < 0 || m > (INT64_C(1) << 31)) return QLORA_ERR_SHAPE;
@@ -230,6 +238,15 @@ qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* 
   if (!aligned16(x) || !aligned16(y)) return QLORA_ERR_ALIGN;
   if (r > 0 && (!aligned16(a) || !aligned16(b))) return QLORA_ERR_ALIGN;
   if (h_out != nullptr && !aligned16(h_out)) return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+qlora_status linear_fwd_impl(const qlora_nf4_weight* w, const qlora::LoraParts* grp, const uint16_t* x, int64_t m,
+                             const uint16_t* a, const uint16_t* b, int r, int rpart, float alpha, uint16_t* y,
+                             float* h_out, void* ws, size_t ws_bytes, hipStream_t stream,
+                             const DropArg* drop = nullptr, bool f16 = false, bool fwd_sized_ws = false) {
+  const qlora_status st = check_fwd_args(w, x, m, a, b, r, y, h_out);
+  if (st != QLORA_OK || m == 0) return st;
   const int64_t n = w->n, k = w->k;
   const bool grouped = grp != nullptr;
   if (drop != nullptr && r == 0) drop = nullptr;  // no adapter, nothing to drop
@@ -419,8 +436,14 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* w, const uint16_t* x, int6
 
 namespace qlora {
 
+qlora_status linear_fwd_check(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                              const uint16_t* b, int r, const uint16_t* y, const float* h_out) {
+  return check_fwd_args(w, x, m, a, b, r, y, h_out);
+}
+
 size_t linear_fwd_scratch_bytes(int64_t m, int64_t n, int64_t k, int r) {
-  if (m <= 0 || n <= 0 || k <= 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  // sizes the forward rejects: 0, and the forward itself reports the error
+  if (!linear_sizes_ok(m, n, k) || r < 0 || r > QLORA_MAX_RANK) return 0;
   return static_cast<size_t>(fwd_layout(m, n, k, r).total);
 }
 
@@ -494,7 +517,7 @@ static qlora_status check_adapter(const uint16_t* a, const uint16_t* b, int r) {
 }
 
 qlora_status qlora_merge(const qlora_nf4_weight* w, const uint16_t* a, const uint16_t* b, int r, float alpha,
-                         qlora_dtype out_dtype, void* out, hipStream_t stream) {
+                         int out_dtype, void* out, hipStream_t stream) {
   qlora_status st = check_weight(w, false);
   if (st != QLORA_OK) return st;
   if (w->k % QLORA_BLOCK != 0) return QLORA_ERR_SHAPE;
@@ -506,7 +529,7 @@ qlora_status qlora_merge(const qlora_nf4_weight* w, const uint16_t* a, const uin
   return hip_status(qlora::launch_merge(view(w), a, b, r, s, out_dtype == QLORA_F32, out, stream));
 }
 
-qlora_status qlora_unmerge(const void* merged, qlora_dtype dtype, int64_t n, int64_t k, const uint16_t* a,
+qlora_status qlora_unmerge(const void* merged, int dtype, int64_t n, int64_t k, const uint16_t* a,
                            const uint16_t* b, int r, float alpha, void* out, hipStream_t stream) {
   if (dtype != QLORA_BF16 && dtype != QLORA_F32) return QLORA_ERR_UNSUPPORTED;
   if (n < 1 || k < 1 || k % 8 != 0 || n > (INT64_C(1) << 40) / k) return QLORA_ERR_SHAPE;
@@ -551,7 +574,7 @@ static qlora_status make_drop(const uint8_t* keep, float p, DropArg* out) {
 }
 
 size_t qlora_linear_dropout_workspace_bytes(int64_t m, int64_t n, int64_t k, int r) {
-  if (m <= 0 || n <= 0 || k <= 0 || r < 0 || r > QLORA_MAX_RANK) return 0;
+  if (!linear_sizes_ok(m, n, k) || r < 0 || r > QLORA_MAX_RANK) return 0;
   if (r == 0) return qlora_linear_workspace_bytes(m, n, k, r);
   return static_cast<size_t>(drop_total(m, n, k, r));
 }

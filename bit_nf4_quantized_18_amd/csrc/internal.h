@@ -168,7 +168,11 @@ hipError_t launch_rank_grads(const float* dh, const uint16_t* x, int64_t k, cons
 // The plain forward (qlora_linear_fwd) on a scratch area the caller
 // provides, checked against the forward's own workspace layout
 // (linear_fwd_scratch_bytes) rather than the two-direction size of the
-// public calls; QLORA_ERR_WORKSPACE if it is too small.
+// public calls; QLORA_ERR_WORKSPACE if it is too small. linear_fwd_check
+// runs the forward's argument checks alone (no device use);
+// linear_fwd_scratch_bytes is 0 for sizes those checks reject.
+qlora_status linear_fwd_check(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
+                              const uint16_t* b, int r, const uint16_t* y, const float* h_out);
 size_t linear_fwd_scratch_bytes(int64_t m, int64_t n, int64_t k, int r);
 qlora_status linear_fwd_scratch(const qlora_nf4_weight* w, const uint16_t* x, int64_t m, const uint16_t* a,
                                 const uint16_t* b, int r, float alpha, uint16_t* y, float* h_out, void* scratch,

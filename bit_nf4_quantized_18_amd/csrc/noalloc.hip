@@ -44,10 +44,11 @@ qlora_status scratch_on_current_device(void** out) {
 extern "C" qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* w, const uint16_t* x, int64_t m,
                                                  const uint16_t* a, const uint16_t* b, int r, float alpha,
                                                  uint16_t* y, float* h_out, hipStream_t stream) {
-  // sizes first: a call that does not fit is rejected before the device is touched
-  if (w != nullptr && w->n > 0 && w->k > 0 && m > 0 && r >= 0 && r <= QLORA_MAX_RANK &&
-      qlora::linear_fwd_scratch_bytes(m, w->n, w->k, r) > QLORA_NOALLOC_SCRATCH_BYTES)
-    return QLORA_ERR_WORKSPACE;
+  // arguments and sizes first: a call that is invalid or does not fit is
+  // rejected before the device is touched
+  const qlora_status chk = qlora::linear_fwd_check(w, x, m, a, b, r, y, h_out);
+  if (chk != QLORA_OK || m == 0) return chk;
+  if (qlora::linear_fwd_scratch_bytes(m, w->n, w->k, r) > QLORA_NOALLOC_SCRATCH_BYTES) return QLORA_ERR_WORKSPACE;
   void* ptr = nullptr;
   const qlora_status st = scratch_on_current_device(&ptr);
   if (st != QLORA_OK) return st;

@@ -86,6 +86,8 @@ typedef enum {
   QLORA_ERR_HIP = -6          /* a kernel launch failed                         */
 } qlora_status;
 
+/* Element types; the calls take them as plain int (any other value is
+ * rejected with QLORA_ERR_UNSUPPORTED). */
 typedef enum { QLORA_BF16 = 0, QLORA_F32 = 1, QLORA_F16 = 2 } qlora_dtype;
 
 #define QLORA_BLOCK 64     /* weights per absmax block              */
@@ -153,7 +155,7 @@ qlora_status qlora_quantize_codebook(const float* w, int64_t numel, int double_q
  * (restore = level[code] * scale; dequantize to bfloat16 before the matmul).
  * Any n, k >= 1 (k need not be a multiple of 64 here).
  * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED (dtype) / HIP. */
-qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, qlora_dtype out_dtype, void* out,
+qlora_status qlora_nf4_dequantize(const qlora_nf4_weight* w, int out_dtype, void* out,
                                   hipStream_t stream);
 
 /* Forward: Y = X W16^T + s (X A^T) B^T with s = fl32(alpha / r).
@@ -269,7 +271,9 @@ qlora_status qlora_linear_bwd_dropout_f16(const qlora_nf4_weight* w, const uint1
                                           size_t ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace that qlora_linear_fwd and qlora_linear_bwd need
- * for these sizes (the larger of the two); 0 if none. Host only, no GPU use. */
+ * for these sizes (the larger of the two); 0 if none, and 0 for sizes the
+ * calls reject (m <= 0 or m > 2^31, n or k outside 1 .. 2^22, r outside
+ * 0 .. QLORA_MAX_RANK). Host only, no GPU use. */
 size_t qlora_linear_workspace_bytes(int64_t m, int64_t n, int64_t k, int r);
 
 /* Largest scratch area qlora_linear_fwd_noalloc uses (16 MiB per device). */
@@ -371,7 +375,7 @@ size_t qlora_linear_grouped_workspace_bytes(int64_t m, int64_t n, int64_t k, int
  * Bit-exact with the CPU oracle. Errors: NULL / ALIGN / SHAPE (k % 64 != 0,
  * r < 0) / UNSUPPORTED (r > QLORA_MAX_RANK, dtype, codebook, flag) / HIP. */
 qlora_status qlora_merge(const qlora_nf4_weight* w, const uint16_t* a, const uint16_t* b, int r,
-                         float alpha, qlora_dtype out_dtype, void* out, hipStream_t stream);
+                         float alpha, int out_dtype, void* out, hipStream_t stream);
 
 /* Take an adapter back out of a merged weight (adapters are stored and
  * swapped per task: Ultralytics glossary "QLoRA", "Compromessi"):
@@ -381,7 +385,7 @@ qlora_status qlora_merge(const qlora_nf4_weight* w, const uint16_t* a, const uin
  *            `merged` itself (in place).
  *   n >= 1, k % 8 == 0. a, b, r, alpha as in qlora_merge.
  * Errors: NULL / ALIGN / SHAPE / UNSUPPORTED / HIP. */
-qlora_status qlora_unmerge(const void* merged, qlora_dtype dtype, int64_t n, int64_t k,
+qlora_status qlora_unmerge(const void* merged, int dtype, int64_t n, int64_t k,
                            const uint16_t* a, const uint16_t* b, int r, float alpha, void* out,
                            hipStream_t stream);
 
@@ -398,8 +402,9 @@ qlora_status qlora_requantize(const qlora_nf4_weight* w, const uint16_t* a, cons
                               uint8_t* codes, uint8_t* scale_codes, float* group_scale,
                               float* absmax, hipStream_t stream);
 
-/* Static, NUL-terminated description of a status. Host only. */
-const char* qlora_status_string(qlora_status status);
+/* Static, NUL-terminated description of a status (any int: values that are
+ * no qlora_status get a generic text). Host only. */
+const char* qlora_status_string(int status);
 
 /* Copy the 16 float32 NF4 levels the kernels use into out16 (host memory).
  * The table is built on the host from the standard-normal quantile at the

@@ -195,3 +195,32 @@ def test_float8_scale_code_bit_exact(gpu_lib, name):
     torch.cuda.synchronize()
     assert np.array_equal(d16.reshape(-1).view(torch.int16).cpu().numpy().view(np.uint16), bits_ref)
     assert np.array_equal(d32.reshape(-1).cpu().numpy().view(np.uint32), w32_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("dq", [1, 0])
+def test_saved_weight_reloads_bit_exact(gpu_lib, tmp_path, dq):
+    """A weight quantized on the GPU, written with save_packed and read back
+    with load_packed, dequantizes to the same bits as before and gives the
+    same forward output; both are checked against the oracle's dequantized
+    weight."""
+    import torch
+
+    n, k = 272, 640
+    w = synth.normal((n, k), 0.02, "storage", "W")
+    say(f"[quant] case=storage_round_trip dq={dq}")
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda(), double_quant=bool(dq))
+    path = tmp_path / "w.npz"
+    gpu_lib.save_packed(path, q)
+    r = gpu_lib.load_packed(path)
+    w_before = gpu_lib.dequantize(q, torch.float32)
+    w_after = gpu_lib.dequantize(r, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(w_before, w_after)
+    lv = O.nf4_levels()
+    ref, _ = O.dequantize(O.quantize(w.reshape(-1), dq, lv), lv)
+    assert np.array_equal(w_after.cpu().numpy().reshape(-1).view(np.uint32), ref.view(np.uint32))
+    x = torch.from_numpy(synth.normal((5, k), 1.0, "storage", "X")).to(torch.bfloat16).cuda()
+    y0, _ = gpu_lib.linear_fwd(q, x)
+    y1, _ = gpu_lib.linear_fwd(r, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
