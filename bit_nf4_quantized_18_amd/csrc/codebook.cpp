@@ -10,6 +10,8 @@
 // bracket is halved 200 times, far below the float64 resolution of the result;
 // each level is divided by the largest in double and rounded once to float.
 #include <cmath>
+#include <cstring>
+#include <limits>
 #include <mutex>
 
 #include "internal.h"
@@ -82,6 +84,83 @@ const Levels& nf4_table() {
   static std::once_flag once;
   static Levels table;
   std::call_once(once, [] { table = build_levels(); });
+  return table;
+}
+
+namespace {
+
+// Total order of floats as integers (-0 and +0 both map to 0).
+int64_t float_key(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, 4);
+  const int64_t mag = static_cast<int64_t>(b & 0x7FFFFFFFu);
+  return (b & 0x80000000u) ? -mag : mag;
+}
+
+float key_float(int64_t key) {
+  const uint32_t b = key < 0 ? (0x80000000u | static_cast<uint32_t>(-key)) : static_cast<uint32_t>(key);
+  float f;
+  std::memcpy(&f, &b, 4);
+  return f;
+}
+
+// The nearest-level rule between lo < hi in float32: true when hi is nearer
+// (ties keep lo). volatile keeps each difference a float32 result.
+bool hi_nearer(float x, float lo, float hi) {
+  volatile float d_lo = x - lo;
+  volatile float d_hi = hi - x;
+  return d_hi < d_lo;
+}
+
+// The smallest float x in (lo, hi] for which hi is nearer: the rule is false
+// at lo and true at hi, and monotone in between, so bisection over the
+// floats' order finds the switch point exactly.
+float switch_point(float lo, float hi) {
+  int64_t a = float_key(lo), b = float_key(hi);
+  while (b - a > 1) {
+    const int64_t mid = a + (b - a) / 2;
+    if (hi_nearer(key_float(mid), lo, hi)) {
+      b = mid;
+    } else {
+      a = mid;
+    }
+  }
+  return key_float(b);
+}
+
+EncodeTable build_encode(const Levels& L) {
+  float u16[15];
+  for (int k = 0; k < 15; ++k) u16[k] = 16.0f * switch_point(L.v[k], L.v[k + 1]);  // exact scaling
+  EncodeTable E;
+  for (int b = 0; b <= 32; ++b) {
+    const float lo = static_cast<float>(b - 16), hi = lo + 1.0f;
+    uint32_t base = 0;
+    float thr = std::numeric_limits<float>::infinity();
+    for (int k = 0; k < 15; ++k) {
+      if (u16[k] <= lo) {
+        ++base;
+      } else if (u16[k] < hi) {
+        thr = u16[k];  // at most one per bucket (switch points are > 1 apart in t)
+      }
+    }
+    E.thr16[b] = thr;
+    E.base[b] = base;
+  }
+  return E;
+}
+
+}  // namespace
+
+const EncodeTable& encode_table(int codebook) {
+  if (codebook == QLORA_CODEBOOK_INT4) {
+    static std::once_flag once;
+    static EncodeTable table;
+    std::call_once(once, [] { table = build_encode(codebook_table(QLORA_CODEBOOK_INT4)); });
+    return table;
+  }
+  static std::once_flag once;
+  static EncodeTable table;
+  std::call_once(once, [] { table = build_encode(nf4_table()); });
   return table;
 }
 

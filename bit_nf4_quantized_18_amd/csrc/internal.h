@@ -28,6 +28,21 @@ const Levels& nf4_table();
 // evenly spaced levels on [-1, 1]); any other value gives the NF4 table.
 const Levels& codebook_table(int codebook);
 
+// Nearest-level encoding of x in [-1, 1] for the quantize kernel, by
+// buckets of t = 16 x. Between adjacent levels L_k < L_k+1 the rule "code
+// k + 1 when fl32(L_k+1 - x) < fl32(x - L_k), else k" switches once, at a
+// float U_k (both distances are monotone in x), so the code of x is the
+// number of switch points U_k <= x. Bucket b = floor(t) + 16 (0 .. 32)
+// covers t in [b - 16, b - 15); base[b] counts the switch points at or
+// below its start and thr16[b] is 16 U_k of the one switch point inside it
+// (+inf if none: adjacent switch points are more than 1/16 apart for both
+// codebooks). Built once per codebook on the host from the level table.
+struct EncodeTable {
+  float thr16[33];
+  uint32_t base[33];
+};
+const EncodeTable& encode_table(int codebook);
+
 // ---------------------------------------------------------------------------
 // Launchers (each enqueues on `s` and returns hipGetLastError()).
 // ---------------------------------------------------------------------------

@@ -17,22 +17,6 @@ namespace {
 constexpr int kBlock = 64;
 constexpr int kGroup = 256;
 
-// Nearest level of x in [-1, 1]: bracket L[k] <= x < L[k+1] by a 4-step
-// binary search over the ascending table (held in LDS, with lv[16] = +inf),
-// then the closer of the two fp32 distances; an exact tie keeps k (the lower
-// index). Levels further away cannot tie: adjacent gaps exceed 0.079 in the
-// NF4 table and are 2/15 in the evenly spaced one.
-__device__ __forceinline__ uint32_t nearest_nf4(float x, const float* lv) {
-  uint32_t k = 0;
-#pragma unroll
-  for (uint32_t half = 8; half >= 1; half >>= 1) {
-    if (x >= lv[k + half]) k += half;
-  }
-  const float d_lo = x - lv[k];      // >= 0, = fl32(|x - L_k|)
-  const float d_hi = lv[k + 1] - x;  // > 0,  = fl32(|x - L_k+1|); +inf for k = 15
-  return (d_hi < d_lo) ? k + 1 : k;
-}
-
 // U_k = fl32(k / 255): correctly rounded float32 division.
 __device__ __forceinline__ float u8_level(uint32_t k) { return static_cast<float>(k) / 255.0f; }
 
@@ -79,17 +63,22 @@ __device__ __forceinline__ uint32_t nearest_e4m4(float x2) {
 // 2 KB contiguous per step. The block absmax is an 8-lane max-reduction; the
 // codes of a lane's 8 elements form one 32-bit store. Block maxima go to LDS
 // and the group maximum M_g is a workgroup reduction.
+//
+// Per weight, x = fl32(w / a_b) (correctly rounded) is formed as t = 16 x by
+// quotient16 from the block's fl32(16 / a_b), and its code is read from the
+// bucket table (EncodeTable) in LDS: one 8-byte read of (16 U, base) and one
+// compare. Blocks whose absmax lies outside [2^-60, 2^60] take the IEEE
+// division instead (same result, more instructions).
 __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restrict__ w, int64_t numel, int dq,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scale_codes,
                                                            float* __restrict__ group_scale,
-                                                           float* __restrict__ absmax_out, Levels L) {
-  __shared__ float lv[17];
+                                                           float* __restrict__ absmax_out, EncodeTable E) {
+  __shared__ u32x2 enc[33];
   __shared__ float blk_max[kGroup];
   __shared__ float wave_max[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 16) lv[tid] = L.v[tid];
-  if (tid == 16) lv[16] = __builtin_inff();
+  if (tid < 33) enc[tid] = u32x2{__float_as_uint(E.thr16[tid]), E.base[tid]};
   __syncthreads();
 
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
@@ -137,11 +126,22 @@ __global__ __launch_bounds__(256) void nf4_quantize_kernel(const float* __restri
     m = fmaxf(m, __shfl_xor(m, 1));
     m = fmaxf(m, __shfl_xor(m, 2));
     m = fmaxf(m, __shfl_xor(m, 4));
+    // t = 16 x for the lane's 8 weights (an all-zero block: every x = 0)
+    float t[8];
+    if (m >= 0x1p-60f && m <= 0x1p60f) {
+      const float y16 = 16.0f / m, m16 = m * 0.0625f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = quotient16(v[it][j], y16, m16);
+    } else {
+      const float mm = m > 0.0f ? m : 1.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) t[j] = 16.0f * (v[it][j] / mm);
+    }
     uint32_t packed = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float x = (m > 0.0f) ? v[it][j] / m : 0.0f;
-      packed |= nearest_nf4(x, lv) << (4 * j);
+      const u32x2 e = enc[encode_bucket(t[j])];
+      packed |= (e[1] + (t[j] >= __uint_as_float(e[0]) ? 1u : 0u)) << (4 * j);
     }
     if (e0 + 8 <= numel) {
       *reinterpret_cast<uint32_t*>(codes + e0 / 2) = packed;
@@ -277,7 +277,7 @@ hipError_t launch_quantize(const float* w, int64_t numel, int dq, int codebook, 
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
   hipLaunchKernelGGL(nf4_quantize_kernel, dim3(static_cast<unsigned>(ngroups)), dim3(256), 0, s, w, numel, dq,
-                     codes, scale_codes, group_scale, absmax, codebook_table(codebook));
+                     codes, scale_codes, group_scale, absmax, encode_table(codebook));
   return hipGetLastError();
 }
 

@@ -15,8 +15,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 @pytest.fixture(scope="module")
 def emul(tmp_path_factory):
     out = str(tmp_path_factory.mktemp("lut") / "lut_emul.so")
-    cmd = ["hipcc", "-O2", "-fPIC", "-shared", "-std=c++17", f"-I{ROOT}/bit_nf4_quantized_18_amd/csrc",
-           f"-I{ROOT}/include", os.path.join(ROOT, "tests", "native", "lut_emul.cpp"), "-o", out]
+    cmd = ["hipcc", "-O2", "-fPIC", "-shared", "-std=c++17", "-ffp-contract=off",
+           f"-I{ROOT}/bit_nf4_quantized_18_amd/csrc", f"-I{ROOT}/include",
+           os.path.join(ROOT, "tests", "native", "lut_emul.cpp"),
+           os.path.join(ROOT, "bit_nf4_quantized_18_amd", "csrc", "codebook.cpp"), "-o", out]
     subprocess.run(cmd, check=True, capture_output=True)
     return ctypes.CDLL(out)
 
@@ -79,3 +81,91 @@ def test_e4m4_unit_matches_oracle_table(emul):
     f.argtypes = [ctypes.c_void_p]
     assert f(out.ctypes.data) == 256
     assert np.array_equal(out.view(np.uint32), O.e4m4_scale_levels().view(np.uint32))
+
+
+def _emul_codes(emul, w, codebook):
+    w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+    codes = np.zeros(w.size, np.uint8)
+    am = np.zeros(-(-w.size // 64), np.float32)
+    f = emul.quant_codes_emul
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    f(w.ctypes.data, w.size, codebook, codes.ctypes.data, am.ctypes.data)
+    return codes, am
+
+
+def _hard_weights(rng):
+    """Inputs that stress the encoding: normal and heavy-tailed weights,
+    values a few ulps either side of every switch point of both codebooks
+    (scaled by many block maxima), exact levels, denormals, tiny and huge
+    blocks, zeros and ties."""
+    parts = [rng.standard_normal(64 * 2000).astype(np.float32) * 0.02,
+             (rng.standard_t(3, 64 * 500) * 0.05).astype(np.float32),
+             (rng.standard_normal(64 * 200) * 1e-41).astype(np.float32),          # denormal blocks
+             (rng.standard_normal(64 * 200) * 1e-25).astype(np.float32),          # absmax below 2^-60
+             (rng.standard_normal(64 * 200) * 1e25).astype(np.float32),           # absmax above 2^60
+             np.zeros(64 * 3, np.float32)]
+    for lv in (O.nf4_levels(), O.int4_levels()):
+        mids = ((lv[:-1].astype(np.float64) + lv[1:]) / 2).astype(np.float32)
+        pts = np.concatenate([lv, mids])
+        near = np.concatenate([np.nextafter(pts, np.float32(np.inf) if s > 0 else -np.float32(np.inf)) for s in (1, -1)]
+                              + [pts])
+        for scale in (1.0, 0.0371, 3.3e-3, 7.7e-7, 2.0 ** -50, 1234.5):
+            blk = np.clip(near, -1, 1).astype(np.float32)
+            # pad to whole blocks, each led by its absmax 1 so x = value exactly (scaled)
+            n = -(-blk.size // 63)
+            body = np.zeros(n * 63, np.float32)
+            body[:blk.size] = blk
+            blocks = np.concatenate([np.ones((n, 1), np.float32), body.reshape(n, 63)], axis=1)
+            parts.append((blocks * np.float32(scale)).reshape(-1).astype(np.float32))
+        # random values across the range with random block maxima
+        x = rng.uniform(-1, 1, 64 * 400).astype(np.float32)
+        parts.append(x * np.repeat(10.0 ** rng.uniform(-30, 30, 400), 64).astype(np.float32))
+    # values below 2^-100 in blocks with a normal absmax
+    tiny = (rng.standard_normal(64 * 50) * 1e-32).astype(np.float32)
+    tiny[::64] = 1.0
+    parts.append(tiny)
+    return np.concatenate(parts)
+
+
+@pytest.mark.parametrize("codebook", [0, 1])
+def test_quantize_encoding_model_matches_oracle(emul, codebook):
+    """The quantize kernel's per-weight path (w / absmax by one FMA correction
+    of a correctly rounded reciprocal, then the bucket table) gives the
+    oracle's codes, element for element, on inputs around every decision."""
+    rng = np.random.Generator(np.random.PCG64(2024 + codebook))
+    w = _hard_weights(rng)
+    lv = O.int4_levels() if codebook == 1 else O.nf4_levels()
+    codes, am = _emul_codes(emul, w, codebook)
+    q = O.quantize(w, False, lv)
+    assert np.array_equal(am.view(np.uint32), q["absmax"].astype(np.float32).view(np.uint32))
+    ref = O.unpack_nibbles(q["codes"], w.size)
+    bad = np.flatnonzero(codes != ref)
+    assert bad.size == 0, (bad[:5], w[bad[:5]], codes[bad[:5]], ref[bad[:5]])
+
+
+@pytest.mark.parametrize("codebook", [0, 1])
+def test_bucket_table_against_levels(emul, codebook):
+    """Every bucket holds at most one switch point, and each switch point lies
+    strictly between its two levels (16 U in t units)."""
+    thr = np.zeros(33, np.float32)
+    base = np.zeros(33, np.uint32)
+    f = emul.encode_table_emul
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(codebook, thr.ctypes.data, base.ctypes.data) == 33
+    lv = O.int4_levels() if codebook == 1 else O.nf4_levels()
+    finite = thr[np.isfinite(thr)]
+    assert finite.size == 15 - 0  # every switch point has its own bucket
+    u = finite / 16
+    assert np.all(u > lv[:-1]) and np.all(u <= lv[1:])
+    assert base[0] == 0 and base[32] == 15 and np.all(np.diff(base.astype(np.int64)) >= 0)
+
+
+def test_quotient16_is_correctly_rounded(emul):
+    """The quantize kernel's division w / absmax (times 16) by one FMA
+    correction of the correctly rounded reciprocal equals the IEEE float32
+    quotient: 3e7 random pairs and four numerators for every significand of
+    the divisor."""
+    f = emul.quotient16_check
+    f.argtypes = [ctypes.c_int64, ctypes.c_uint64]
+    f.restype = ctypes.c_int64
+    assert f(30_000_000, 77) == 0
