@@ -57,7 +57,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--only", default="", help="comma list of parts to run (train,f16,dropout,gemm,library,copy,decode,decode_token,dequant,quant,merge,cpu)")
+    ap.add_argument("--counters", action="store_true",
+                    help="launch once each, in a fixed order, the kernels whose HBM counters are summarised under "
+                         "profiles/ (a 256 MiB copy, quantize, dequantize, decode GEMV), print the order to stderr "
+                         "and exit; meant to run under rocprofv3 --pmc")
+    ap.add_argument("--only", default="", help="comma list of parts to run (train,f16,dropout,c5,gemm,library,copy,decode,decode_token,dequant,quant,merge,cpu)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the layer has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -80,6 +84,10 @@ def main():
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
+
+    if args.counters:
+        counter_sequence(qn, synth, torch, dev)
+        return
 
     wl = synth.LAYERS_7B
     M, R, ALPHA = wl.m, wl.r, wl.alpha
@@ -235,6 +243,103 @@ def main():
         parts["train_step_dropout"]["p"] = p_drop
         for L in layers:
             del L["keep"], L["wsd"]
+
+    # ----------------------------------------- 65B-shaped layer set (C5)
+    # q/k/v/o 8192x8192, gate/up 22016x8192, down 8192x22016; 4096 tokens;
+    # LoRA r=64, alpha=16; Student-t(4) x 0.02 weights. Inputs are drawn on
+    # the device from one seeded generator (Student-t(4) as z / sqrt(chi2_4 /
+    # 4) from five normals), quantized there, and the fwd+bwd step of the
+    # seven linears (gate/up grouped) is captured in one graph and replayed.
+    if want("c5"):
+        wl5 = synth.LAYERS_65B
+        M5, R5, A5 = wl5.m, wl5.r, wl5.alpha
+        log("[bench] 65B layer set: drawing and quantizing the weights on the device")
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(6504)
+
+        def dnormal(shape, std):
+            return torch.randn(shape, generator=gen, device=dev) * std
+
+        def dstudent_t4(shape, scale):
+            chi2 = torch.zeros(shape, device=dev)
+            for _ in range(4):
+                chi2.add_(torch.randn(shape, generator=gen, device=dev).square_())
+            return torch.randn(shape, generator=gen, device=dev).div_(chi2.div_(4.0).sqrt_()).mul_(scale)
+
+        def pack_cat(qs):
+            return qn.PackedNF4(sum(q.n for q in qs), qs[0].k, torch.cat([q.codes for q in qs]), True,
+                                torch.cat([q.scale_codes for q in qs]), torch.cat([q.group_scale for q in qs]))
+
+        by5 = {lay.name: lay for lay in wl5.layers}
+        x_h = dnormal((M5, 8192), 1.0).to(torch.bfloat16)
+        x_f = dnormal((M5, 22016), 1.0).to(torch.bfloat16)
+        groups5 = []
+        # at r = 64 three stacked adapters would take 192 H slots, beyond the
+        # 128 of one call: q, k and v run as single calls
+        for names in (("q_proj",), ("k_proj",), ("v_proj",), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",)):
+            lays = [by5[nm] for nm in names]
+            k5 = lays[0].k
+            qs = []
+            for lay in lays:
+                w = dstudent_t4((lay.n, k5), 0.02)
+                qs.append(qn.quantize(w))
+                del w
+            ntot = sum(lay.n for lay in lays)
+            G = dict(parts=[lay.n for lay in lays], q=pack_cat(qs) if len(qs) > 1 else qs[0],
+                     x=x_f if k5 == 22016 else x_h,
+                     a=dnormal((len(lays) * R5, k5), 1.0 / R5).to(torch.bfloat16),
+                     b=dnormal((ntot, R5), 0.01).to(torch.bfloat16),
+                     dy=dnormal((M5, ntot), 1.0).to(torch.bfloat16),
+                     y=torch.empty((M5, ntot), dtype=torch.bfloat16, device=dev),
+                     h=torch.empty((M5, len(lays) * R5), dtype=torch.float32, device=dev),
+                     dx=torch.empty((M5, k5), dtype=torch.bfloat16, device=dev),
+                     da=torch.empty((len(lays) * R5, k5), dtype=torch.float32, device=dev),
+                     db=torch.empty((ntot, R5), dtype=torch.float32, device=dev))
+            nbytes = (qn.grouped_workspace_bytes(M5, ntot, k5, len(lays), R5) if len(lays) > 1
+                      else qn.workspace_bytes(M5, ntot, k5, R5))
+            G["ws"] = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+            groups5.append(G)
+            del qs
+        torch.cuda.synchronize()
+
+        def step65():
+            for G in groups5:
+                if len(G["parts"]) == 1:
+                    qn.linear_fwd(G["q"], G["x"], G["a"], G["b"], A5, out=G["y"], h_out=G["h"], ws=G["ws"])
+                    qn.linear_bwd(G["q"], G["x"], G["dy"], G["a"], G["b"], A5, h=G["h"], dx=G["dx"], da=G["da"],
+                                  db=G["db"], ws=G["ws"])
+                else:
+                    qn.linear_fwd_grouped(G["q"], G["parts"], G["x"], G["a"], G["b"], A5, out=G["y"], h_out=G["h"],
+                                          ws=G["ws"])
+                    qn.linear_bwd_grouped(G["q"], G["parts"], G["x"], G["dy"], G["a"], G["b"], A5, h=G["h"],
+                                          dx=G["dx"], da=G["da"], db=G["db"], ws=G["ws"])
+
+        fl65 = sum(fwd_flops(M5, lay.n, lay.k, R5) + bwd_flops(M5, lay.n, lay.k, R5) for lay in wl5.layers)
+        step65()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step65()
+        g.replay()
+        torch.cuda.synchronize()
+        reps65 = 10
+        e0, e1 = ev(), ev()
+        e0.record()
+        for _ in range(reps65):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms65 = e0.elapsed_time(e1) / reps65
+        tf65 = fl65 / (ms65 * 1e-3) / 1e12
+        parts["train_step_65b"] = {"ms_per_step": ms65, "tflops": tf65, "gflop_per_step": fl65 / 1e9,
+                                   "frac_bf16_peak": tf65 / BF16_PEAK_TFLOPS, "replays": reps65,
+                                   "workload": "llama65b_layer_set_m4096_r64", "tokens": M5, "lora_r": R5,
+                                   "lora_alpha": A5, "weights": "Student-t(4) x 0.02, drawn on the device",
+                                   "launches": "gate/up grouped; q, k, v, o and down single"}
+        log(f"[bench] 65B layer set fwd+bwd (graph): {ms65:.3f} ms  {tf65:.1f} TFLOP/s "
+            f"({100 * tf65 / BF16_PEAK_TFLOPS:.1f}% of bf16 peak)")
+        del g, groups5, x_h, x_f
+        torch.cuda.empty_cache()
 
     # ------------------------------------------- fused dequant-GEMM kernels
     roofline = None
@@ -491,15 +596,25 @@ def main():
                                                          qn.binding._stream()), "quantize")
             qcall(ws_pool[0])
             torch.cuda.synchronize()
+            # one graph over the pool (distinct sources), replayed: launch
+            # gaps are the graph's, not the Python loop's
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                for src in ws_pool:
+                    qcall(src)
+            g.replay()
+            torch.cuda.synchronize()
             e0, e1 = ev(), ev()
             e0.record()
-            for src in ws_pool:
-                qcall(src)
+            for _ in range(3):
+                g.replay()
             e1.record()
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / len(ws_pool)
+            del g
+            us = e0.elapsed_time(e1) * 1e3 / (3 * len(ws_pool))
             byt = n * k * (4 + 0.5 + 1 / 64 + 1 / 4096)
             qres.append({"n": n, "k": k, "us_per_call": us, "GBps": byt / (us * 1e-6) / 1e9,
+                         "weights_per_s": n * k / (us * 1e-6),
                          "frac_hbm_peak": byt / (us * 1e-6) / 1e9 / HBM_PEAK_GBS})
             log(f"[bench] quantize {n}x{k}: {us:.2f} us  {byt / (us * 1e-6) / 1e9:.0f} GB/s")
             del ws_pool, w
@@ -552,8 +667,12 @@ def main():
     # -------------------------------------------------------- CPU baseline
     cpu = None
     if want("cpu") and not args.no_cpu:
-        cpu = cpu_baseline(layers, M, R, ALPHA, wl)
-        log(f"[bench] cpu oracle: {cpu['value']:.4f} {cpu['unit']} on {cpu['cores']} threads")
+        cpu = cpu_baseline(layers, M, R, ALPHA, wl, parts)
+        log(f"[bench] cpu oracle: {cpu['value']:.4f} {cpu['unit']} ({cpu['blas_threads']} BLAS threads, "
+            f"{cpu['host_cpus']} host CPUs)")
+        for name, leg in cpu["legs"].items():
+            log(f"[bench] cpu oracle {name}: " + ", ".join(f"{k}={v:.4g}" for k, v in leg.items()
+                                                            if isinstance(v, float)))
 
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -566,6 +685,65 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "parts": parts,
     }
     print(json.dumps(line), flush=True)
+
+
+def counter_sequence(qn, synth, torch, dev):
+    """Setup first (weights quantized, inputs drawn), then exactly one launch
+    per line below, in this order and with nothing launched in between, so
+    the last dispatches of a counter trace map onto these lines one to one.
+    Algorithmic bytes (read, written) are printed with each line."""
+    MiB = 1 << 20
+    src = torch.ones(256 * MiB, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ops = []
+    ops.append(("copy 256 MiB", lambda: dst.copy_(src), 256 * MiB, 256 * MiB))
+    shapes = [(4096, 4096), (11008, 4096), (4096, 11008)]
+    layers = {(l.n, l.k): l for l in synth.DECODE_7B.layers}
+    packed, w32 = {}, {}
+    for (n, k) in shapes:
+        w32[(n, k)] = torch.from_numpy(synth.weight(synth.DECODE_7B, layers[(n, k)])).to(dev)
+        packed[(n, k)] = qn.quantize(w32[(n, k)])
+    scratch_q = {key: (torch.empty(key[0] * key[1] // 2, dtype=torch.uint8, device=dev),
+                       torch.empty(key[0] * key[1] // 64, dtype=torch.uint8, device=dev),
+                       torch.empty(-(-(key[0] * key[1] // 64) // 256), dtype=torch.float32, device=dev))
+                 for key in shapes[:2]}
+    lib = qn.load()
+    P = qn.binding._ptr
+    for (n, k) in shapes[:2]:
+        c, sc, gs = scratch_q[(n, k)]
+
+        def qcall(n=n, k=k, c=c, sc=sc, gs=gs):
+            qn.binding._check(lib.qlora_nf4_quantize(P(w32[(n, k)]), n * k, 1, P(c), P(sc), P(gs), None,
+                                                     qn.binding._stream()), "quantize")
+        ops.append((f"quantize {n}x{k}", qcall, 4 * n * k, n * k * (0.5 + 1 / 64 + 1 / 4096)))
+    outs = {key: torch.empty(key, dtype=torch.bfloat16, device=dev) for key in shapes[:2]}
+    for (n, k) in shapes[:2]:
+        def dcall(n=n, k=k):
+            qn.binding._check(lib.qlora_nf4_dequantize(qn.binding.ctypes.byref(packed[(n, k)].c_struct()), 0,
+                                                       P(outs[(n, k)]), qn.binding._stream()), "dequantize")
+        ops.append((f"dequantize bf16 {n}x{k}", dcall, n * k * (0.5 + 1 / 64 + 1 / 4096), 2 * n * k))
+    gemv_in = {}
+    for (n, k) in shapes:
+        lay = layers[(n, k)]
+        a = torch.from_numpy(synth.lora_a(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
+        b = torch.from_numpy(synth.lora_b(synth.DECODE_7B, lay)).to(torch.bfloat16).to(dev)
+        for m in (1, 16):
+            x = torch.from_numpy(synth.activations(synth.DECODE_7B, lay, m)).to(torch.bfloat16).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(1, qn.workspace_bytes(m, n, k, 16)), dtype=torch.uint8, device=dev)
+            gemv_in[(n, k, m)] = (x, a, b, y, ws)
+
+            def gcall(n=n, k=k, m=m):
+                x, a, b, y, ws = gemv_in[(n, k, m)]
+                qn.linear_fwd(packed[(n, k)], x, a, b, 32.0, want_h=False, out=y, ws=ws)
+            rd = n * k * (0.5 + 1 / 64 + 1 / 4096) + 2 * m * k + 2 * 16 * (k + n)
+            ops.append((f"decode GEMV {n}x{k} m={m} r=16", gcall, rd, 2 * m * n))
+    torch.cuda.synchronize()
+    for name, fn, rd, wr in ops:
+        fn()
+        log(f"[counters] {name}: algorithmic read {rd:.0f} B, write {wr:.0f} B")
+    torch.cuda.synchronize()
+    log(f"[counters] {len(ops)} launches")
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "nf4_gemm_fwd_7b_layers_traffic.md")
@@ -607,24 +785,48 @@ def step_fwd_base(layers, M):
     return sum(2.0 * M * L["lay"].n * L["lay"].k for L in layers)
 
 
-def cpu_baseline(layers, M, R, ALPHA, wl, min_s=10.0, max_passes=24):
-    """The oracle, untouched, on a bounded sample of the same step: for every
+def cpu_threads():
+    """(host CPUs this process may run on, threads of the BLAS that numpy uses)."""
+    host = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        blas = None
+    return host, blas
+
+
+def timed_passes(fn, min_s, max_passes):
+    """Run fn() in whole passes until at least min_s seconds (at most
+    max_passes); returns (seconds, passes)."""
+    t, n = 0.0, 0
+    while n < max_passes and (n == 0 or t < min_s):
+        t0 = time.perf_counter()
+        fn()
+        t += time.perf_counter() - t0
+        n += 1
+    return t, n
+
+
+def cpu_baseline(layers, M, R, ALPHA, wl, parts, min_s=10.0, max_passes=24):
+    """The oracle, untouched, on bounded samples of the benchmarked work,
+    each leg next to the GPU figure it compares with.
+
+    Headline (value): the training step of the 7B layer set -- for every
     linear, the first 2048 weight rows (output features) and all 2048 token
-    rows; oracle quantization (not timed, once), then oracle dequantization,
-    float64 forward and backward, timed over whole passes of the layer set
-    until at least min_s seconds have run (at most max_passes passes).
-    Scaled to the metric's unit with the sample's algorithmic flops."""
+    rows; oracle quantization (once, untimed), then oracle dequantization,
+    float64 forward and backward, timed over whole passes until at least
+    min_s seconds have run. Scaled to TFLOP/s with the sample's algorithmic
+    flops. The legs: quantization of the 11008x4096 decode weight (a row
+    sample), the one-token decode forward of the 4096x4096 weight (whole),
+    and a sample of the 65B layer set (extrapolated to its full step)."""
     import numpy as np
 
     import synth
     from oracle import linear as OL
     from oracle import nf4 as O
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    host, blas = cpu_threads()
     ms, ns = 2048, 2048
     sample = []
     for L in layers:
@@ -635,24 +837,93 @@ def cpu_baseline(layers, M, R, ALPHA, wl, min_s=10.0, max_passes=24):
                        L["dy"][:ms, :ns].float().cpu().numpy().astype(np.float64),
                        L["a"].float().cpu().numpy().astype(np.float64),
                        L["b"][:ns].float().cpu().numpy().astype(np.float64)))
-    flops = 0.0
-    t_total = 0.0
-    passes = 0
-    # whole passes over the layer set until at least min_s of oracle work
-    while passes < max_passes and (passes == 0 or t_total < min_s):
+    flops_pass = sum(fwd_flops(ms, ns, lay.k, R) + bwd_flops(ms, ns, lay.k, R) for lay, *_ in sample)
+
+    def train_pass():
         for lay, q, x, dy, a, b in sample:
-            t0 = time.perf_counter()
             _, bits = O.dequantize(q)
             w16 = O.bf16_bits_to_f32(bits).reshape(ns, lay.k)
             OL.linear_fwd(x, w16, a, b, ALPHA, R)
             OL.linear_bwd(x, w16, a, b, dy, ALPHA, R)
-            t_total += time.perf_counter() - t0
-            flops += fwd_flops(ms, ns, lay.k, R) + bwd_flops(ms, ns, lay.k, R)
-        passes += 1
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+
+    t_total, passes = timed_passes(train_pass, min_s, max_passes)
+    flops = flops_pass * passes
+    del sample
+    legs = {}
+
+    # quantize (double quant) of the 11008x4096 decode weight: 512 of its rows
+    lay_up = next(l for l in synth.DECODE_7B.layers if (l.n, l.k) == (11008, 4096))
+    wq = synth.weight(synth.DECODE_7B, lay_up)[:512].reshape(-1)
+    tq, nq = timed_passes(lambda: O.quantize(wq, True), 2.0, 8)
+    gpu_q = next((e for e in parts.get("quantize_dq", []) if (e["n"], e["k"]) == (11008, 4096)), None)
+    legs["quantize_11008x4096"] = {
+        "oracle_weights_per_s": wq.size * nq / tq, "sample": f"512 of 11008 rows ({wq.size} weights), {nq} pass(es)",
+        "gpu_weights_per_s": gpu_q["weights_per_s"] if gpu_q else None}
+
+    # one-token decode forward of the 4096x4096 weight with its adapter
+    # (r = 16): oracle dequantization + float64 matvec and LoRA, per call
+    lay_at = next(l for l in synth.DECODE_7B.layers if (l.n, l.k) == (4096, 4096))
+    q_at = O.quantize(synth.weight(synth.DECODE_7B, lay_at).reshape(-1), True)
+    x1 = synth.activations(synth.DECODE_7B, lay_at, 1).astype(np.float64)
+    a1 = synth.lora_a(synth.DECODE_7B, lay_at).astype(np.float64)
+    b1 = synth.lora_b(synth.DECODE_7B, lay_at).astype(np.float64)
+
+    def gemv_call():
+        _, bits = O.dequantize(q_at)
+        OL.linear_fwd(x1, O.bf16_bits_to_f32(bits).reshape(4096, 4096), a1, b1, 32.0, 16)
+
+    tg, ng = timed_passes(gemv_call, 2.0, 8)
+    gpu_g = next((e for e in parts.get("decode_gemv", []) if (e["n"], e["k"], e["m"]) == (4096, 4096, 1)), None)
+    legs["decode_gemv_4096x4096_m1"] = {
+        "oracle_us_per_call": tg / ng * 1e6, "sample": f"whole weight, {ng} call(s); quantization untimed",
+        "gpu_us_per_call": gpu_g["us_per_call"] if gpu_g else None}
+
+    # 65B layer set, sampled: q_proj (8192 x 8192) with 1024 of its weight
+    # rows; forward and dX on 64 token rows, dA and dB on all 4096; the rate
+    # is extrapolated to the full fwd+bwd step of the seven linears
+    wl5 = synth.LAYERS_65B
+    lay5 = wl5.layers[0]
+    n5, m5s = 1024, 64
+    tag = "cpu_sample_65b"
+    q5 = O.quantize(synth.student_t((n5, lay5.k), 4, 0.02, tag, "W").reshape(-1), True)
+    x5 = synth.normal((wl5.m, lay5.k), 1.0, tag, "X").astype(np.float64)
+    dy5 = synth.normal((wl5.m, n5), 1.0, tag, "dY").astype(np.float64)
+    a5 = synth.normal((wl5.r, lay5.k), 1.0 / wl5.r, tag, "A").astype(np.float64)
+    b5 = synth.normal((n5, wl5.r), 0.01, tag, "B").astype(np.float64)
+    s5 = OL.lora_scale(wl5.alpha, wl5.r)
+
+    def c5_pass():
+        _, bits = O.dequantize(q5)
+        w16 = O.bf16_bits_to_f32(bits).reshape(n5, lay5.k)
+        OL.linear_fwd(x5[:m5s], w16, a5, b5, wl5.alpha, wl5.r)
+        OL.linear_bwd(x5[:m5s], w16, a5, b5, dy5[:m5s], wl5.alpha, wl5.r)
+        h = x5 @ a5.T
+        dh = s5 * (dy5 @ b5)
+        _ = dh.T @ x5, s5 * (dy5.T @ h)
+
+    t5, n5p = timed_passes(c5_pass, 2.0, 8)
+    # flops of one pass: forward and backward on the sampled token rows, then
+    # H, dH, dA and dB on all token rows (dequantization counts none)
+    fl5 = (fwd_flops(m5s, n5, lay5.k, wl5.r) + bwd_flops(m5s, n5, lay5.k, wl5.r)
+           + 4 * wl5.m * wl5.r * lay5.k + 4 * wl5.m * n5 * wl5.r) * n5p
+    rate5 = fl5 / t5
+    step5 = sum(fwd_flops(wl5.m, lay.n, lay.k, wl5.r) + bwd_flops(wl5.m, lay.n, lay.k, wl5.r) for lay in wl5.layers)
+    gpu5 = parts.get("train_step_65b")
+    legs["train_step_65b"] = {
+        "oracle_tflops_on_sample": rate5 / 1e12,
+        "oracle_step_s_extrapolated": step5 / rate5,
+        "extrapolation": True,
+        "sample": f"q_proj, {n5} of 8192 weight rows; forward and dX on {m5s} of {wl5.m} token rows, dA and dB "
+                  f"on all {wl5.m}; {n5p} pass(es), {fl5 / 1e9:.1f} GFLOP in {t5:.2f} s; the full step's "
+                  f"{step5 / 1e12:.2f} TFLOP divided by the sample's rate",
+        "gpu_step_s": gpu5["ms_per_step"] * 1e-3 if gpu5 else None}
+
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(blas or host), "kind": "oracle",
+            "host_cpus": host, "blas_threads": blas,
             "sample": f"7B layer set: per linear the first {ns} weight rows and {ms} of {M} token rows; "
                       f"oracle dequantization + float64 forward and backward timed over {passes} pass(es) "
-                      f"({flops / 1e9:.2f} GFLOP in {t_total:.2f} s), oracle quantization untimed"}
+                      f"({flops / 1e9:.2f} GFLOP in {t_total:.2f} s), oracle quantization untimed",
+            "legs": legs}
 
 
 if __name__ == "__main__":
