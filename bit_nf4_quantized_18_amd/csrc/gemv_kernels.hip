@@ -187,7 +187,11 @@ __device__ __forceinline__ void static_for(F&& f) {
 // partial sums cross waves: the only barriers are the pair table's and H's.
 // H (fused, up to 32 slots) is one contiguous A row per wave, read in whole
 // 1 KB runs and dotted with X read from LDS in the same order.
-constexpr int kRowsX = 2 * 2 * 4096;  // X staging: up to 2 tokens x 4096 bf16
+// X is held in registers for k <= 4096 (two 2048-wide halves) and read from
+// LDS per row for k <= 12288 (six halves)
+constexpr int kHalvesReg = 2;
+constexpr int kHalvesLds = 6;
+constexpr int kRowsX = 2 * 2 * 2048 * kHalvesLds;  // X staging: up to 2 tokens x 12288 bf16
 constexpr int kRowsH = 2 * QLORA_MAX_RANK;  // H: up to 2 tokens x 128 slots
 constexpr int kRowsSmem = kTabBytes + kRowsX + 4 * kRowsH + 4 * kThreads;
 
@@ -208,31 +212,37 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   }
 }
 
-// Loads of one weight row for lane l (two 1 KB runs, the two scale codes or
-// absmax values, the row's two candidate group scales, B[row][l]).
+// Loads of one weight row for lane l (one 1 KB run per 2048-wide half, the
+// halves' scale codes or absmax values, the row's two candidate group scales,
+// B[row][l]).
+template <int kNH>
 struct RowLoads {
-  u32x4 c[2];
-  uint32_t s[2];  // scale code bytes (DQ) or absmax bits
-  u32x2 gs;       // group scales of (row nbk) >> 8 and the next (DQ)
-  uint32_t b;     // B[row][lane] for lane < rb
+  u32x4 c[kNH];
+  uint32_t s[kNH];  // scale code bytes (DQ) or absmax bits
+  u32x2 gs;         // group scales of (row nbk) >> 8 and the next (DQ)
+  uint32_t b;       // B[row][lane] for lane < rb
 };
 
-// six vector loads in every form: two code runs, two scale codes (or absmax
-// values), the group scales (a second B load without double quantization),
-// B; the prologue's explicit wait counts on it
-constexpr int kRowLoads = 6;
+// 2 kNH + 2 vector loads in every form: the code runs, the scale codes (or
+// absmax values), the group scales (a second B load without double
+// quantization), B; the prologue's explicit wait counts on it. Halves past
+// k read zeros from out-of-range offsets, so the count never changes.
+template <int kNH>
+constexpr int row_loads() {
+  return 2 * kNH + 2;
+}
 
-template <bool kDQ>
-__device__ __forceinline__ void load_row(RowLoads& L, const Rsrc& R, const GemvArgs& g, int row, int lane, int K,
+template <bool kDQ, int kNH>
+__device__ __forceinline__ void load_row(RowLoads<kNH>& L, const Rsrc& R, const GemvArgs& g, int row, int lane, int K,
                                          int nbk) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kNH; ++h) {
     const int k0 = 2048 * h + 32 * lane;
     const int off = k0 < K ? row * (K / 2) + (k0 >> 1) : R.codes_oob;
     L.c[h] = __builtin_amdgcn_raw_buffer_load_b128(R.codes, off, 0, 0);
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kNH; ++h) {
     const int blk = 32 * h + (lane >> 1);
     if (kDQ) {
       L.s[h] = __builtin_amdgcn_raw_buffer_load_b8(R.sc, blk < nbk ? row * nbk + blk : 0x7FFFFFF0, 0, 0);
@@ -248,9 +258,13 @@ __device__ __forceinline__ void load_row(RowLoads& L, const Rsrc& R, const GemvA
   L.b = __builtin_amdgcn_raw_buffer_load_b16(R.b, lane < g.rb ? 2 * (row * g.rb + lane) : R.b_oob, 0, 0);
 }
 
-template <bool kF16, bool kDQ, int kM, int kH, int kRPW>
+// kXL: k up to 12288, X read from LDS for every row (no fused H); otherwise
+// k up to 4096 with X in registers.
+template <bool kF16, bool kDQ, int kM, int kH, int kRPW, bool kXL>
 __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvArgs g) {
   static_assert(kM == 1 || kM == 2, "one or two tokens");
+  static_assert(!(kXL && kH == 1), "H is fused only with X in registers");
+  constexpr int kNH = kXL ? kHalvesLds : kHalvesReg;
   __shared__ __attribute__((aligned(16))) unsigned char smem[kRowsSmem];
   unsigned char* tab = smem;
   unsigned char* xst = smem + kTabBytes;
@@ -275,32 +289,32 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvArgs g) {
   // X into LDS in the order of the lanes' weights: copy t = (tok, h, c)
   // holds, for every lane l, the 8 values X[tok][2048 h + 32 l + 8 c ..], so
   // each later fragment read is one contiguous 1 KB (no bank conflicts).
-  // One copy per wave (at most 2 tokens x 2 halves x 4).
-  const int nh = K > 2048 ? 2 : 1;
+  // At most 2 tokens x 6 halves x 4 copies, up to three per wave.
+  const int nh = (K + 2047) >> 11;
   const int ncopy = kM * nh * 4;
-  if (wv < ncopy) {
-    const int tok = wv / (nh * 4), h = (wv >> 2) % nh, c = wv & 3;
+  for (int t = wv; t < ncopy; t += kWaves) {
+    const int tok = t / (nh * 4), h = (t >> 2) % nh, c = t & 3;
     const int kk = 2048 * h + 32 * lane + 8 * c;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.x, (lds_void*)(xst + wv * 1024), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.x, (lds_void*)(xst + t * 1024), 16,
                                              kk < K ? (tok * K + kk) * 2 : rs.x_oob, 0, 0, 0);
   }
   // the first rows' loads, so that HBM is busy while the table is built
   // (two ahead with the fused H, whose A row and X fragments need registers
   // while these rows are in flight; three otherwise)
-  constexpr int kAheadMax = kH == 1 ? 2 : 3;
+  constexpr int kAheadMax = (kH == 1 || kXL) ? 2 : 3;
   constexpr int kAhead = kRPW < kAheadMax ? kRPW : kAheadMax;
-  RowLoads rl[kRPW];
+  RowLoads<kNH> rl[kRPW];
   static_for<0, kAhead>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
     __builtin_amdgcn_sched_barrier(0);
-    load_row<kDQ>(rl[q], rs, g, row_of(q), lane, K, nbk);
+    load_row<kDQ, kNH>(rl[q], rs, g, row_of(q), lane, K, nbk);
     __builtin_amdgcn_sched_barrier(0);
   });
   build_pair_table<kF16>(tab, g.L, tid, wv);
   // this wave's X copy has landed (it was issued before the row loads: the
   // compiler does not track global -> LDS copies, so the count is explicit)
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<kAhead * kRowLoads>();
+  wait_vmcnt<kAhead * row_loads<kNH>()>();
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   // X staging offset of (tok, h, c) for lane l: ((tok nh + h) 4 + c) 1024 + 16 l
@@ -393,33 +407,36 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvArgs g) {
     __syncthreads();
   }
 
-  // X in registers, in the order of the lane's weights (zeros past K)
-  u32x4 xr[kM][2][4];
+  // X in registers (k <= 4096), in the order of the lane's weights (zeros
+  // past K); with kXL each row reads its fragments from LDS instead
+  u32x4 xr[kM][kHalvesReg][4];
+  if constexpr (!kXL) {
 #pragma unroll
-  for (int tok = 0; tok < kM; ++tok)
+    for (int tok = 0; tok < kM; ++tok)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < kHalvesReg; ++h)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        xr[tok][h][c] = h < nh ? *reinterpret_cast<const u32x4*>(xst + ((tok * nh + h) * 4 + c) * 1024 + 16 * lane)
-                               : u32x4{0, 0, 0, 0};
+        for (int c = 0; c < 4; ++c)
+          xr[tok][h][c] = h < nh ? *reinterpret_cast<const u32x4*>(xst + ((tok * nh + h) * 4 + c) * 1024 + 16 * lane)
+                                 : u32x4{0, 0, 0, 0};
+  }
   const int hstride = kH == 1 ? 32 : g.rh;
 
   static_for<0, kRPW>([&](auto qc) {
     constexpr int q = decltype(qc)::value;
     if constexpr (q >= 1 && q + kAhead - 1 < kRPW) {
       __builtin_amdgcn_sched_barrier(0);
-      load_row<kDQ>(rl[q + kAhead - 1], rs, g, row_of(q + kAhead - 1), lane, K, nbk);
+      load_row<kDQ, kNH>(rl[q + kAhead - 1], rs, g, row_of(q + kAhead - 1), lane, K, nbk);
       __builtin_amdgcn_sched_barrier(0);
     }
     const int row = row0 + wv + kWaves * q;
     if (row < N) {
-      const RowLoads& L = rl[q];
+      const RowLoads<kNH>& L = rl[q];
       float acc[kM];
 #pragma unroll
       for (int tok = 0; tok < kM; ++tok) acc[tok] = 0.0f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < kNH; ++h) {
         if (h < nh) {
           float p[kM];
 #pragma unroll
@@ -428,9 +445,12 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvArgs g) {
           for (int d = 0; d < 4; ++d) {
             const u32x4 wv4 = lookup8(tab, L.c[h][d], lane4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int tok = 0; tok < kM; ++tok) {
+              const u32x4 xv = kXL ? *reinterpret_cast<const u32x4*>(xst + ((tok * nh + h) * 4 + d) * 1024 + 16 * lane)
+                                   : xr[tok][h < kHalvesReg ? h : 0][d];
 #pragma unroll
-              for (int tok = 0; tok < kM; ++tok) p[tok] = dot2<kF16>(wv4[e], xr[tok][h][d][e], p[tok]);
+              for (int e = 0; e < 4; ++e) p[tok] = dot2<kF16>(wv4[e], xv[e], p[tok]);
+            }
           }
           const int blk = 32 * h + (lane >> 1);
           float sc;
@@ -483,9 +503,11 @@ int device_cus() {
 
 bool gemv_fuses_h(int64_t m, int64_t k, int r, const LoraParts* parts) {
   if (r <= 0) return false;
-  // 3 to 16 tokens, or k > 4096 (the matrix-core kernels of gemv_mfma.hip):
-  // up to 16 slots
-  if (m > 2 || k > 4096) return r <= 16;
+  // 3 to 16 tokens, or k > 12288 (the matrix-core kernels of
+  // gemv_mfma.hip): up to 16 slots
+  if (m > 2 || k > 2048 * kHalvesLds) return r <= 16;
+  // one or two tokens with X read from LDS per row: H from partial sums
+  if (k > 2048 * kHalvesReg) return false;
   const bool grouped = parts != nullptr && parts->g > 1;
   return grouped ? parts->rpart <= 16 : r <= 32;
 }
@@ -495,9 +517,14 @@ namespace {
 template <bool kF16, bool kDQ, int kM, int kRPW>
 void launch_rows_rpw(const GemvArgs& g, int kh, hipStream_t st) {
   const unsigned grid = static_cast<unsigned>((g.w.n + kWaves * kRPW - 1) / (kWaves * kRPW));
-  auto kern = kh == 0   ? gemv_rows_kernel<kF16, kDQ, kM, 0, kRPW>
-              : kh == 1 ? gemv_rows_kernel<kF16, kDQ, kM, 1, kRPW>
-                        : gemv_rows_kernel<kF16, kDQ, kM, 2, kRPW>;
+  if (g.w.k > 2048 * kHalvesReg) {  // H from partial sums here (kh is 0 or 2)
+    auto kern = kh == 0 ? gemv_rows_kernel<kF16, kDQ, kM, 0, kRPW, true> : gemv_rows_kernel<kF16, kDQ, kM, 2, kRPW, true>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, st, g);
+    return;
+  }
+  auto kern = kh == 0   ? gemv_rows_kernel<kF16, kDQ, kM, 0, kRPW, false>
+              : kh == 1 ? gemv_rows_kernel<kF16, kDQ, kM, 1, kRPW, false>
+                        : gemv_rows_kernel<kF16, kDQ, kM, 2, kRPW, false>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, st, g);
 }
 
@@ -537,7 +564,7 @@ hipError_t launch_gemv(const PackedW& w, const uint16_t* x, int64_t m, const uin
                        int hsplits, const uint16_t* b, int r, float s, uint16_t* y, float* h_out, hipStream_t st,
                        bool f16, const LoraParts* parts) {
   if (m < 1 || m > 16 || w.n % 16 != 0 || w.k % 64 != 0 || r < 0 || r > QLORA_MAX_RANK) return hipErrorInvalidValue;
-  if (m > 2 || w.k > 4096) return launch_gemv_mfma(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st, f16, parts);
+  if (m > 2 || w.k > 2048 * kHalvesLds) return launch_gemv_mfma(w, x, m, a, hpart, hsplits, b, r, s, y, h_out, st, f16, parts);
   GemvArgs g;
   g.w = w;
   g.x = x;

@@ -29,6 +29,8 @@ DECODE_CASES = [
     ("qkv_decode_r32_m7", 7, (256, 256, 256), 256, 32, 64.0),
     ("qkv_decode_r4_m3_k4608", 3, (256, 256, 512), 4608, 4, 8.0),
     ("qkv_decode_r7_m2", 2, (256, 512, 256), 320, 7, 14.0),  # g r = 21: split partials, padded to 32 slots
+    ("gateup_decode_m1_k6208", 1, (512, 256), 6208, 16, 32.0),    # one token, k > 4096: X from LDS, H partials
+    ("qkv_decode_m2_k8192", 2, (256, 256, 256), 8192, 8, 16.0),
 ]
 
 

@@ -32,6 +32,10 @@ FWD_BWD_CASES = [
     ("decode_long_k_m2", 2, 64, 16384, 16, 32.0, True),          # k > 4096 at two tokens: H from the skinny kernel
     ("decode_rank32_m1", 1, 160, 4096, 32, 64.0, True),          # one token, two fused H tiles, full k
     ("decode_rank20_m2_k2112", 2, 48, 2112, 20, 40.0, True),     # two tokens, ragged k past one 2048 half
+    ("decode_xl_m1_k11008_r16", 1, 96, 11008, 16, 32.0, True),   # k > 4096 at one token: X read from LDS per row
+    ("decode_xl_m2_k4160_r8", 2, 64, 4160, 8, 16.0, True),       # ragged third half
+    ("decode_xl_m2_k12288_r0", 2, 48, 12288, 0, 0.0, True),      # the largest k of that form, base only
+    ("decode_xl_m1_k6144_r40_nodq", 1, 80, 6144, 40, 80.0, False),
 ]
 
 
