@@ -15,11 +15,12 @@ from oracle import linear as OL
 pytestmark = pytest.mark.gpu
 
 # (name, m, n, k, r, alpha): matmul path with a large scratch use first, then
-# a smaller matmul-path call, then a decode call whose H partial sums live in
-# the scratch array (r > 16)
+# a smaller matmul-path call, then decode calls whose H partial sums live in
+# the scratch array (r > 16; one token at k > 4096)
 CASES = [
     ("noalloc_m300_n272_k320_r16", 300, 272, 320, 16, 32.0),
     ("noalloc_m40_n128_k256_r24", 40, 128, 256, 24, 48.0),
+    ("noalloc_decode_m1_n96_k6144_r16", 1, 96, 6144, 16, 32.0),
     ("noalloc_decode_m8_n128_k256_r24", 8, 128, 256, 24, 48.0),
 ]
 
