@@ -121,9 +121,16 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     // ======================= producers =======================
     const int pt = tid - 256;
     const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
-    // W: forward -> weight row p0 + pt/2, k-half pt%2 of the step;
-    //    backward -> weight row q0 + pt%64, k-quarter pt/64 of the output tile
-    const int w_r = kTransW ? (pt & 63) : (pt >> 1);
+    // W: forward -> k-half lane%2 of one of the wave's 32 weight rows;
+    //    backward -> weight row q0 + pt%64, k-quarter pt/64 of the output tile.
+    // The LDS write path takes 8 lanes of a 16-byte store per cycle over a
+    // 128-byte span of banks, and tile rows 2i and 2i+1 share a swizzle key.
+    // Forward, lanes 8g..8g+7 therefore take rows of four different keys,
+    // g%2 + 2(q + 4((g/2)%2)) + 16(g/4) with q = (lane/2)%4, so their stores
+    // fall on 8 distinct 16-byte bank groups (with rows pt/2 every store
+    // instruction took two passes).
+    const int fwd_row = ((lane >> 3) & 1) + 2 * (((lane >> 1) & 3) + 4 * ((lane >> 4) & 1)) + 16 * (lane >> 5);
+    const int w_r = kTransW ? (pt & 63) : pw * 32 + fwd_row;
     const int w_c = kTransW ? (pt >> 6) * 32 : (pt & 1) * 32;
     // A resource: this tile's rows only (rows past M read as zeros)
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A + m0 * Qn, (M - m0 < kBM ? M - m0 : kBM) * Qn * 2);
