@@ -75,6 +75,25 @@ __device__ __forceinline__ u32x2 ld_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Forward: lanes 2i and 2i+1 unpack the two halves of one 64-weight block and
+// so share its table. Each converts only the level pairs 2q + h (h = lane % 2,
+// q = 0..3; lv holds its 8 levels) and takes the other four from its
+// neighbour by a DPP swap; sel_l / sel_h order the two sources per lane so
+// that every lane ends with make_block_lut's table.
+template <bool kF16>
+__device__ __forceinline__ BlockLut make_block_lut_pair(const float (&lv)[8], float s, uint32_t sel_l, uint32_t sel_h) {
+  BlockLut t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t own = cvt_16x2<kF16>(lv[2 * q] * s, lv[2 * q + 1] * s);
+    // quad_perm [1, 0, 3, 2]: the value of lane l ^ 1
+    const uint32_t oth = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(own), 0xB1, 0xF, 0xF, true));
+    t.tl[q] = byte_perm(oth, own, sel_l);
+    t.th[q] = byte_perm(oth, own, sel_h);
+  }
+  return t;
+}
+
 template <bool kTransW, bool kDQ, bool kF16>
 __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t* __restrict__ A, int64_t M,
                                                        int64_t P, int64_t Qn, const uint16_t* __restrict__ ep_a,
@@ -132,6 +151,18 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     const int fwd_row = ((lane >> 3) & 1) + 2 * (((lane >> 1) & 3) + 4 * ((lane >> 4) & 1)) + 16 * (lane >> 5);
     const int w_r = kTransW ? (pt & 63) : pw * 32 + fwd_row;
     const int w_c = kTransW ? (pt >> 6) * 32 : (pt & 1) * 32;
+    // forward table halves: lane h = lane % 2 converts the level pairs 2q + h;
+    // its own pair is the low source of the byte permutes for h = 0, the high
+    // one for h = 1
+    const int hp = lane & 1;
+    float lv[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lv[2 * q] = hp ? L.v[4 * q + 2] : L.v[4 * q];
+      lv[2 * q + 1] = hp ? L.v[4 * q + 3] : L.v[4 * q + 1];
+    }
+    const uint32_t sel_l = hp ? 0x02000604u : 0x06040200u;
+    const uint32_t sel_h = hp ? 0x03010705u : 0x07050301u;
     // A resource: this tile's rows only (rows past M read as zeros)
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(A + m0 * Qn, (M - m0 < kBM ? M - m0 : kBM) * Qn * 2);
     const __amdgpu_buffer_rsrc_t crsrc = make_rsrc(w.codes, w.n * K / 2);
@@ -183,7 +214,8 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     };
     auto store_w = [&](int kt, u32x4 c, uint32_t sc, float gs) {
       const float s = kDQ ? dq_unit(sc, w.dq) * gs : gs;
-      const BlockLut lut = make_block_lut<kF16>(L.v, wk_ok ? s : 0.0f);
+      const BlockLut lut = kTransW ? make_block_lut<kF16>(L.v, wk_ok ? s : 0.0f)
+                                   : make_block_lut_pair<kF16>(lv, s, sel_l, sel_h);
       uint16_t* bs = Bs + (kt % kStages) * kBStage;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {

@@ -196,14 +196,26 @@ __host__ __device__ __forceinline__ void lut8_decode_order(const BlockLut& t, ui
   out[3] = byte_perm(ho, lo, 0x07030602u);
 }
 
-// Same lookup, natural order: (e0,e1), (e2,e3), (e4,e5), (e6,e7).
+// Same lookup, natural order: (e0,e1), (e2,e3), (e4,e5), (e6,e7). The
+// nibbles are first spread into selector bytes in element order (bytes i and
+// i + 1 of c interleaved with those of c >> 4, low nibble of each byte taken),
+// so the pairs come out without a second reordering pass: 27 operations per
+// 8 weights against 29 for the decode-order lookup plus 4 byte permutes.
 __host__ __device__ __forceinline__ void lut8_natural_order(const BlockLut& t, uint32_t c, uint32_t out[4]) {
-  uint32_t d[4];
-  lut8_decode_order(t, c, d);
-  out[0] = byte_perm(d[2], d[0], 0x05040100u);
-  out[1] = byte_perm(d[2], d[0], 0x07060302u);
-  out[2] = byte_perm(d[3], d[1], 0x05040100u);
-  out[3] = byte_perm(d[3], d[1], 0x07060302u);
+  const uint32_t c4 = c >> 4;
+  const uint32_t n0 = byte_perm(c4, c, 0x05010400u);  // e0 e1 e2 e3 in the low nibbles
+  const uint32_t n1 = byte_perm(c4, c, 0x07030602u);  // e4 e5 e6 e7
+  const uint32_t s0 = (n0 & 0x0F0F0F0Fu) | ((n0 << 1) & 0x10101010u);
+  const uint32_t s1 = (n1 & 0x0F0F0F0Fu) | ((n1 << 1) & 0x10101010u);
+  const uint32_t s0b = s0 ^ 0x18181818u, s1b = s1 ^ 0x18181818u;
+  const uint32_t l0 = byte_perm(t.tl[1], t.tl[0], s0) & byte_perm(t.tl[3], t.tl[2], s0b);
+  const uint32_t h0 = byte_perm(t.th[1], t.th[0], s0) & byte_perm(t.th[3], t.th[2], s0b);
+  const uint32_t l1 = byte_perm(t.tl[1], t.tl[0], s1) & byte_perm(t.tl[3], t.tl[2], s1b);
+  const uint32_t h1 = byte_perm(t.th[1], t.th[0], s1) & byte_perm(t.th[3], t.th[2], s1b);
+  out[0] = byte_perm(h0, l0, 0x05010400u);
+  out[1] = byte_perm(h0, l0, 0x07030602u);
+  out[2] = byte_perm(h1, l1, 0x05010400u);
+  out[3] = byte_perm(h1, l1, 0x07030602u);
 }
 
 // Decode order of 8 consecutive bf16 values held as 4 dwords (x0x1, x2x3,
