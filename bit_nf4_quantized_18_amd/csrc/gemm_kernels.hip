@@ -75,11 +75,11 @@ __device__ __forceinline__ u32x2 ld_tr4(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Forward: lanes 2i and 2i+1 unpack the two halves of one 64-weight block and
-// so share its table. Each converts only the level pairs 2q + h (h = lane % 2,
-// q = 0..3; lv holds its 8 levels) and takes the other four from its
-// neighbour by a DPP swap; sel_l / sel_h order the two sources per lane so
-// that every lane ends with make_block_lut's table.
+// Lanes 2i and 2i+1 of a producer wave unpack the two halves of one 64-weight
+// block and so share its table. Each converts only the level pairs 2q + h
+// (h = lane % 2, q = 0..3; lv holds its 8 levels) and takes the other four
+// from its neighbour by a DPP swap; sel_l / sel_h order the two sources per
+// lane so that every lane ends with make_block_lut's table.
 template <bool kF16>
 __device__ __forceinline__ BlockLut make_block_lut_pair(const float (&lv)[8], float s, uint32_t sel_l, uint32_t sel_h) {
   BlockLut t;
@@ -141,7 +141,9 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     const int pt = tid - 256;
     const int pw = __builtin_amdgcn_readfirstlane(wave - 4);
     // W: forward -> k-half lane%2 of one of the wave's 32 weight rows;
-    //    backward -> weight row q0 + pt%64, k-quarter pt/64 of the output tile.
+    //    backward -> weight row q0 + 32 (pw/2) + lane/2, k-quarter
+    //    2 (pw%2) + lane%2 of the output tile.
+    // Either way lanes 2i and 2i+1 hold the two halves of one 64-weight block.
     // The LDS write path takes 8 lanes of a 16-byte store per cycle over a
     // 128-byte span of banks, and tile rows 2i and 2i+1 share a swizzle key.
     // Forward, lanes 8g..8g+7 therefore take rows of four different keys,
@@ -149,11 +151,11 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     // fall on 8 distinct 16-byte bank groups (with rows pt/2 every store
     // instruction took two passes).
     const int fwd_row = ((lane >> 3) & 1) + 2 * (((lane >> 1) & 3) + 4 * ((lane >> 4) & 1)) + 16 * (lane >> 5);
-    const int w_r = kTransW ? (pt & 63) : pw * 32 + fwd_row;
-    const int w_c = kTransW ? (pt >> 6) * 32 : (pt & 1) * 32;
-    // forward table halves: lane h = lane % 2 converts the level pairs 2q + h;
-    // its own pair is the low source of the byte permutes for h = 0, the high
-    // one for h = 1
+    const int w_r = kTransW ? (pw >> 1) * 32 + (lane >> 1) : pw * 32 + fwd_row;
+    const int w_c = kTransW ? (2 * (pw & 1) + (lane & 1)) * 32 : (pt & 1) * 32;
+    // table halves: lane h = lane % 2 converts the level pairs 2q + h; its own
+    // pair is the low source of the byte permutes for h = 0, the high one for
+    // h = 1
     const int hp = lane & 1;
     float lv[8];
 #pragma unroll
@@ -214,8 +216,9 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     };
     auto store_w = [&](int kt, u32x4 c, uint32_t sc, float gs) {
       const float s = kDQ ? dq_unit(sc, w.dq) * gs : gs;
-      const BlockLut lut = kTransW ? make_block_lut<kF16>(L.v, wk_ok ? s : 0.0f)
-                                   : make_block_lut_pair<kF16>(lv, s, sel_l, sel_h);
+      // (backward: both halves of a block lie on the same side of K; the
+      // forward's blocks are all inside it)
+      const BlockLut lut = make_block_lut_pair<kF16>(lv, kTransW && !wk_ok ? 0.0f : s, sel_l, sel_h);
       uint16_t* bs = Bs + (kt % kStages) * kBStage;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
