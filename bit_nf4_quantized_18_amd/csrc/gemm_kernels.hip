@@ -43,6 +43,8 @@
 // rows in that XCD's L2. The rank-r LoRA term is one more pass of MFMAs.
 // kF16 builds the same kernel for IEEE-half compute: half lookup tables, the
 // f16 MFMA and a half output; everything else is bit-pattern movement.
+#include <type_traits>
+
 #include "bufmem.h"
 #include "internal.h"
 #include "mfma.h"
@@ -192,12 +194,16 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     const int s_step = kTransW ? static_cast<int>(kBQ * nbk) : 1;
     const bool wk_ok = wk0 < K;  // backward: the output tile may pass K
 
-    u32x4 rc[2];     // codes ring (2 stages)
-    uint32_t rs[2];  // scale code ring (double quant)
-    float rg[2];     // group max (double quant) or absmax ring
+    // code ring, one slot per LDS stage: stage s's codes are held in slot
+    // s % 3 from two steps before its unpack until it
+    u32x4 rc[kStages];
+    uint32_t rs[kStages];  // scale codes (double quant)
+    float rg[kStages];     // group maxima (double quant) or absmax values
 
-    auto dma_a = [&](int kt) {
-      uint16_t* as = As + (kt % kStages) * kAStage + pw * (8 * 512);
+    // st = kt % kStages, a constant in every call below (the step loop
+    // advances three steps at a time), so the LDS addresses fold
+    auto dma_a = [&](int kt, int st) {
+      uint16_t* as = As + st * kAStage + pw * (8 * 512);
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, (lds_void*)(as + u * 512), 16,
@@ -208,18 +214,19 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
       const int soff = s_voff + kt * s_step;
       if (kDQ) {
         sc = __builtin_amdgcn_raw_buffer_load_b8(srsrc, soff, 0, 0);
-        gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grsrc, (soff / kGroup) * 4, 0, 0));
+        gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           grsrc, static_cast<int>((static_cast<uint32_t>(soff) / kGroup) * 4), 0, 0));
       } else {
         sc = 0;
         gs = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff * 4, 0, 0));
       }
     };
-    auto store_w = [&](int kt, u32x4 c, uint32_t sc, float gs) {
+    auto store_w = [&](int st, u32x4 c, uint32_t sc, float gs) {
       const float s = kDQ ? dq_unit(sc, w.dq) * gs : gs;
       // (backward: both halves of a block lie on the same side of K; the
       // forward's blocks are all inside it)
       const BlockLut lut = make_block_lut_pair<kF16>(lv, kTransW && !wk_ok ? 0.0f : s, sel_l, sel_h);
-      uint16_t* bs = Bs + (kt % kStages) * kBStage;
+      uint16_t* bs = Bs + st * kBStage;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t wv[4];
@@ -239,14 +246,14 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
 
     // prologue: A of stages 0 and 1 and unpacked W of stages 0 and 1 in LDS;
     // codes of stage 2 loaded, of stage 3 in flight
-    dma_a(0);
-    dma_a(1);
+    dma_a(0, 0);
+    dma_a(1, 1);
     load_w(0, rc[0], rs[0], rg[0]);
     load_w(1, rc[1], rs[1], rg[1]);
     store_w(0, rc[0], rs[0], rg[0]);
-    load_w(2, rc[0], rs[0], rg[0]);
+    load_w(2, rc[2], rs[2], rg[2]);
     store_w(1, rc[1], rs[1], rg[1]);
-    load_w(3, rc[1], rs[1], rg[1]);
+    load_w(3, rc[0], rs[0], rg[0]);
     // same state at the loop head from here and from the loop's back edge:
     // only the codes of the next stage outstanding
     __builtin_amdgcn_sched_barrier(0);
@@ -259,18 +266,25 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
     // the end the stages past the last one are filled too, from zeros (reads
     // outside the buffer resources) or from unused in-range bytes, into LDS
     // slots that are read neither now nor later.
-    auto step = [&](int kt, int cs) {
-      dma_a(kt + 2);
-      store_w(kt + 2, rc[cs], rs[cs], rg[cs]);
-      load_w(kt + 4, rc[cs], rs[cs], rg[cs]);
+    // S = kt % 3: stage kt + 2 is unpacked from slot (S + 2) % 3, and the
+    // codes of stage kt + 4 go to slot (S + 1) % 3, whose stage kt + 1 was
+    // unpacked in the previous step.
+    auto step = [&](int kt, auto s_c) {
+      constexpr int S = decltype(s_c)::value;
+      constexpr int st = (S + 2) % kStages, nx = (S + 1) % kStages;
+      dma_a(kt + 2, st);
+      store_w(st, rc[st], rs[st], rg[st]);
+      load_w(kt + 4, rc[nx], rs[nx], rg[nx]);
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<kWLoads>();
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     };
-    for (int kt = 0; kt < nk; kt += 2) {
-      step(kt, 0);
-      if (kt + 1 < nk) step(kt + 1, 1);
+    static_assert(kStages == 3, "the step loop advances one ring turn at a time");
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+      if (kt + 2 < nk) step(kt + 2, std::integral_constant<int, 2>{});
     }
     // no load may still be writing LDS when the wave ends
     wait_vmcnt<0>();
@@ -306,20 +320,22 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   // two register sets of fragments: while the MFMAs of one half-step run,
   // the other set is filled from LDS
   u32x4 fa0[8], fb0[4], fa1[8], fb1[4];
-  auto read = [&](int kt, int half, u32x4(&xa)[8], u32x4(&xb)[4]) {
+  // st = kt % kStages, a constant in every call (the loop below advances
+  // three steps at a time)
+  auto read = [&](int st, int half, u32x4(&xa)[8], u32x4(&xb)[4]) {
     const int col = half ? col1 : col0;
-    const uint16_t* as = As + (kt % kStages) * kAStage + arow + col;
+    const uint16_t* as = As + st * kAStage + arow + col;
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) xa[mt] = ld16(as + 16 * mt * kBQ);
     if (kTransW) {
-      const uint16_t* bs = Bs + (kt % kStages) * kBStage + half * (32 * kBP);
+      const uint16_t* bs = Bs + st * kBStage + half * (32 * kBP);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const u32x2 lo = ld_tr4(bs + toff[nt]), hi = ld_tr4(bs + toff[nt] + 4 * kBP);
         xb[nt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
     } else {
-      const uint16_t* bs = Bs + (kt % kStages) * kBStage + brow + col;
+      const uint16_t* bs = Bs + st * kBStage + brow + col;
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) xb[nt] = ld16(bs + 16 * nt * kBQ);
     }
@@ -331,14 +347,20 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
       for (int mt = 0; mt < 8; ++mt) acc[nt][mt] = mma16<kF16>(xb[nt], xa[mt], acc[nt][mt]);
   };
 
+  auto cstep = [&](int kt, auto s_c) {
+    constexpr int S = decltype(s_c)::value;  // kt % 3
+    read(S, 1, fa1, fb1);                                       // second half of this step
+    mma(fa0, fb0);                                              // first half
+    if (kt + 1 < nk) read((S + 1) % kStages, 0, fa0, fb0);      // next step, written two steps ago
+    mma(fa1, fb1);                                              // second half
+    __syncthreads();
+  };
   __syncthreads();
   read(0, 0, fa0, fb0);
-  for (int kt = 0; kt < nk; ++kt) {
-    read(kt, 1, fa1, fb1);                              // second half of this step
-    mma(fa0, fb0);                                      // first half
-    if (kt + 1 < nk) read(kt + 1, 0, fa0, fb0);         // next step, written two steps ago
-    mma(fa1, fb1);                                      // second half
-    __syncthreads();
+  for (int kt = 0; kt < nk; kt += 3) {
+    cstep(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) cstep(kt + 1, std::integral_constant<int, 1>{});
+    if (kt + 2 < nk) cstep(kt + 2, std::integral_constant<int, 2>{});
   }
 
   // LoRA term: rpad more contraction slots, operands straight from global memory.
