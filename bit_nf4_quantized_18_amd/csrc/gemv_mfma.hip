@@ -156,8 +156,8 @@ __global__ __launch_bounds__(WAVES * 64) void gemv_kernel(PackedW w, const uint1
     if (has_slice) copy_slice(xrsrc, M, base);
     __builtin_amdgcn_sched_barrier(0);
     const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_c * 32));
-    const u32x4 c0 = __builtin_nontemporal_load(cp);
-    const u32x4 c1 = __builtin_nontemporal_load(cp + 1);
+    const u32x4 c0 = cp[0];
+    const u32x4 c1 = cp[1];
     const int bi = n_c * nbk + kb_c;
     uint8_t scode = 0;
     float gsc;
@@ -328,8 +328,8 @@ __global__ __launch_bounds__(1024) void gemv_persistent_kernel(PackedW w, const 
     const int n_c = real ? (n < N ? n : N - 1) : 0;
     const int kb_r = real ? kb_c : 0;
     const u32x4* cp = reinterpret_cast<const u32x4*>(w.codes + (n_c * (K / 2) + kb_r * 32));
-    T.c0 = __builtin_nontemporal_load(cp);
-    T.c1 = __builtin_nontemporal_load(cp + (real ? 1 : 0));
+    T.c0 = cp[0];
+    T.c1 = cp[real ? 1 : 0];
     const int bi = n_c * nbk + kb_r;
     if (kDQ) {
       T.scode = w.scale_codes[bi];

@@ -92,7 +92,8 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(const float* __
 
   // Vector loads are unconditional from clamped addresses (a guarded load
   // makes the compiler wait for all outstanding loads); only the lanes that
-  // straddle the end of the array redo theirs with element loads.
+  // straddle the end of the array redo theirs with element loads. Plain
+  // loads: with the nontemporal hint the kernel ran 4-7% slower.
   float v[kQSteps][8];
   const int64_t last8 = numel >= 8 ? numel - 8 : 0;
 #pragma unroll
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(const float* __
     const int64_t e0 = b * kBlock + part * 8;
     if (numel >= 8) {
       const f32x4* p = reinterpret_cast<const f32x4*>(w + (e0 < last8 ? e0 : (last8 & ~INT64_C(3))));
-      const f32x4 a = __builtin_nontemporal_load(p);
-      const f32x4 c = __builtin_nontemporal_load(p + 1);
+      const f32x4 a = p[0];
+      const f32x4 c = p[1];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v[it][j] = a[j];
