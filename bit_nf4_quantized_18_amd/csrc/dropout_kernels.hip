@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void mask_input_kernel(const uint16_t* __restr
                                                          uint16_t* __restrict__ xm) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < count8; i += stride) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x) + i);
-    const u32x2 kb = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(keep) + i);
+    const u32x4 v = reinterpret_cast<const u32x4*>(x)[i];
+    const u32x2 kb = reinterpret_cast<const u32x2*>(keep)[i];
     const u32x4 o = {v[0] & keep_halves(kb[0], 0), v[1] & keep_halves(kb[0], 1), v[2] & keep_halves(kb[1], 0),
                      v[3] & keep_halves(kb[1], 1)};
     reinterpret_cast<u32x4*>(xm)[i] = o;
