@@ -64,10 +64,16 @@ constexpr int kBStage = kBP * kBQ;
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kBQ + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 // Backward weight tile: 64 contraction rows n x 128 output columns, the
-// weight's own orientation. Chunk c of row n is stored at c ^ swz_t_key(n):
-// the transposed fragment reads below then hit every bank once per 32 lanes.
+// weight's own orientation. Chunk c of row n is stored at
+// (c ^ ((c >> 2) & 1)) ^ swz_t_key(n): the transposed fragment reads below
+// then hit every bank once per 32 lanes, and the producers' 16-byte stores
+// (lanes 2i, 2i+1 writing chunk j of quarters 2b, 2b+1 of one row) fall on 8
+// distinct 16-byte bank groups per 8 lanes: the odd quarter's chunks are
+// swapped in pairs.
 __device__ __forceinline__ int swz_t_key(int n) { return 2 * (n & 3) + 8 * ((n >> 3) & 1); }
-__device__ __forceinline__ int swz_t(int n, int chunk) { return n * kBP + ((chunk ^ swz_t_key(n)) << 3); }
+__device__ __forceinline__ int swz_t(int n, int chunk) {
+  return n * kBP + (((chunk ^ ((chunk >> 2) & 1)) ^ swz_t_key(n)) << 3);
+}
 
 // ds_read_b64_tr_b16: in each group of 16 lanes, lane 4p + e receives element
 // e of the 8-byte rows addressed by lanes p, p + 4, p + 8 and p + 12.
@@ -301,14 +307,17 @@ __global__ __launch_bounds__(512) void nf4_gemm_kernel(PackedW w, const uint16_t
   // backward: the first operand of the MFMA is column k0 + i of the [n][k]
   // tile, contraction slots n = 32 half + 8g + e'. Lane 16g + 4t + p supplies
   // the address of row 32 half + 8g + t (then + 4) at columns k0 + 4p .. +3
-  // (k0 = 64 wp + 16 nt): with swz_t_key(n) = 2t + 8 (g & 1), the stored chunk
-  // is (p / 2) | ((nt ^ t) << 1) | ((wp ^ (g & 1)) << 3).
+  // (k0 = 64 wp + 16 nt): logical chunk 8 wp + 2 nt + p / 2, in quarter
+  // 2 wp + nt / 2; with swz_t_key(n) = 2t + 8 (g & 1) (and the odd quarters'
+  // pair swap) the stored chunk is
+  // ((p / 2) ^ (nt / 2)) | ((nt ^ t) << 1) | ((wp ^ (g & 1)) << 3).
   int toff[4] = {0, 0, 0, 0};
   if (kTransW) {
     const int tp = i & 3, tt = i >> 2;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
-      toff[nt] = (8 * g + tt) * kBP + 8 * ((tp >> 1) | ((nt ^ tt) << 1) | ((wp ^ (g & 1)) << 3)) + 4 * (tp & 1);
+      toff[nt] = (8 * g + tt) * kBP + 8 * (((tp >> 1) ^ (nt >> 1)) | ((nt ^ tt) << 1) | ((wp ^ (g & 1)) << 3)) +
+                 4 * (tp & 1);
   }
 
   f32x4 acc[4][8];  // [weight tile nt][token tile mt]: acc = W x^T tile
