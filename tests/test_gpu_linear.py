@@ -36,6 +36,12 @@ FWD_BWD_CASES = [
     ("decode_xl_m2_k4160_r8", 2, 64, 4160, 8, 16.0, True),       # ragged third half
     ("decode_xl_m2_k12288_r0", 2, 48, 12288, 0, 0.0, True),      # the largest k of that form, base only
     ("decode_xl_m1_k6144_r40_nodq", 1, 80, 6144, 40, 80.0, False),
+    # several GEMM tiles with ragged tails in m and n, and every remainder of
+    # the k-step count modulo the three-stage ring, forward (k / 64 steps)
+    # and dX (n / 64 steps)
+    ("gemm_ragged_m300_n400_k1024_r16", 300, 400, 1024, 16, 32.0, True),        # 16 and 7 steps
+    ("gemm_ragged_m520_n272_k1088_r24_nodq", 520, 272, 1088, 24, 48.0, False),  # 17 and 5 steps
+    ("gemm_ragged_m257_n1040_k960_r8", 257, 1040, 960, 8, 16.0, True),          # 15 and 17 steps
 ]
 
 
