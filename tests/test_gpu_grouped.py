@@ -16,6 +16,7 @@ CASES = [
     ("gateup_m17", 17, (512, 256), 192, 16, 16.0),             # smallest m on the GEMM path
     ("qkv_r32", 64, (256, 256, 256), 256, 32, 64.0),           # g r = 96: the general projection
     ("four_parts_m40", 40, (256, 256, 256, 256), 128, 16, 32.0),
+    ("qkv_m260_k1088", 260, (256, 512, 512), 1088, 16, 32.0),  # 17 forward and 20 dX steps, ragged m
 ]
 
 # Decode sizes (m <= 16, the GEMV): H in the kernel when g r <= 16, else from
