@@ -183,7 +183,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 // and the products are 2-wide dot products (v_dot2_f32_bf16) with X held in
 // registers in the same order; per half block the float32 sum is multiplied
 // by the block scale. The LoRA-up term enters as lane j's share s H[j] B[row][j]
-// (j < rb), and one butterfly sum over the 64 lanes gives the output. No
+// (j < rb), and one wave sum (DPP, then the four row sums) gives the output. No
 // partial sums cross waves: the only barriers are the pair table's and H's.
 // H (fused, up to 32 slots) is one contiguous A row per wave, read in whole
 // 1 KB runs and dotted with X read from LDS in the same order.
@@ -195,10 +195,26 @@ constexpr int kRowsX = 2 * 2 * 2048 * kHalvesLds;  // X staging: up to 2 tokens 
 constexpr int kRowsH = 2 * QLORA_MAX_RANK;  // H: up to 2 tokens x 128 slots
 constexpr int kRowsSmem = kTabBytes + kRowsX + 4 * kRowsH + 4 * kThreads;
 
+// v + (v moved across lanes by the DPP control kCtrl)
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false);
+  return v + __builtin_bit_cast(float, s);
+}
+
+// Sum over the 64 lanes, returned in every lane: quad sums and 16-lane row
+// sums by DPP (no LDS round trip), then the four row sums read as scalars.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v = dpp_add<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = dpp_add<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = dpp_add<0x124>(v);  // row_ror 4
+  v = dpp_add<0x128>(v);  // row_ror 8
+  const int bits = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(bits, 48));
+  return (r0 + r1) + (r2 + r3);
 }
 
 template <bool kF16>
@@ -298,10 +314,10 @@ __global__ __launch_bounds__(kThreads) void gemv_rows_kernel(GemvArgs g) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs.x, (lds_void*)(xst + t * 1024), 16,
                                              kk < K ? (tok * K + kk) * 2 : rs.x_oob, 0, 0, 0);
   }
-  // the first rows' loads, so that HBM is busy while the table is built
-  // (two ahead with the fused H, whose A row and X fragments need registers
-  // while these rows are in flight; three otherwise)
-  constexpr int kAheadMax = (kH == 1 || kXL) ? 2 : 3;
+  // the first rows' loads, so that HBM is busy while the table is built;
+  // two rows ahead per wave (three or more in flight made every shape
+  // slower, one made the multi-row shapes slower)
+  constexpr int kAheadMax = 2;
   constexpr int kAhead = kRPW < kAheadMax ? kRPW : kAheadMax;
   RowLoads<kNH> rl[kRPW];
   static_for<0, kAhead>([&](auto qc) {
