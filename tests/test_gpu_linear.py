@@ -29,7 +29,7 @@ FWD_BWD_CASES = [
     ("decode_rank5_m2", 2, 96, 192, 5, 10.0, True),              # H inside the GEMV, ragged rank
     ("decode_k8192_r4_m5", 5, 48, 8192, 4, 8.0, True),           # H inside the GEMV, two passes over k
     ("decode_rank24_m8", 8, 128, 256, 24, 48.0, True),           # r > 16: H from the skinny kernel
-    ("decode_long_k_m2", 2, 64, 16384, 16, 32.0, True),          # k > 4096 at two tokens: H from the skinny kernel
+    ("decode_long_k_m2", 2, 64, 16384, 16, 32.0, True),          # k > 12288 at two tokens: the matrix-core multi-pass GEMV, H fused
     ("decode_rank32_m1", 1, 160, 4096, 32, 64.0, True),          # one token, two fused H tiles, full k
     ("decode_rank20_m2_k2112", 2, 48, 2112, 20, 40.0, True),     # two tokens, ragged k past one 2048 half
     ("decode_xl_m1_k11008_r16", 1, 96, 11008, 16, 32.0, True),   # k > 4096 at one token: X read from LDS per row
