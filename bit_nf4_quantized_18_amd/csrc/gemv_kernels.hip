@@ -1,5 +1,5 @@
-// Decode path, one or two tokens and k <= 4096: Y = X W16^T + s H B^T with
-// W read straight from its packed NF4 form (3 to 16 tokens, and k > 4096:
+// Decode path, one or two tokens and k <= 12288: Y = X W16^T + s H B^T with
+// W read straight from its packed NF4 form (3 to 16 tokens, and k > 12288:
 // gemv_mfma.hip).
 //
 // Ultralytics glossary "QLoRA", section "Come funziona QLoRA": each frozen

@@ -1,6 +1,6 @@
-// Decode path, 3 to 16 tokens (any k) and one or two tokens at k > 4096:
+// Decode path, 3 to 16 tokens (any k) and one or two tokens at k > 12288:
 // Y = X W16^T + s H B^T with W read straight from its packed NF4 form, in one
-// launch (one or two tokens at k <= 4096 take the row-per-wave kernel of
+// launch (one or two tokens at k <= 12288 take the row-per-wave kernel of
 // gemv_kernels.hip).
 //
 // Ultralytics glossary "QLoRA", section "Come funziona QLoRA": each frozen

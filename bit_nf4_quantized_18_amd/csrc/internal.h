@@ -104,9 +104,9 @@ struct LoraParts {
 // from launch_skinny_decode). r = 0: base only. h_out (m x r, may be null)
 // receives H. Grouped weights (parts != null): r = g rpart slots of H (a is
 // r x k), b is n x rpart and row p of part l takes H's slots l rpart ..
-// (l+1) rpart - 1. H is fused for 3..16 tokens or k > 4096 when r <= 16;
+// (l+1) rpart - 1. H is fused for 3..16 tokens, or k > 12288, when r <= 16;
 // for one or two tokens at k <= 4096 when r <= 32 (one part) or rpart <= 16
-// (grouped).
+// (grouped); never for one or two tokens at 4096 < k <= 12288.
 // A call with parts fuses whenever the same call without them would.
 bool gemv_fuses_h(int64_t m, int64_t k, int r, const LoraParts* parts);
 int device_cus();

@@ -32,6 +32,8 @@ DECODE_CASES = [
     ("qkv_decode_r7_m2", 2, (256, 512, 256), 320, 7, 14.0),  # g r = 21: split partials, padded to 32 slots
     ("gateup_decode_m1_k6208", 1, (512, 256), 6208, 16, 32.0),    # one token, k > 4096: X from LDS, H partials
     ("qkv_decode_m2_k8192", 2, (256, 256, 256), 8192, 8, 16.0),
+    ("qkv_decode_m4", 4, (256, 512, 256), 320, 16, 32.0),          # four tokens: g r = 48, H from split partials
+    ("gateup_decode_m3_r24", 3, (512, 256), 448, 24, 48.0),
 ]
 
 

@@ -36,6 +36,11 @@ FWD_BWD_CASES = [
     ("decode_xl_m2_k4160_r8", 2, 64, 4160, 8, 16.0, True),       # ragged third half
     ("decode_xl_m2_k12288_r0", 2, 48, 12288, 0, 0.0, True),      # the largest k of that form, base only
     ("decode_xl_m1_k6144_r40_nodq", 1, 80, 6144, 40, 80.0, False),
+    # three or four tokens: the matrix-core GEMV
+    ("decode_m4_k4096_r32", 4, 160, 4096, 32, 64.0, True),           # r > 16: H from split partials
+    ("decode_m3_k2112_r40", 3, 48, 2112, 40, 80.0, True),            # H from partials, ragged k
+    ("decode_m4_k256_r0_nodq", 4, 272, 256, 0, 0.0, False),          # base only, one pass
+    ("decode_m3_k4160_r16", 3, 64, 4160, 16, 32.0, True),            # fused H, two passes over k
     # several GEMM tiles with ragged tails in m and n, and every remainder of
     # the k-step count modulo the three-stage ring, forward (k / 64 steps)
     # and dX (n / 64 steps)
