@@ -1,12 +1,16 @@
-"""GPU parity at the largest weight the linear calls accept, n k = 2^31
-(32768 x 65536): the fp32 source is 8 GiB, so its last rows lie past every
+"""GPU parity at the size limits of the linear calls.
+
+The largest weight, n k = 2^31 (32768 x 65536): the fp32 source is 8 GiB, so its last rows lie past every
 32-bit byte offset, and the packed codes fill 1 GiB. Sampled weight rows are
 checked against the oracle: codes, scale codes, group scales and the
 dequantized bf16 values bit for bit, the outputs of those rows in the
 forward (one token: the matrix-core GEMV, 32 tokens: the fused GEMM) within
 the 1e-2 bound, and the backward with dY non-zero only on those rows (so dX
 depends on no other weight row, while the dX GEMM still contracts over all
-32768 of them); dA and dB in full."""
+32768 of them); dA and dB in full.
+
+The longest row, k = 2^22 (n = 16): every output of the forward and
+backward at one and 32 tokens."""
 import numpy as np
 import pytest
 
@@ -99,3 +103,43 @@ def test_max_size_sampled(gpu_lib):
     edx, eda, edb = rel(f64(dx), dx_ref), rel(f64(da), da_ref), rel(f64(db), db_ref)
     say(f"   rel err dx={edx:.2e} da={eda:.2e} db={edb:.2e}")
     assert max(edx, eda, edb) <= TOL
+
+
+def test_max_k_full(gpu_lib):
+    """The longest accepted row, k = 2^22, with n = 16 (64 M weights): the
+    one-token GEMV makes 1024 passes over k, the 32-token GEMM 65536 K-steps
+    in one workgroup, the dX GEMM 32768 output tiles of one ragged step.
+    Every output is checked against the oracle."""
+    import torch
+
+    n, k, tag = 16, 1 << 22, "max_k"
+    w = synth.normal((n, k), 0.02, tag, "W")
+    say(f"[max_k] oracle quantization of {n} x {k}")
+    ref = O.quantize(w.reshape(-1), True)
+    _, bits = O.dequantize(ref)
+    w16 = O.bf16_bits_to_f32(bits).reshape(n, k).astype(np.float64)
+    say("[max_k] quantize")
+    q = gpu_lib.quantize(torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(q.codes.cpu().numpy(), ref["codes"])
+    assert np.array_equal(q.scale_codes.cpu().numpy(), ref["scale_codes"])
+    del w
+    a = to_bf16(synth.normal((R, k), 1.0 / R, tag, "A"))
+    b = to_bf16(synth.normal((n, R), 0.01, tag, "B"))
+    a64, b64 = f64(a), f64(b)
+    ac, bc = a.cuda(), b.cuda()
+    for m in (1, 32):
+        x = to_bf16(synth.normal((m, k), 1.0, tag, f"X{m}"))
+        dy = to_bf16(synth.normal((m, n), 1.0, tag, f"dY{m}"))
+        say(f"[max_k] forward and backward m={m}")
+        xc = x.cuda()
+        y, h = gpu_lib.linear_fwd(q, xc, ac, bc, ALPHA)
+        dx, da, db = gpu_lib.linear_bwd(q, xc, dy.cuda(), ac, bc, ALPHA, h=h)
+        torch.cuda.synchronize()
+        x64, dy64 = f64(x), f64(dy)
+        y_ref, h_ref = OL.linear_fwd(x64, w16, a64, b64, ALPHA, R)
+        dx_ref, da_ref, db_ref = OL.linear_bwd(x64, w16, a64, b64, dy64, ALPHA, R)
+        errs = [rel(f64(y), y_ref), rel(f64(h), h_ref), rel(f64(dx), dx_ref), rel(f64(da), da_ref),
+                rel(f64(db), db_ref)]
+        say("   rel err y/h/dx/dA/dB = " + " ".join(f"{e:.2e}" for e in errs))
+        assert max(errs) <= TOL
