@@ -250,8 +250,9 @@ def test_fused_gemm_matches_dequantize_then_matmul(gpu_lib):
     assert rel(f64(y), f64(ref)) <= 4e-3
 
 
-@pytest.mark.parametrize("m,k,r", [(4, 320, 16), (300, 320, 16), (4, 4608, 32)],
-                         ids=["gemv_fused_h", "gemm", "gemv_multipass_split_h"])
+@pytest.mark.parametrize("m,k,r", [(4, 320, 16), (300, 320, 16), (4, 4608, 32), (1, 4096, 16), (2, 8192, 16)],
+                         ids=["gemv_fused_h", "gemm", "gemv_multipass_split_h", "gemv_rows_fused_h",
+                              "gemv_rows_x_lds_split_h"])
 def test_graph_replay_matches_eager(gpu_lib, m, k, r):
     """Forward + backward captured in a HIP graph: every replay (with eager
     work and synchronisation in between, outputs and workspace overwritten)
