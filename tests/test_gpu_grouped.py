@@ -99,6 +99,15 @@ def test_grouped_7b_layers(gpu_lib, parts):
     run_case(gpu_lib, f"7b_{len(parts)}", 2048, parts, 4096, 16, 32.0)
 
 
+@pytest.mark.parametrize("m", [1, 2])
+@pytest.mark.parametrize("parts", [(4096, 4096, 4096), (11008, 11008)], ids=["qkv_7b", "gateup_7b"])
+def test_grouped_7b_decode(gpu_lib, parts, m):
+    """The 7B q/k/v and gate/up groups at one and two tokens: the row-per-wave
+    GEMV with 48 and 96 rows per workgroup, so the workgroups at the part
+    boundaries hold rows of two parts and form both parts' H slots."""
+    run_case(gpu_lib, f"7b_decode_{len(parts)}_m{m}", m, parts, 4096, 16, 32.0)
+
+
 @pytest.mark.parametrize("m", [96, 3], ids=["gemm_m96", "gemv_m3"])
 def test_grouped_equals_separate_calls(gpu_lib, m):
     """One part of a grouped call and the single-linear call on that part's
