@@ -36,6 +36,11 @@ FWD_BWD_CASES = [
     ("decode_xl_m2_k4160_r8", 2, 64, 4160, 8, 16.0, True),       # ragged third half
     ("decode_xl_m2_k12288_r0", 2, 48, 12288, 0, 0.0, True),      # the largest k of that form, base only
     ("decode_xl_m1_k6144_r40_nodq", 1, 80, 6144, 40, 80.0, False),
+    # the row-per-wave GEMV at every rows-per-wave count (n / (16 x 256 CUs), rounded up to 1, 2, 3, 4, 6, 8)
+    ("decode_rpw2_m1_k320", 1, 8192, 320, 16, 32.0, True),           # two rows per wave, fused H
+    ("decode_rpw2_xl_m1_k6144", 1, 8192, 6144, 16, 32.0, True),      # two rows per wave, X from LDS, H partials
+    ("decode_rpw4_m2_k256", 2, 16384, 256, 16, 32.0, True),          # four rows per wave, two tokens
+    ("decode_rpw8_m1_k256_nodq", 1, 40960, 256, 8, 16.0, False),     # eight rows per wave, 320 workgroups
     # three or four tokens: the matrix-core GEMV
     ("decode_m4_k4096_r32", 4, 160, 4096, 32, 64.0, True),           # r > 16: H from split partials
     ("decode_m3_k2112_r40", 3, 48, 2112, 40, 80.0, True),            # H from partials, ragged k
