@@ -689,10 +689,16 @@ hipError_t launch_skinny_decode(const uint16_t* P, const uint16_t* Q, int64_t m,
                                 float* part, int splits, hipStream_t s, bool f16) {
   if (m > 16) return hipErrorInvalidValue;
   const dim3 grid(1, static_cast<unsigned>(splits));
-  switch (rpad / 16) {
+  if (rpad % 32 != 0 || r > rpad) return hipErrorInvalidValue;
+  // rank tiles of 16 that hold the r real slots (the partial sums are written for j < r only)
+  switch ((r + 15) / 16) {
+    case 1: launch_skinny_decode_rt<1>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
     case 2: launch_skinny_decode_rt<2>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
+    case 3: launch_skinny_decode_rt<3>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
     case 4: launch_skinny_decode_rt<4>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
+    case 5: launch_skinny_decode_rt<5>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
     case 6: launch_skinny_decode_rt<6>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
+    case 7: launch_skinny_decode_rt<7>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
     case 8: launch_skinny_decode_rt<8>(grid, s, P, Q, m, qn, r, rpad, part, splits, f16); break;
     default: return hipErrorInvalidValue;
   }
