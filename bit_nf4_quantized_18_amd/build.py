@@ -69,7 +69,9 @@ def build(verbose: bool = False) -> str:
         msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
     tmp = LIB + ".tmp"
-    rc, out = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs)
+    # -z defs: an unresolved symbol (a kernel stub the host pass did not emit,
+    # say) fails the build here instead of the first dlopen
+    rc, out = _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Wl,-z,defs", "-o", tmp] + objs)
     if rc != 0:
         raise RuntimeError(f"link failed:\n{out}")
     os.replace(tmp, LIB)

@@ -397,8 +397,15 @@ __global__ void rank_final_kernel(const float* __restrict__ part, int64_t cn, in
 // the V tile (32 x 256 bf16, whole 512-byte row runs) and the U tile
 // (32 x 16 float32) with global->LDS buffer loads, three chunks ahead in a
 // ring of four, so each CU keeps tens of KB of reads in flight without
-// spending registers on them. Eight compute waves only read LDS and run the
-// float32 matrix-core product v_mfma_f32_16x16x4_f32 (D[16 ranks][16 cols]
+// spending registers on them. Eight compute waves only read LDS. With bf16
+// V, each float32 U is split into two bf16 terms, hi (U with its low 16 bits
+// dropped) and lo = bf16(U - hi), so U enters the product to 16 significant
+// bits (relative error below 2^-16), and the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16, float32 accumulation) run two MFMAs per 32 rows
+// and 16 columns instead of eight float32 ones; the layout is described at
+// the bf16 branch below. With fp16 V (whose range could not hold every U
+// split this way), they run the float32 matrix-core product
+// v_mfma_f32_16x16x4_f32 (D[16 ranks][16 cols]
 // += U^T[16 ranks][4 rows] V[4 rows][16 cols], all in float32): wave w owns
 // the 64 columns 64 (w % 4) .. +63 and every other group of 4 rows
 // (w / 4); lane (g, i) reads row g of a group, U[row][j0 + i] and the 4
@@ -424,6 +431,19 @@ constexpr int kRgWaves = 8;              // compute waves; one more wave copies
 
 __device__ __forceinline__ f32x4 mfma_16x16x4_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// bf16 V tile: the 16-byte chunk c of row r is stored at chunk c ^ rg_swz(r),
+// so that each 32-lane half of a transposing read (16 rows x 8 bytes: rows
+// 4 s + const over s and two adjacent rows) covers every bank once.
+__device__ __forceinline__ int rg_swz(int r) { return (2 * ((r >> 2) & 3)) | (8 * (r & 1)); }
+
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane 4 p + e receives element
+// e of the 8-byte rows addressed by lanes p, p + 4, p + 8 and p + 12.
+__device__ __forceinline__ u32x2 rg_ld_tr(const uint16_t* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 template <bool kF16>
@@ -459,7 +479,10 @@ __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGrad
     // ======================= copy wave =======================
     // V instruction u: rows 2u, 2u+1 (lane / 32), 16 bytes at column 8 (lane % 32);
     // U instruction q: rows 16q + lane / 4, floats j0 + 4 (lane % 4) .. +3.
-    const int v_voff = static_cast<int>(((lane >> 5) * cn + 8 * (lane & 31)) * 2);
+    // (bf16: the lane fetches the column chunk that rg_swz puts in its slot;
+    // row 2u + lane / 32 gives rg_swz = 2 ((u / 2) % 4) + 8 (lane / 32))
+    const int v_voff = static_cast<int>((lane >> 5) * cn * 2);
+    const int v_chunk = lane & 31, v_key = 8 * (lane >> 5);
     const int u_voff = static_cast<int>(((lane >> 2) * ldu + uj0 + 4 * (lane & 3)) * 4);
     auto copy_chunk = [&](int c) {
       const int64_t m0 = mb + static_cast<int64_t>(c) * kRgRows;
@@ -473,8 +496,10 @@ __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGrad
       // (whole offsets in the vector operand: the scalar offset is not range checked)
 #pragma unroll
       for (int u = 0; u < 16; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(vs + u * (2 * kRgCols)), 16,
-                                                 v_voff + static_cast<int>(u * 4 * cn), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (lds_void*)(vs + u * (2 * kRgCols)), 16,
+            v_voff + 16 * (kF16 ? v_chunk : (v_chunk ^ (v_key | (2 * ((u >> 1) & 3))))) + static_cast<int>(u * 4 * cn),
+            0, 0, 0);
 #pragma unroll
       for (int q = 0; q < 2; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ur, (lds_void*)(us + q * 256), 16, u_voff + q * 64 * ldu, 0, 0, 0);
@@ -502,6 +527,61 @@ __global__ __launch_bounds__((kRgWaves + 1) * 64) void rank_grad_kernel(RankGrad
 
   // ======================= compute waves =======================
   const int i = lane & 15, g = lane >> 4;
+  if constexpr (!kF16) {
+    // bf16: wave w owns the 32 columns 32 w .. +31 (two 16-column MFMA tiles)
+    // and all 32 rows of every chunk, so no sums cross waves. Contraction
+    // slot e of lane (i, g) is chunk row 4 e + g. The U^T operand: U[4 e +
+    // g][j0 + i], split as hi = U with the low 16 bits dropped and lo =
+    // bf16(U - hi), two MFMAs per tile. The V operand: two transposing LDS
+    // reads per tile; lane (i, g) addresses, in read h, row 4 (i / 4) + 16 h
+    // + g at columns 4 (i % 4) .. +3 of the tile, and receives column i of
+    // the four rows the lanes i % 4 + 4 s address.
+    int voff[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 4 * (i >> 2) + 16 * h + g;
+        const int col = 32 * wave + 16 * t + 4 * (i & 3);
+        voff[t][h] = row * kRgCols + (((col >> 3) ^ rg_swz(row)) << 3) + (col & 7);
+      }
+    f32x4 acc2[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    for (int c = 0; c < nch; ++c) {
+      __syncthreads();  // chunk c is in LDS
+      const uint16_t* vs = Vs + (c % kRgStages) * kRgV;
+      const float* us = Us + (c % kRgStages) * kRgU + 16 * g + i;
+      uint32_t ahi[4], alo[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float u0 = us[64 * e], u1 = us[64 * (e + 1)];  // rows 4 e + g, 4 (e + 1) + g
+        const uint32_t h0 = __float_as_uint(u0) >> 16, h1 = __float_as_uint(u1) >> 16;
+        const uint32_t l0 = f32_to_bf16_rne(u0 - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16_rne(u1 - __uint_as_float(h1 << 16));
+        ahi[e >> 1] = h0 | (h1 << 16);
+        alo[e >> 1] = l0 | (l1 << 16);
+      }
+      const u32x4 ah = u32x4{ahi[0], ahi[1], ahi[2], ahi[3]}, al = u32x4{alo[0], alo[1], alo[2], alo[3]};
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x2 b0 = rg_ld_tr(vs + voff[t][0]), b1 = rg_ld_tr(vs + voff[t][1]);
+        const u32x4 bv = u32x4{b0[0], b0[1], b1[0], b1[1]};
+        acc2[t] = mma16<false>(ah, bv, acc2[t]);
+        acc2[t] = mma16<false>(al, bv, acc2[t]);
+      }
+      __syncthreads();  // the slot may be refilled
+    }
+    // acc2[t][v] = sum for rank j0 + 4 g + v, column c0 + 32 w + 16 t + i
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t col = c0 + 32 * wave + 16 * t + i;
+      if (col < cn) {  // cn % 16 == 0: a tile is whole or absent
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          pb.part[(static_cast<int64_t>(s) * r + j0 + 4 * g + v) * cn + col] = acc2[t][v];
+      }
+    }
+    return;
+  }
   const int quad = wave & 3, half = wave >> 2;
   f32x4 acc[4];
 #pragma unroll
