@@ -31,11 +31,24 @@ def group_slice(w, row):
     return flat[g0 * gsz:min((g1 + 1) * gsz, n * k)].copy(), row * k - g0 * gsz
 
 
-def test_7b_grouped_step_graph(gpu_lib):
+def sample_rows(parts):
+    """About 30 weight rows of a (stacked) weight: every part's first and last
+    row and evenly spaced ones between, so that the sampled outputs' largest
+    magnitude is typical of the layer even at one token."""
+    n = sum(parts)
+    edges = np.cumsum([0] + list(parts))
+    rows = set(np.linspace(0, n - 1, 24).astype(int).tolist())
+    for l in range(len(parts)):
+        rows.update((int(edges[l]), int(edges[l + 1]) - 1))
+    return sorted(rows)
+
+
+def _build(gpu_lib, M, R):
+    """The grouped 7B calls (q/k/v, o, gate/up, down) at M tokens, with their
+    inputs, output buffers and workspaces, from the benchmark's seeded data."""
     import torch
 
     wl = synth.LAYERS_7B
-    M, R, ALPHA = wl.m, wl.r, wl.alpha
     dev = "cuda"
     byname = {lay.name: lay for lay in wl.layers}
     bf = torch.bfloat16
@@ -43,7 +56,6 @@ def test_7b_grouped_step_graph(gpu_lib):
     def t16(a):
         return torch.from_numpy(a).to(bf).to(dev)
 
-    say("[step] build the grouped 7B step")
     calls = []
     for names in GROUPS:
         lays = [byname[nm] for nm in names]
@@ -51,12 +63,14 @@ def test_7b_grouped_step_graph(gpu_lib):
         w = np.concatenate([synth.weight(wl, lay) for lay in lays], axis=0)
         n = w.shape[0]
         g = len(lays)
-        c = dict(names=names, parts=[lay.n for lay in lays], w_rows=[group_slice(w, row) for row in (0, n - 1)],
+        c = dict(names=names, parts=[lay.n for lay in lays],
+                 rows=sample_rows([lay.n for lay in lays]),
                  q=gpu_lib.quantize(torch.from_numpy(w).to(dev)),
-                 x=t16(synth.activations(wl, lays[0])),
+                 x=t16(synth.activations(wl, lays[0], M)),
                  a=torch.cat([t16(synth.lora_a(wl, lay)) for lay in lays]),
                  b=torch.cat([t16(synth.lora_b(wl, lay)) for lay in lays]),
-                 dy=torch.cat([t16(synth.grad_output(wl, lay)) for lay in lays], dim=1))
+                 dy=torch.cat([t16(synth.grad_output(wl, lay, M)) for lay in lays], dim=1))
+        c["w_rows"] = [group_slice(w, row) for row in c["rows"]]
         del w
         ws_bytes = (gpu_lib.grouped_workspace_bytes(M, n, k, g, R) if g > 1 else gpu_lib.workspace_bytes(M, n, k, R))
         c["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -67,25 +81,36 @@ def test_7b_grouped_step_graph(gpu_lib):
                         db=torch.empty((n, R), dtype=torch.float32, device=dev))
         calls.append(c)
     torch.cuda.synchronize()
+    return calls
 
-    def step():
-        for c in calls:
-            o = c["out"]
-            if len(c["parts"]) == 1:
-                gpu_lib.linear_fwd(c["q"], c["x"], c["a"], c["b"], ALPHA, out=o["y"], h_out=o["h"], ws=c["ws"])
-                gpu_lib.linear_bwd(c["q"], c["x"], c["dy"], c["a"], c["b"], ALPHA, h=o["h"], dx=o["dx"],
+
+def _step(gpu_lib, calls, alpha, bwd):
+    for c in calls:
+        o = c["out"]
+        if len(c["parts"]) == 1:
+            gpu_lib.linear_fwd(c["q"], c["x"], c["a"], c["b"], alpha, out=o["y"], h_out=o["h"], ws=c["ws"])
+            if bwd:
+                gpu_lib.linear_bwd(c["q"], c["x"], c["dy"], c["a"], c["b"], alpha, h=o["h"], dx=o["dx"],
                                    da=o["da"], db=o["db"], ws=c["ws"])
-            else:
-                gpu_lib.linear_fwd_grouped(c["q"], c["parts"], c["x"], c["a"], c["b"], ALPHA, out=o["y"],
-                                           h_out=o["h"], ws=c["ws"])
-                gpu_lib.linear_bwd_grouped(c["q"], c["parts"], c["x"], c["dy"], c["a"], c["b"], ALPHA, h=o["h"],
+        else:
+            gpu_lib.linear_fwd_grouped(c["q"], c["parts"], c["x"], c["a"], c["b"], alpha, out=o["y"],
+                                       h_out=o["h"], ws=c["ws"])
+            if bwd:
+                gpu_lib.linear_bwd_grouped(c["q"], c["parts"], c["x"], c["dy"], c["a"], c["b"], alpha, h=o["h"],
                                            dx=o["dx"], da=o["da"], db=o["db"], ws=c["ws"])
+
+
+def _graph_equals_eager(calls, step, keys):
+    """Eager run, then one graph of the same calls replayed three times with
+    outputs and workspaces overwritten in between: every replay equals the
+    eager run bit for bit."""
+    import torch
 
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         step()
         torch.cuda.synchronize()
-        eager = [{key: v.clone() for key, v in c["out"].items()} for c in calls]
+        eager = [{key: c["out"][key].clone() for key in keys} for c in calls]
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=s):
             step()
@@ -99,26 +124,47 @@ def test_7b_grouped_step_graph(gpu_lib):
             graph.replay()
             torch.cuda.synchronize()
             for c, e in zip(calls, eager):
-                for key, v in c["out"].items():
-                    assert torch.equal(v, e[key]), (rep, c["names"], key)
+                for key in keys:
+                    assert torch.equal(c["out"][key], e[key]), (rep, c["names"], key)
 
-    # the graph's Y against the oracle on each call's first and last weight row
-    # (the last row lies in the last part of a grouped call)
-    s_lora = OL.lora_scale(ALPHA, R)
+
+def _check_sampled_y(calls, M, R, alpha):
+    """The sampled weight rows' output columns of each call against the
+    oracle (a row of part l takes slots l R .. (l + 1) R - 1 of H)."""
+    s_lora = OL.lora_scale(alpha, R)
     for c in calls:
-        n = c["out"]["y"].shape[1]
-        cols = [0, n - 1]
         k = c["x"].shape[1]
-        w16 = np.stack([O.bf16_bits_to_f32(O.dequantize(O.quantize(sl, True))[1])[off:off + k]
-                        for sl, off in c["w_rows"]])
         x64 = f64(c["x"])
         a64, b64 = f64(c["a"]), f64(c["b"])
-        # row 0 belongs to part 0 (A rows 0..R-1), row n-1 to the last part
-        g = len(c["parts"])
-        ref = np.empty((M, 2))
-        for j, (col, part) in enumerate(zip(cols, (0, g - 1))):
+        edges = np.cumsum([0] + c["parts"])
+        ref = np.empty((M, len(c["rows"])))
+        for j, (row, (sl, off)) in enumerate(zip(c["rows"], c["w_rows"])):
+            w16 = O.bf16_bits_to_f32(O.dequantize(O.quantize(sl, True))[1])[off:off + k].astype(np.float64)
+            part = int(np.searchsorted(edges, row, side="right")) - 1
             h = x64 @ a64[part * R:(part + 1) * R].T
-            ref[:, j] = x64 @ w16[j].astype(np.float64) + s_lora * (h @ b64[col])
-        e = rel(f64(c["out"]["y"])[:, cols], ref)
-        say(f"[step] {'/'.join(c['names'])}: rel err of sampled Y columns {e:.2e}")
+            ref[:, j] = x64 @ w16 + s_lora * (h @ b64[row])
+        e = rel(f64(c["out"]["y"])[:, c["rows"]], ref)
+        say(f"[step] m={M} {'/'.join(c['names'])}: rel err of {len(c['rows'])} sampled Y columns {e:.2e}")
         assert e <= TOL
+
+
+def test_7b_grouped_step_graph(gpu_lib):
+    wl = synth.LAYERS_7B
+    M, R, ALPHA = wl.m, wl.r, wl.alpha
+    say("[step] build the grouped 7B training step")
+    calls = _build(gpu_lib, M, R)
+    _graph_equals_eager(calls, lambda: _step(gpu_lib, calls, ALPHA, True), ("y", "h", "dx", "da", "db"))
+    _check_sampled_y(calls, M, R, ALPHA)
+
+
+@pytest.mark.parametrize("m", [1, 2])
+def test_7b_grouped_decode_graph(gpu_lib, m):
+    """One layer set of the decode token: the four grouped forward calls at
+    one or two tokens (the row-per-wave GEMV, H inside or from the
+    projection) as one graph."""
+    wl = synth.LAYERS_7B
+    R, ALPHA = wl.r, wl.alpha
+    say(f"[step] build the grouped 7B decode calls, m={m}")
+    calls = _build(gpu_lib, m, R)
+    _graph_equals_eager(calls, lambda: _step(gpu_lib, calls, ALPHA, False), ("y", "h"))
+    _check_sampled_y(calls, m, R, ALPHA)
